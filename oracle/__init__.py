@@ -1,0 +1,194 @@
+"""CPU oracle of the token-importance path (ctypes wrapper over sp_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, the smoke check and the
+benchmark's CPU-baseline leg, never by the library. The arithmetic lives in
+``sp_oracle.c`` (plain fp64 loops); this wrapper only marshals arrays.
+
+Parity status of each function (what pins it, beyond itself):
+
+* ``importance``: closed forms (all-zero Q, a single hot key, a hot
+  lookahead key that only later queries see), row sums, brute force against
+  a numpy softmax on tiny shapes, permutation invariants.
+* ``pool_chunk``: identity at W=1, constants, impulses, numpy convolution,
+  hand-computed boosts and normalisation.
+* ``select_top_p`` / ``select_mass``: exhaustive subset search on small
+  chunk counts, and the kept-token counts printed in the pull request's
+  stress tables (``tests/golden/pr_kept_counts.txt``).
+* ``gather``: brute-force list construction.
+
+End-to-end scores on large random inputs have no printed values on the
+pages; there they rest on the pins above.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sp_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libsp_oracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_fp = ctypes.POINTER(ctypes.c_float)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (OpenMP) into ``oracle/libsp_oracle.so``."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+                               "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB_PATH)
+        L.oracle_softmax_row.argtypes = [ctypes.c_int, _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_double, _fp, _fp,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp]
+        L.oracle_importance.argtypes = [ctypes.c_int, _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_double, _fp, _fp, _dp,
+                                        ctypes.c_int]
+        L.oracle_pool_chunk.argtypes = [ctypes.c_int64, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double,
+                                        _dp, _dp]
+        L.oracle_top_p_count.argtypes = [ctypes.c_int64, ctypes.c_double]
+        L.oracle_top_p_count.restype = ctypes.c_int64
+        L.oracle_select_top_p.argtypes = [ctypes.c_int64, _dp, ctypes.c_double, _u8p]
+        L.oracle_select_top_p.restype = ctypes.c_int64
+        L.oracle_select_mass.argtypes = [ctypes.c_int64, _dp, ctypes.c_double, _u8p]
+        L.oracle_select_mass.restype = ctypes.c_int64
+        L.oracle_gather.argtypes = [ctypes.c_int64, ctypes.c_int, _u8p, _i32p, _i32p, _i32p]
+        L.oracle_gather.restype = ctypes.c_int64
+        L.oracle_max_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray, t):
+    return a.ctypes.data_as(t)
+
+
+def max_threads() -> int:
+    return int(lib().oracle_max_threads())
+
+
+def _as_f32(x) -> np.ndarray:
+    """Widen Q/K to a contiguous fp32 numpy array (exact for bf16 input)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return np.ascontiguousarray(x.detach().to("cpu", torch.float32).numpy())
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def softmax_row(offsets, q, k, n_layers, Hq, Hkv, d, L, scale, b, l, j, h) -> np.ndarray:
+    """Softmax probabilities of query (b, l, j, h) over its N_b + j + 1 visible keys."""
+    off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    qf, kf = _as_f32(q), _as_f32(k)
+    n = int(off[b + 1] - off[b])
+    p = np.empty(n + j + 1, dtype=np.float64)
+    rc = lib().oracle_softmax_row(len(off) - 1, _ptr(off, _i64p), n_layers, Hq, Hkv, d, L, scale,
+                                  _ptr(qf, _fp), _ptr(kf, _fp), b, l, j, h, _ptr(p, _dp))
+    if rc != 0:
+        raise ValueError("oracle_softmax_row: bad arguments")
+    return p
+
+
+def importance(offsets, q, k, n_layers, Hq, Hkv, d, L, scale, nthreads: int = 0) -> np.ndarray:
+    """Importance of every prompt token, [sum N_b] fp64."""
+    off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    qf, kf = _as_f32(q), _as_f32(k)
+    B = len(off) - 1
+    assert qf.size == B * n_layers * L * Hq * d, "q has the wrong size"
+    assert kf.size == n_layers * (int(off[-1]) + B * L) * Hkv * d, "k has the wrong size"
+    imp = np.empty(int(off[-1]), dtype=np.float64)
+    rc = lib().oracle_importance(B, _ptr(off, _i64p), n_layers, Hq, Hkv, d, L, scale,
+                                 _ptr(qf, _fp), _ptr(kf, _fp), _ptr(imp, _dp), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_importance: bad arguments")
+    return imp
+
+
+def pool_chunk(imp, W=13, C=32, normalize=True, first_n=64, first_mult=1.5,
+               last_n=128, last_mult=1.3):
+    """(token_scores [n], chunk_scores [ceil(n/C)]) of one prompt, fp64."""
+    x = np.ascontiguousarray(np.asarray(imp, dtype=np.float64))
+    n = x.size
+    nc = (n + C - 1) // C if C >= 1 else 1
+    ts = np.empty(n, dtype=np.float64)
+    cs = np.empty(nc, dtype=np.float64)
+    rc = lib().oracle_pool_chunk(n, _ptr(x, _dp), W, C, int(bool(normalize)), first_n, first_mult,
+                                 last_n, last_mult, _ptr(ts, _dp), _ptr(cs, _dp))
+    if rc != 0:
+        raise ValueError("oracle_pool_chunk: bad arguments")
+    return ts, cs
+
+
+def top_p_count(nc: int, p: float) -> int:
+    return int(lib().oracle_top_p_count(nc, p))
+
+
+def select(chunk_scores, mode: str, param: float) -> np.ndarray:
+    """Keep flags [nc] (uint8) of one prompt; mode is 'top_p' or 'mass'."""
+    cs = np.ascontiguousarray(np.asarray(chunk_scores, dtype=np.float64))
+    keep = np.zeros(cs.size, dtype=np.uint8)
+    fn = {"top_p": lib().oracle_select_top_p, "mass": lib().oracle_select_mass}[mode]
+    rc = fn(cs.size, _ptr(cs, _dp), float(param), _ptr(keep, _u8p))
+    if rc < 0:
+        raise ValueError("oracle select: bad arguments")
+    return keep
+
+
+def gather(keep, ids, C=32):
+    """(kept_ids, kept_pos) of one prompt."""
+    kp = np.ascontiguousarray(np.asarray(keep, dtype=np.uint8))
+    idv = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+    n = idv.size
+    out_i = np.empty(n, dtype=np.int32)
+    out_p = np.empty(n, dtype=np.int32)
+    w = lib().oracle_gather(n, C, _ptr(kp, _u8p), _ptr(idv, _i32p), _ptr(out_i, _i32p),
+                            _ptr(out_p, _i32p))
+    if w < 0:
+        raise ValueError("oracle_gather: bad arguments")
+    return out_i[:w].copy(), out_p[:w].copy()
+
+
+def pipeline(inputs, mode: str = None, param: float = None, nthreads: int = 0, imp=None):
+    """Whole path on a ``workloads.Inputs``: per-prompt results as a dict of lists."""
+    w = inputs.workload
+    if mode is None:
+        mode, param = w.select
+    if imp is None:
+        imp = importance(inputs.offsets.numpy(), inputs.q, inputs.k, w.n_layers, w.n_q_heads,
+                         w.n_kv_heads, w.head_dim, w.n_lookahead, inputs.scale, nthreads)
+    off = inputs.offsets.numpy()
+    ids = inputs.token_ids.numpy()
+    fm, lm = (1.5, 1.3) if w.boost else (1.0, 1.0)
+    out = {"imp": imp, "token_scores": [], "chunk_scores": [], "keep": [], "kept_ids": [],
+           "kept_pos": []}
+    for b in range(len(off) - 1):
+        x = imp[off[b]:off[b + 1]]
+        ts, cs = pool_chunk(x, w.pool_window, w.chunk_size, w.normalize, 64, fm, 128, lm)
+        keep = select(cs, mode, param)
+        ki, kp = gather(keep, ids[off[b]:off[b + 1]], w.chunk_size)
+        out["token_scores"].append(ts)
+        out["chunk_scores"].append(cs)
+        out["keep"].append(keep)
+        out["kept_ids"].append(ki)
+        out["kept_pos"].append(kp)
+    return out

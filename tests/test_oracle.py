@@ -1,0 +1,427 @@
+"""Pins of the CPU oracle against facts other than itself.
+
+Each test checks the oracle against something the pages or mathematics fix:
+closed forms, invariants, library routines on tiny shapes, exhaustive search,
+and the kept-token counts printed on the pull-request page. None of these
+needs a GPU.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_problem(rng, lengths, n_layers, Hq, Hkv, d, L, scale_q=1.0):
+    B = len(lengths)
+    off = np.zeros(B + 1, dtype=np.int64)
+    off[1:] = np.cumsum(lengths)
+    q = (rng.standard_normal((B, n_layers, L, Hq, d)) * scale_q).astype(np.float32)
+    k = rng.standard_normal((n_layers, int(off[-1]) + B * L, Hkv, d)).astype(np.float32)
+    return off, q, k
+
+
+def _importance_bruteforce(off, q, k, n_layers, Hq, Hkv, d, L, scale):
+    """Independent route: dense logits via numpy, masked softmax via scipy,
+    reductions via numpy max/mean over named axes."""
+    B = len(off) - 1
+    G = Hq // Hkv
+    out = []
+    for b in range(B):
+        n = int(off[b + 1] - off[b])
+        k0 = int(off[b]) + b * L
+        kb = k[:, k0:k0 + n + L].astype(np.float64)            # [l][key][g][d]
+        kq = np.repeat(kb, G, axis=2)                           # [l][key][h][d]
+        qb = q[b].astype(np.float64)                            # [l][j][h][d]
+        s = np.einsum("ljhd,lkhd->ljhk", qb, kq) * scale        # [l][j][h][key]
+        key_pos = np.arange(n + L)
+        mask = key_pos[None, :] <= (n + np.arange(L))[:, None]  # [j][key]
+        s = np.where(mask[None, :, None, :], s, -np.inf)
+        p = scipy.special.softmax(s, axis=-1)[..., :n]          # prompt columns
+        stepmax = p.max(axis=2).max(axis=0)                     # heads, then layers -> [j][k]
+        out.append(stepmax.mean(axis=0))
+    return np.concatenate(out)
+
+
+# ----------------------------------------------------------------------------
+# Softmax rows and importance
+# ----------------------------------------------------------------------------
+
+def test_softmax_rows_sum_to_one_and_match_scipy():
+    rng = np.random.default_rng(0)
+    off, q, k = _rand_problem(rng, [7, 12], 2, 4, 2, 8, 3, scale_q=2.0)
+    scale = 1 / math.sqrt(8)
+    for (b, l, j, h) in itertools.product(range(2), range(2), range(3), range(4)):
+        p = oracle.softmax_row(off, q, k, 2, 4, 2, 8, 3, scale, b, l, j, h)
+        n = off[b + 1] - off[b]
+        assert p.size == n + j + 1
+        assert abs(p.sum() - 1.0) < 1e-12
+        k0 = int(off[b]) + b * 3
+        s = k[l, k0:k0 + n + j + 1, h // 2, :].astype(np.float64) @ q[b, l, j, h].astype(np.float64)
+        np.testing.assert_allclose(p, scipy.special.softmax(s * scale), rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(lengths=[5], n_layers=1, Hq=1, Hkv=1, d=4, L=1),
+    dict(lengths=[9, 4, 13], n_layers=3, Hq=4, Hkv=2, d=8, L=3),
+    dict(lengths=[17], n_layers=2, Hq=8, Hkv=2, d=16, L=8),
+    dict(lengths=[6, 11], n_layers=2, Hq=6, Hkv=3, d=4, L=2),
+])
+def test_importance_matches_bruteforce(shape):
+    rng = np.random.default_rng(1)
+    off, q, k = _rand_problem(rng, shape["lengths"], shape["n_layers"], shape["Hq"],
+                              shape["Hkv"], shape["d"], shape["L"], scale_q=3.0)
+    scale = 1 / math.sqrt(shape["d"])
+    args = (shape["n_layers"], shape["Hq"], shape["Hkv"], shape["d"], shape["L"], scale)
+    got = oracle.importance(off, q, k, *args)
+    ref = _importance_bruteforce(off, q, k, *args)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_importance_all_zero_q_is_uniform_closed_form():
+    """Zero queries give uniform rows: p = 1/(N+j+1), so
+    imp = (1/L) * sum_j 1/(N+j+1) at every prompt position."""
+    rng = np.random.default_rng(2)
+    lengths, L = [50, 33], 8
+    off, q, k = _rand_problem(rng, lengths, 3, 4, 1, 16, L)
+    q[:] = 0
+    imp = oracle.importance(off, q, k, 3, 4, 1, 16, L, 0.25)
+    for b, n in enumerate(lengths):
+        want = sum(1.0 / (n + j + 1) for j in range(L)) / L
+        np.testing.assert_allclose(imp[off[b]:off[b + 1]], want, rtol=1e-14)
+
+
+def test_importance_single_hot_prompt_key_closed_form():
+    """All keys zero except key k0 of group 0, whose logit is `a` for every
+    query of group 0. Group-0 rows: p(k0) = e^a/(e^a+N+j), others
+    1/(e^a+N+j); group-1 rows are uniform 1/(N+j+1)."""
+    n, L, d, a, k0 = 40, 4, 8, 2.5, 17
+    off = np.array([0, n], dtype=np.int64)
+    q = np.zeros((1, 2, L, 4, d), dtype=np.float32)   # 2 layers, Hq=4, Hkv=2
+    k = np.zeros((2, n + L, 2, d), dtype=np.float32)
+    k[:, k0, 0, 0] = 1.0
+    scale = 0.5
+    q[:, :, :, 0:2, 0] = a / scale                     # group-0 heads
+    imp = oracle.importance(off, q, k, 2, 4, 2, d, L, scale)
+    ea = math.exp(a)
+    want_hot = sum(ea / (ea + n + j) for j in range(L)) / L
+    want_cold = sum(1.0 / (n + j + 1) for j in range(L)) / L
+    assert abs(imp[k0] - want_hot) < 1e-14
+    others = np.delete(imp, k0)
+    np.testing.assert_allclose(others, want_cold, rtol=1e-14)
+
+
+def test_importance_causal_lookahead_key_closed_form():
+    """A hot key at lookahead position N+2 is seen only by queries j >= 2.
+    With one KV group, prompt keys get 1/(N+j+1) for j < 2 and
+    1/(e^a+N+j) for j >= 2."""
+    n, L, d, a = 30, 5, 4, 3.0
+    off = np.array([0, n], dtype=np.int64)
+    q = np.zeros((1, 1, L, 2, d), dtype=np.float32)   # 1 layer, Hq=2, Hkv=1
+    k = np.zeros((1, n + L, 1, d), dtype=np.float32)
+    k[0, n + 2, 0, 0] = 1.0
+    q[0, 0, :, :, 0] = a                                # scale 1
+    imp = oracle.importance(off, q, k, 1, 2, 1, d, L, 1.0)
+    ea = math.exp(a)
+    want = (sum(1.0 / (n + j + 1) for j in range(2)) + sum(1.0 / (ea + n + j) for j in range(2, L))) / L
+    np.testing.assert_allclose(imp, want, rtol=1e-14)
+
+
+def test_importance_invariant_to_layer_and_head_permutations():
+    rng = np.random.default_rng(3)
+    n_layers, Hq, Hkv, d, L = 3, 6, 3, 8, 4
+    off, q, k = _rand_problem(rng, [21, 10], n_layers, Hq, Hkv, d, L, scale_q=2.0)
+    args = (n_layers, Hq, Hkv, d, L, 0.3)
+    base = oracle.importance(off, q, k, *args)
+    # permute layers
+    perm = [2, 0, 1]
+    np.testing.assert_allclose(oracle.importance(off, q[:, perm], k[perm], *args), base, rtol=1e-14)
+    # permute q-heads inside each group (G = 2)
+    hp = [1, 0, 3, 2, 5, 4]
+    np.testing.assert_allclose(oracle.importance(off, q[:, :, :, hp], k, *args), base, rtol=1e-14)
+    # permute KV groups together with their q-heads
+    gp = [2, 0, 1]
+    hp2 = [h for g in gp for h in (2 * g, 2 * g + 1)]
+    np.testing.assert_allclose(oracle.importance(off, q[:, :, :, hp2], k[:, :, gp], *args), base,
+                               rtol=1e-14)
+    # duplicating a layer leaves the max over layers unchanged
+    q2 = np.concatenate([q, q[:, :1]], axis=1)
+    k2 = np.concatenate([k, k[:1]], axis=0)
+    np.testing.assert_allclose(oracle.importance(off, q2, k2, n_layers + 1, Hq, Hkv, d, L, 0.3),
+                               base, rtol=1e-14)
+
+
+def test_importance_prompts_are_independent():
+    """A prompt's scores do not depend on the other prompts of the batch."""
+    rng = np.random.default_rng(4)
+    off, q, k = _rand_problem(rng, [12, 20], 2, 4, 2, 8, 3)
+    both = oracle.importance(off, q, k, 2, 4, 2, 8, 3, 0.4)
+    k1 = np.ascontiguousarray(k[:, 15:15 + 23])
+    one = oracle.importance(np.array([0, 20]), q[1:], k1, 2, 4, 2, 8, 3, 0.4)
+    np.testing.assert_allclose(both[12:], one, rtol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# Pooling, normalisation, boosts, chunk means
+# ----------------------------------------------------------------------------
+
+def test_pool_window_one_is_identity():
+    x = np.random.default_rng(5).random(77)
+    ts, cs = oracle.pool_chunk(x, W=1, C=32, normalize=False, first_mult=1.0, last_mult=1.0)
+    np.testing.assert_array_equal(ts, x)
+    np.testing.assert_allclose(cs, [x[0:32].mean(), x[32:64].mean(), x[64:77].mean()], rtol=1e-15)
+
+
+def test_pool_constant_and_impulse():
+    ts, _ = oracle.pool_chunk(np.full(40, 0.25), W=13, normalize=False, first_mult=1.0, last_mult=1.0)
+    np.testing.assert_allclose(ts, 0.25, rtol=1e-15)
+    n, k0 = 40, 3
+    x = np.zeros(n)
+    x[k0] = 1.0
+    ts, _ = oracle.pool_chunk(x, W=13, normalize=False, first_mult=1.0, last_mult=1.0)
+    for t in range(n):
+        lo, hi = max(0, t - 6), min(n - 1, t + 6)
+        want = 1.0 / (hi - lo + 1) if lo <= k0 <= hi else 0.0
+        assert abs(ts[t] - want) < 1e-15
+
+
+def test_pool_matches_numpy_convolve():
+    x = np.random.default_rng(6).random(300)
+    ts, _ = oracle.pool_chunk(x, W=13, normalize=False, first_mult=1.0, last_mult=1.0)
+    sums = np.convolve(x, np.ones(13), mode="same")
+    counts = np.convolve(np.ones_like(x), np.ones(13), mode="same")
+    np.testing.assert_allclose(ts, sums / counts, rtol=1e-13)
+    assert counts[0] == 7 and counts[6] == 13 and counts[-1] == 7
+
+
+def test_normalise_then_boost_hand_values():
+    """Constant scores carry no signal -> 1.0; then boosts: first 64 x1.5,
+    last 128 x1.3. N=3212 puts the boost edge 12 tokens into chunk 96."""
+    n = 3212
+    _, cs = oracle.pool_chunk(np.full(n, 0.37), W=13, C=32, normalize=True)
+    assert cs.size == 101
+    np.testing.assert_allclose(cs[:2], 1.5, rtol=1e-15)
+    np.testing.assert_allclose(cs[2:96], 1.0, rtol=1e-15)
+    assert abs(cs[96] - (12 * 1.0 + 20 * 1.3) / 32) < 1e-15
+    np.testing.assert_allclose(cs[97:], 1.3, rtol=1e-15)
+    # min-max scaling of a ramp, W=1, no boosts
+    x = np.arange(10, dtype=np.float64) * 2.0 + 5.0
+    ts, _ = oracle.pool_chunk(x, W=1, C=4, normalize=True, first_mult=1.0, last_mult=1.0)
+    np.testing.assert_allclose(ts, np.arange(10) / 9.0, rtol=1e-15)
+
+
+def test_overlapping_boosts_multiply():
+    ts, _ = oracle.pool_chunk(np.ones(100), W=1, C=32, normalize=False)
+    np.testing.assert_allclose(ts[:64], 1.5 * 1.3)        # n < 192: all of 0..63 in both
+    np.testing.assert_allclose(ts[64:], 1.3)
+
+
+def test_pool_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        oracle.pool_chunk(np.ones(10), W=12)
+    with pytest.raises(ValueError):
+        oracle.pool_chunk(np.ones(10), C=0)
+
+
+# ----------------------------------------------------------------------------
+# Selection
+# ----------------------------------------------------------------------------
+
+def _order_key(cs, i):
+    return (-cs[i], i)
+
+
+def _best_set(cs, cands):
+    """The candidate whose members, listed in selection order, are
+    lexicographically first."""
+    return min(cands, key=lambda s: sorted(_order_key(cs, i) for i in s))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_top_p_matches_exhaustive_search(seed):
+    rng = np.random.default_rng(100 + seed)
+    nc = int(rng.integers(1, 11))
+    cs = rng.integers(0, 4, nc).astype(np.float64)       # small value set -> ties
+    for p in (0.05, 0.15, 0.3, 0.5, 0.77, 1.0):
+        kc = oracle.top_p_count(nc, p)
+        assert kc == max(1, min(nc, math.ceil(p * nc - 1e-9)))
+        cands = [set(c) | {nc - 1} for c in itertools.combinations(range(nc - 1), kc - 1)]
+        want = _best_set(cs, cands)
+        keep = oracle.select(cs, "top_p", p)
+        assert set(np.nonzero(keep)[0]) == want
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_mass_matches_exhaustive_search(seed):
+    """Smallest set containing the final chunk whose mass reaches
+    mass * total; among those, the first in selection order. Integer scores
+    keep every sum exact."""
+    rng = np.random.default_rng(200 + seed)
+    nc = int(rng.integers(1, 11))
+    cs = rng.integers(0, 5, nc).astype(np.float64)
+    total = cs.sum()
+    for m in (0.1, 0.5, 0.85, 0.9, 1.0):
+        want = None
+        for size in range(1, nc + 1):
+            cands = [set(c) | {nc - 1} for c in itertools.combinations(range(nc - 1), size - 1)]
+            ok = [s for s in cands if sum(cs[i] for i in s) >= m * total]
+            if ok:
+                want = _best_set(cs, ok)
+                break
+        keep = oracle.select(cs, "mass", m)
+        assert set(np.nonzero(keep)[0]) == want
+
+
+def _golden_counts():
+    rows = []
+    with open(os.path.join(GOLDEN, "pr_kept_counts.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                n, p, kept = line.split()
+                rows.append((int(n), float(p), int(kept)))
+    return rows
+
+
+def test_golden_kept_counts_from_pull_request():
+    """Reproduce the 23 printed (N, p, kept) triples. The printed count is
+    (kc - 1) full chunks + the final (partial) chunk, plus one BOS token when
+    chunk 0 is not among the kept chunks; scores are built to put chunk 0
+    in or out as the printed count implies, and the oracle's own selection
+    and compaction must then give exactly the printed count."""
+    rows = _golden_counts()
+    assert len(rows) == 23
+    C = 32
+    for n, p, kept in rows:
+        nc = (n + C - 1) // C
+        kc = oracle.top_p_count(nc, p)
+        tail = n - (nc - 1) * C
+        base = (kc - 1) * C + tail
+        extra = kept - base
+        assert extra in (0, 1), (n, p, kept, kc)
+        bos_separate = extra == 1
+        assert not (bos_separate and kc == nc)
+        # scores: descending with index except that chunk 0 is placed last
+        # when BOS must come on its own, first otherwise.
+        cs = np.linspace(1.0, 0.5, nc)
+        cs[0] = 0.0 if bos_separate else 2.0
+        keep = oracle.select(cs, "top_p", p)
+        ids = np.arange(n, dtype=np.int32) + 1000
+        ki, kp = oracle.gather(keep, ids, C)
+        assert ki.size == kept, (n, p, kept)
+        assert kp[0] == 0 and np.all(np.diff(kp) > 0)
+
+
+def test_golden_counts_reject_other_rules():
+    """The printed counts rule out neighbouring readings: rounding to nearest
+    or down instead of up, and a final chunk kept on top of the budget."""
+    rows = _golden_counts()
+    C = 32
+
+    def count(n, kc, chunk0_in):
+        nc = (n + C - 1) // C
+        tail = n - (nc - 1) * C
+        return (kc - 1) * C + tail + (0 if chunk0_in or kc == nc else 1)
+
+    def consistent(kc_fn, on_top=False):
+        for n, p, kept in rows:
+            nc = (n + C - 1) // C
+            kc = kc_fn(nc, p)
+            if on_top:
+                kc = min(nc, kc + 1)
+            if kept not in (count(n, kc, True), count(n, kc, False)):
+                return False
+        return True
+
+    assert consistent(lambda nc, p: oracle.top_p_count(nc, p))
+    assert not consistent(lambda nc, p: max(1, round(p * nc)))
+    assert not consistent(lambda nc, p: max(1, math.floor(p * nc)))
+    assert not consistent(lambda nc, p: oracle.top_p_count(nc, p), on_top=True)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_selection_monotone_in_p_and_mass(seed):
+    rng = np.random.default_rng(300 + seed)
+    cs = rng.random(int(rng.integers(1, 300)))
+    prev = None
+    for p in np.linspace(0.01, 1.0, 40):
+        cur = set(np.nonzero(oracle.select(cs, "top_p", p))[0])
+        if prev is not None:
+            assert prev <= cur
+        prev = cur
+    assert prev == set(range(cs.size))
+    prev = None
+    for m in np.linspace(0.01, 1.0, 40):
+        cur = set(np.nonzero(oracle.select(cs, "mass", m))[0])
+        if prev is not None:
+            assert prev <= cur
+        prev = cur
+
+
+def test_select_single_chunk_and_bad_args():
+    assert list(oracle.select([0.3], "top_p", 0.01)) == [1]
+    assert list(oracle.select([0.3], "mass", 0.5)) == [1]
+    with pytest.raises(ValueError):
+        oracle.select([0.3, 0.1], "top_p", 0.0)
+    with pytest.raises(ValueError):
+        oracle.select([0.3, 0.1], "mass", 1.5)
+
+
+# ----------------------------------------------------------------------------
+# Compaction
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(6))
+def test_gather_matches_list_comprehension(seed):
+    rng = np.random.default_rng(400 + seed)
+    n = int(rng.integers(1, 500))
+    C = int(rng.choice([1, 7, 32]))
+    nc = (n + C - 1) // C
+    keep = (rng.random(nc) < 0.4).astype(np.uint8)
+    ids = rng.integers(0, 1 << 17, n).astype(np.int32)
+    ki, kp = oracle.gather(keep, ids, C)
+    want = [t for t in range(n) if t == 0 or keep[t // C]]
+    assert kp.tolist() == want
+    assert ki.tolist() == [int(ids[t]) for t in want]
+    assert ki.size == sum(min(C, n - c * C) for c in range(nc) if keep[c]) + (0 if keep[0] else 1)
+
+
+# ----------------------------------------------------------------------------
+# Whole path on small planted workloads
+# ----------------------------------------------------------------------------
+
+def test_planted_spans_selected_n800():
+    """The 800-token fp32 workload (3 planted spans, top-p 0.15): all spans
+    are kept and the kept count is 3 spans + the final chunk + BOS."""
+    inp = workloads.make_inputs(workloads.WORKLOADS["n800_fp32"])
+    out = oracle.pipeline(inp)
+    keep = out["keep"][0]
+    for c in inp.spans[0]:
+        assert keep[c] == 1
+    assert keep.sum() == oracle.top_p_count(25, 0.15) == 4
+    assert out["kept_ids"][0].size == 3 * 32 + 32 + (0 if keep[0] else 1)
+
+
+def test_planted_spans_selected_small_bf16_shapes():
+    w = workloads.small_workload("n32k_bf16", lengths=(2500,), n_spans=6, seed=77)
+    inp = workloads.make_inputs(w)
+    for mode, param in (("mass", 0.85), ("top_p", 0.15)):
+        out = oracle.pipeline(inp, mode, param)
+        for c in inp.spans[0]:
+            assert out["keep"][0][c] == 1, (mode, c)
+
+
+def test_all_zero_q_gives_equal_chunk_scores():
+    w = workloads.small_workload("n800_fp32", lengths=(300,))
+    inp = workloads.make_inputs(w)
+    inp.q.zero_()
+    out = oracle.pipeline(inp)
+    cs = out["chunk_scores"][0]
+    np.testing.assert_allclose(cs, cs[0], rtol=1e-13)
