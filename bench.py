@@ -1,0 +1,161 @@
+"""Benchmark of the token-importance path on one MI355X.
+
+One step = the whole path on one batch: sp_score_attention, sp_pool_chunk,
+sp_select_chunks and sp_gather_kept, from Q/K/token ids resident in HBM to
+the kept-token list. Prints one JSON line (rank 0) with whole-path throughput
+in prompt tokens per second, the scoring kernel's achieved HBM bandwidth
+against the 8 TB/s peak, and the CPU oracle timed on the host as a baseline.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--algo auto|two_pass|stream]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prompt tokens scored+selected/s at N=131072; % of HBM bandwidth roofline"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def score_algorithmic_bytes(inp) -> int:
+    """Bytes the scoring stage must move at least once: K and Q read, the
+    fp32 importance written."""
+    w = inp.workload
+    return inp.k.numel() * inp.k.element_size() + inp.q.numel() * inp.q.element_size() + \
+        4 * int(inp.offsets[-1])
+
+
+def cpu_baseline(inp, mode, param):
+    """The oracle as it stands, on the host cores, over the whole workload."""
+    import oracle
+    w = inp.workload
+    threads = oracle.max_threads()
+    used = min(threads, len(inp.lengths) * w.n_lookahead)
+    t0 = time.perf_counter()
+    oracle.pipeline(inp, mode, param)
+    dt = time.perf_counter() - t0
+    toks = int(inp.offsets[-1])
+    return {"value": toks / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"whole workload {w.name}: {len(inp.lengths)} prompt(s), {toks} tokens, all "
+                      f"{w.n_layers} layers; fp64 C loops with OpenMP over (prompt, step) pairs; "
+                      f"{dt:.2f} s",
+            "seconds": dt, "host_threads": threads}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="n128k_bf16")
+    ap.add_argument("--algo", default="auto")
+    ap.add_argument("--mode", default=None, help="top_p or mass (default: the workload's)")
+    ap.add_argument("--param", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
+              "(prompts of a batch are independent; see the sharding notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    from draft_attention_token_amd import specprefill as sp
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS[args.workload]
+    mode, param = (args.mode, args.param) if args.mode else w.select
+    log(f"generating {w.name}")
+    inp = workloads.make_inputs(w)
+    q, k, ids = inp.q.to(dev), inp.k.to(dev), inp.token_ids.to(dev)
+    torch.cuda.synchronize()
+    tokens = int(inp.offsets[-1])
+    pipe = sp.Pipeline(inp.offsets, w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                       w.n_lookahead, w.dtype, dev, W=w.pool_window, C=w.chunk_size,
+                       normalize=w.normalize, boost=w.boost, mode=mode, param=param,
+                       algo=args.algo)
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        pipe.run(q, k, ids)
+    torch.cuda.synchronize()
+
+    # Whole path: K steps between two events on the stream the calls use.
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    t_host = time.perf_counter()
+    for _ in range(args.steps):
+        pipe.run(q, k, ids)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"whole path {ms_step * 1e3:.1f} us/step (host clock {t_host / args.steps * 1e6:.1f} us)")
+
+    # Scoring stage alone, same stream, same inputs: per-launch average.
+    adesc = pipe.adesc
+    import ctypes
+    L = sp.lib()
+    st = ctypes.c_void_p(stream.cuda_stream)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(args.steps):
+        rc = L.sp_score_attention(ctypes.byref(adesc), pipe.batch.ref(), ctypes.c_void_p(q.data_ptr()),
+                                  ctypes.c_void_p(k.data_ptr()),
+                                  ctypes.c_void_p(pipe.importance.data_ptr()),
+                                  ctypes.c_void_p(pipe.ws_score.data_ptr()), pipe.ws_score.numel(), st)
+        assert rc == 0, sp.status_string(rc)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    ms_score = s0.elapsed_time(s1) / args.steps
+    alg_bytes = score_algorithmic_bytes(inp)
+    achieved = alg_bytes / (ms_score * 1e-3) / 1e9
+    log(f"scoring {ms_score * 1e3:.1f} us -> {achieved:.0f} GB/s algorithmic")
+
+    kept = int(pipe.kept_offsets[-1])
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "prompts": len(inp.lengths), "prompt_tokens": tokens,
+                   "lookahead": w.n_lookahead, "layers": w.n_layers, "q_heads": w.n_q_heads,
+                   "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "pool_window": w.pool_window,
+                   "chunk": w.chunk_size, "normalize": w.normalize, "boost": w.boost,
+                   "select": f"{mode} {param}", "score_algo": args.algo, "kept_tokens": kept},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "sp_score_attention", "launch_us": ms_score * 1e3,
+                     "algorithmic_bytes": alg_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(inp, mode, param)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

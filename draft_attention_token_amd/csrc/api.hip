@@ -1,0 +1,273 @@
+// C ABI of libspecprefill: argument checks, per-prompt tables, workspace
+// layout and launches. Every check runs before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include "sp_internal.h"
+
+using namespace sp;
+
+namespace {
+
+constexpr int64_t kMaxTotalTokens = (int64_t)1 << 30;   // keeps int32 token offsets safe
+
+// Checks a batch; on success fills N (per prompt) and the token total.
+sp_status check_batch(const sp_batch *batch, int64_t *total) {
+  if (!batch || !batch->token_offsets) return SP_ERR_INVALID_ARGUMENT;
+  if (batch->n_prompts < 1) return SP_ERR_INVALID_ARGUMENT;
+  if (batch->n_prompts > SP_MAX_PROMPTS) return SP_ERR_UNSUPPORTED;
+  const int64_t *off = batch->token_offsets;
+  if (off[0] != 0) return SP_ERR_INVALID_ARGUMENT;
+  for (int b = 0; b < batch->n_prompts; ++b)
+    if (off[b + 1] <= off[b]) return SP_ERR_INVALID_ARGUMENT;
+  if (off[batch->n_prompts] >= kMaxTotalTokens) return SP_ERR_UNSUPPORTED;
+  *total = off[batch->n_prompts];
+  return SP_OK;
+}
+
+// Table with unit_off[b] = prefix of ceil((N_b + extra) / per) and tok_off.
+SegTable make_table(const sp_batch *batch, int extra, int per, int L) {
+  SegTable t;
+  memset(&t, 0, sizeof(t));
+  t.B = batch->n_prompts;
+  t.L = L;
+  t.unit_off[0] = 0;
+  for (int b = 0; b < t.B; ++b) {
+    const int64_t n = batch->token_offsets[b + 1] - batch->token_offsets[b];
+    t.unit_off[b + 1] = t.unit_off[b] + (int32_t)((n + extra + per - 1) / per);
+    t.tok_off[b] = (int32_t)batch->token_offsets[b];
+  }
+  t.tok_off[t.B] = (int32_t)batch->token_offsets[t.B];
+  return t;
+}
+
+sp_status check_attn(const sp_attn_desc *d, AttnShape *s) {
+  if (!d) return SP_ERR_INVALID_ARGUMENT;
+  if (d->n_layers < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->n_lookahead < 1)
+    return SP_ERR_INVALID_ARGUMENT;
+  if (d->n_q_heads % d->n_kv_heads != 0) return SP_ERR_INVALID_ARGUMENT;
+  if (d->dtype != SP_DTYPE_F32 && d->dtype != SP_DTYPE_BF16) return SP_ERR_INVALID_ARGUMENT;
+  if (!(isfinite(d->scale))) return SP_ERR_INVALID_ARGUMENT;
+  if (d->algo < SP_SCORE_AUTO || d->algo > SP_SCORE_STREAM) return SP_ERR_INVALID_ARGUMENT;
+  if (d->head_dim != 64 && d->head_dim != 128) return SP_ERR_UNSUPPORTED;
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if ((int64_t)d->n_lookahead * G > kRows) return SP_ERR_UNSUPPORTED;
+  s->n_layers = d->n_layers;
+  s->Hq = d->n_q_heads;
+  s->Hkv = d->n_kv_heads;
+  s->d = d->head_dim;
+  s->L = d->n_lookahead;
+  s->G = G;
+  s->scale_log2 = d->scale * kLog2e;
+  s->dtype = d->dtype;
+  return SP_OK;
+}
+
+sp_status check_pool(const sp_pool_desc *d, PoolParams *p) {
+  if (!d) return SP_ERR_INVALID_ARGUMENT;
+  if (d->pool_window < 1 || d->pool_window % 2 == 0) return SP_ERR_INVALID_ARGUMENT;
+  if (d->pool_window > kMaxPoolWindow) return SP_ERR_UNSUPPORTED;
+  if (d->chunk_size < 1) return SP_ERR_INVALID_ARGUMENT;
+  if (d->chunk_size > 1024) return SP_ERR_UNSUPPORTED;
+  if (d->normalize != 0 && d->normalize != 1) return SP_ERR_INVALID_ARGUMENT;
+  if (d->boost_first_n < 0 || d->boost_last_n < 0) return SP_ERR_INVALID_ARGUMENT;
+  if (!(d->boost_first_mult > 0.f) || !(d->boost_last_mult > 0.f) ||
+      !isfinite(d->boost_first_mult) || !isfinite(d->boost_last_mult))
+    return SP_ERR_INVALID_ARGUMENT;
+  p->W = d->pool_window;
+  p->C = d->chunk_size;
+  p->normalize = d->normalize;
+  p->first_n = d->boost_first_n;
+  p->last_n = d->boost_last_n;
+  p->first_mult = d->boost_first_mult;
+  p->last_mult = d->boost_last_mult;
+  return SP_OK;
+}
+
+sp_status check_chunks(const sp_batch *batch, int32_t C, int *max_nc) {
+  if (C < 1) return SP_ERR_INVALID_ARGUMENT;
+  if (C > 1024) return SP_ERR_UNSUPPORTED;
+  int m = 0;
+  for (int b = 0; b < batch->n_prompts; ++b) {
+    const int64_t n = batch->token_offsets[b + 1] - batch->token_offsets[b];
+    const int64_t nc = (n + C - 1) / C;
+    if (nc > SP_MAX_CHUNKS_PER_PROMPT) return SP_ERR_UNSUPPORTED;
+    if (nc > m) m = (int)nc;
+  }
+  *max_nc = m;
+  return SP_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+sp_status launched(hipError_t e) { return e == hipSuccess ? SP_OK : SP_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int sp_abi_version(void) { return SP_ABI_VERSION; }
+
+const char *sp_status_string(int status) {
+  switch (status) {
+    case SP_OK: return "ok";
+    case SP_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SP_ERR_UNSUPPORTED: return "unsupported shape or size";
+    case SP_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case SP_ERR_DEVICE: return "device launch failed";
+    default: return "unknown status";
+  }
+}
+
+sp_status sp_score_workspace_bytes(const sp_attn_desc *desc, const sp_batch *batch,
+                                   size_t *bytes) {
+  if (!bytes) return SP_ERR_INVALID_ARGUMENT;
+  AttnShape s;
+  int64_t total;
+  sp_status st = check_attn(desc, &s);
+  if (st != SP_OK) return st;
+  if ((st = check_batch(batch, &total)) != SP_OK) return st;
+  const SegTable tiles = make_table(batch, s.L, kTile, s.L);
+  const int total_tiles = tiles.unit_off[tiles.B];
+  // Enough for whichever kernel the call may run (AUTO can fall back).
+  size_t need = score_two_pass_ws(s, tiles.B, total_tiles);
+  if (desc->algo != SP_SCORE_TWO_PASS && score_stream_supported(s, tiles.B, total_tiles)) {
+    const size_t ss = score_stream_ws(s, tiles.B, total_tiles);
+    need = desc->algo == SP_SCORE_STREAM ? ss : (ss > need ? ss : need);
+  }
+  *bytes = need;
+  return SP_OK;
+}
+
+sp_status sp_score_attention(const sp_attn_desc *desc, const sp_batch *batch, const void *q,
+                             const void *k, float *importance, void *ws, size_t ws_bytes,
+                             void *stream) {
+  AttnShape s;
+  int64_t total;
+  sp_status st = check_attn(desc, &s);
+  if (st != SP_OK) return st;
+  if ((st = check_batch(batch, &total)) != SP_OK) return st;
+  if (!q || !k || !importance) return SP_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k)) return SP_ERR_INVALID_ARGUMENT;
+  const SegTable tiles = make_table(batch, s.L, kTile, s.L);
+  const int total_tiles = tiles.unit_off[tiles.B];
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const bool stream_ok = score_stream_supported(s, tiles.B, total_tiles);
+  if (desc->algo == SP_SCORE_STREAM && !stream_ok) return SP_ERR_UNSUPPORTED;
+  if (desc->algo != SP_SCORE_TWO_PASS && stream_ok) {
+    const size_t need = score_stream_ws(s, tiles.B, total_tiles);
+    if (ws_bytes < need || (need && !ws)) return SP_ERR_WORKSPACE_TOO_SMALL;
+    bool supported = true;
+    hipError_t e = launch_score_stream(s, tiles, total_tiles, q, k, importance, ws, ws_bytes, hs,
+                                       &supported);
+    if (supported) return launched(e);
+    if (desc->algo == SP_SCORE_STREAM) return SP_ERR_UNSUPPORTED;
+  }
+  const size_t need = score_two_pass_ws(s, tiles.B, total_tiles);
+  if (ws_bytes < need || !ws) return SP_ERR_WORKSPACE_TOO_SMALL;
+  return launched(launch_score_two_pass(s, tiles, total_tiles, q, k, importance, ws, hs));
+}
+
+sp_status sp_pool_workspace_bytes(const sp_pool_desc *desc, const sp_batch *batch,
+                                  size_t *bytes) {
+  if (!bytes) return SP_ERR_INVALID_ARGUMENT;
+  PoolParams p;
+  int64_t total;
+  sp_status st = check_pool(desc, &p);
+  if (st != SP_OK) return st;
+  if ((st = check_batch(batch, &total)) != SP_OK) return st;
+  const SegTable blocks = make_table(batch, 0, kPoolBlockTokens, 0);
+  *bytes = pool_ws(blocks.B, blocks.unit_off[blocks.B], total);
+  return SP_OK;
+}
+
+sp_status sp_pool_chunk(const sp_pool_desc *desc, const sp_batch *batch, const float *importance,
+                        float *token_scores, float *chunk_scores, void *ws, size_t ws_bytes,
+                        void *stream) {
+  PoolParams p;
+  int64_t total;
+  int max_nc;
+  sp_status st = check_pool(desc, &p);
+  if (st != SP_OK) return st;
+  if ((st = check_batch(batch, &total)) != SP_OK) return st;
+  if ((st = check_chunks(batch, p.C, &max_nc)) != SP_OK) return st;
+  if (!importance || !chunk_scores) return SP_ERR_INVALID_ARGUMENT;
+  const SegTable blocks = make_table(batch, 0, kPoolBlockTokens, 0);
+  const SegTable chunks = make_table(batch, 0, p.C, 0);
+  const size_t need = pool_ws(blocks.B, blocks.unit_off[blocks.B], total);
+  if (ws_bytes < need || !ws) return SP_ERR_WORKSPACE_TOO_SMALL;
+  return launched(launch_pool_chunk(p, blocks, blocks.unit_off[blocks.B], chunks,
+                                    chunks.unit_off[chunks.B], importance, token_scores,
+                                    chunk_scores, ws, reinterpret_cast<hipStream_t>(stream)));
+}
+
+sp_status sp_select_workspace_bytes(const sp_batch *batch, int32_t chunk_size, size_t *bytes) {
+  if (!bytes) return SP_ERR_INVALID_ARGUMENT;
+  int64_t total;
+  int max_nc;
+  sp_status st = check_batch(batch, &total);
+  if (st != SP_OK) return st;
+  if ((st = check_chunks(batch, chunk_size, &max_nc)) != SP_OK) return st;
+  *bytes = 0;
+  return SP_OK;
+}
+
+sp_status sp_select_chunks(int32_t mode, double param, const sp_batch *batch, int32_t chunk_size,
+                           const float *chunk_scores, uint8_t *keep, int32_t *n_kept_chunks,
+                           void *ws, size_t ws_bytes, void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int64_t total;
+  int max_nc;
+  if (mode != SP_SELECT_TOP_P && mode != SP_SELECT_MASS) return SP_ERR_INVALID_ARGUMENT;
+  if (!(param > 0.0) || !(param <= 1.0)) return SP_ERR_INVALID_ARGUMENT;
+  sp_status st = check_batch(batch, &total);
+  if (st != SP_OK) return st;
+  if ((st = check_chunks(batch, chunk_size, &max_nc)) != SP_OK) return st;
+  if (!chunk_scores || !keep || !n_kept_chunks) return SP_ERR_INVALID_ARGUMENT;
+  const SegTable chunks = make_table(batch, 0, chunk_size, 0);
+  SelectBudget kc;
+  memset(&kc, 0, sizeof(kc));
+  for (int b = 0; b < chunks.B; ++b) {
+    const int64_t nc = chunks.unit_off[b + 1] - chunks.unit_off[b];
+    int64_t v = (int64_t)ceil(param * (double)nc - 1e-9);
+    if (v > nc) v = nc;
+    if (v < 1) v = 1;
+    kc.kc[b] = (int32_t)v;
+  }
+  return launched(launch_select(mode, param, chunks, kc, max_nc, chunk_scores, keep,
+                                n_kept_chunks, reinterpret_cast<hipStream_t>(stream)));
+}
+
+sp_status sp_gather_workspace_bytes(const sp_batch *batch, int32_t chunk_size, size_t *bytes) {
+  if (!bytes) return SP_ERR_INVALID_ARGUMENT;
+  int64_t total;
+  int max_nc;
+  sp_status st = check_batch(batch, &total);
+  if (st != SP_OK) return st;
+  if ((st = check_chunks(batch, chunk_size, &max_nc)) != SP_OK) return st;
+  const SegTable chunks = make_table(batch, 0, chunk_size, 0);
+  *bytes = gather_ws(chunks.B, chunks.unit_off[chunks.B]);
+  return SP_OK;
+}
+
+sp_status sp_gather_kept(const sp_batch *batch, int32_t chunk_size, const uint8_t *keep,
+                         const int32_t *token_ids, int32_t *kept_ids, int32_t *kept_pos,
+                         int64_t *kept_offsets, void *ws, size_t ws_bytes, void *stream) {
+  int64_t total;
+  int max_nc;
+  sp_status st = check_batch(batch, &total);
+  if (st != SP_OK) return st;
+  if ((st = check_chunks(batch, chunk_size, &max_nc)) != SP_OK) return st;
+  if (!keep || !token_ids || !kept_ids || !kept_pos || !kept_offsets)
+    return SP_ERR_INVALID_ARGUMENT;
+  const SegTable chunks = make_table(batch, 0, chunk_size, 0);
+  const SegTable blocks = make_table(batch, 0, kGatherBlockTokens, 0);
+  const size_t need = gather_ws(chunks.B, chunks.unit_off[chunks.B]);
+  if (ws_bytes < need || !ws) return SP_ERR_WORKSPACE_TOO_SMALL;
+  return launched(launch_gather(chunks, blocks, blocks.unit_off[blocks.B], chunk_size, keep,
+                                token_ids, kept_ids, kept_pos, kept_offsets, ws,
+                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

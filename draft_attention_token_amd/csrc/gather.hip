@@ -1,0 +1,111 @@
+// Kept-token compaction: BOS plus every token of a kept chunk, in ascending
+// order, with its token id and original position.
+//
+// Method: "SpecPrefill — Implementation Guide", Sparse Prefill (the target
+// prefills only the kept tokens at their original position ids);
+// "Speculative prefill" (llama.cpp pull request 27692), Approach step 4
+// (kept chunks plus BOS).
+//
+// k_gather_scan: one block per prompt; an exact integer scan over the kept
+//   chunks gives each chunk's first output slot and the prompt's count
+//   (kept chunk tokens, plus one when BOS sits in a dropped chunk 0).
+// k_gather_write: one block per 1024 tokens; every kept token's slot follows
+//   from its chunk's slot, so the writes need no further scan.
+#include "sp_internal.h"
+
+namespace sp {
+namespace {
+
+constexpr int kScanThreads = 1024;
+constexpr int kWriteThreads = 256;
+
+__global__ __launch_bounds__(kScanThreads) void k_gather_scan(SegTable chunks, int C,
+                                                              const uint8_t *__restrict__ keep,
+                                                              int32_t *__restrict__ chunk_out,
+                                                              int32_t *__restrict__ counts) {
+  __shared__ int part[kScanThreads];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int c0 = chunks.unit_off[b], nc = chunks.unit_off[b + 1] - c0;
+  const int N = chunks.tok_off[b + 1] - chunks.tok_off[b];
+  const int per = (nc + kScanThreads - 1) / kScanThreads;
+  const int a0 = min(nc, tid * per), a1 = min(nc, a0 + per);
+  int s = 0;
+  for (int c = a0; c < a1; ++c)
+    if (keep[c0 + c]) s += min(C, N - c * C);
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < kScanThreads; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = tid > 0 ? part[tid - 1] : 0;
+  for (int c = a0; c < a1; ++c) {
+    chunk_out[c0 + c] = run;
+    if (keep[c0 + c]) run += min(C, N - c * C);
+  }
+  if (tid == kScanThreads - 1) counts[b] = part[kScanThreads - 1] + (keep[c0] ? 0 : 1);
+}
+
+__global__ __launch_bounds__(kWriteThreads) void k_gather_write(
+    SegTable chunks, SegTable blocks, int C, const uint8_t *__restrict__ keep,
+    const int32_t *__restrict__ chunk_out, const int32_t *__restrict__ counts,
+    const int32_t *__restrict__ ids, int32_t *__restrict__ kept_ids,
+    int32_t *__restrict__ kept_pos, int64_t *__restrict__ kept_offsets) {
+  __shared__ int64_t base_s;
+  const int blk = blockIdx.x, tid = threadIdx.x;
+  const int b = seg_of(blocks, blk);
+  if (tid == 0) {
+    int64_t acc = 0;
+    for (int i = 0; i < b; ++i) acc += counts[i];
+    base_s = acc;
+    if (blk == 0) {
+      int64_t o = 0;
+      kept_offsets[0] = 0;
+      for (int i = 0; i < blocks.B; ++i) {
+        o += counts[i];
+        kept_offsets[i + 1] = o;
+      }
+    }
+  }
+  __syncthreads();
+  const int64_t base = base_s;
+  const int c0 = chunks.unit_off[b];
+  const int64_t tok0 = blocks.tok_off[b];
+  const int N = blocks.tok_off[b + 1] - blocks.tok_off[b];
+  const int t0 = (blk - blocks.unit_off[b]) * kGatherBlockTokens;
+  const int t1 = min(N, t0 + kGatherBlockTokens);
+  const bool k0 = keep[c0] != 0;
+  for (int t = t0 + tid; t < t1; t += kWriteThreads) {
+    const int c = t / C;
+    int64_t out;
+    if (t == 0 && !k0) out = base;
+    else if (keep[c0 + c]) out = base + (k0 ? 0 : 1) + chunk_out[c0 + c] + (t - c * C);
+    else continue;
+    kept_ids[out] = ids[tok0 + t];
+    kept_pos[out] = t;
+  }
+}
+
+}  // namespace
+
+size_t gather_ws(int B, int total_chunks) {
+  return align_up((size_t)total_chunks * sizeof(int32_t)) + align_up((size_t)B * sizeof(int32_t));
+}
+
+hipError_t launch_gather(const SegTable &chunks, const SegTable &blocks, int total_blocks, int C,
+                         const uint8_t *keep, const int32_t *ids, int32_t *kept_ids,
+                         int32_t *kept_pos, int64_t *kept_offsets, void *ws, hipStream_t st) {
+  const int total_chunks = chunks.unit_off[chunks.B];
+  int32_t *chunk_out = reinterpret_cast<int32_t *>(ws);
+  int32_t *counts = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(ws) +
+                                                align_up((size_t)total_chunks * sizeof(int32_t)));
+  hipLaunchKernelGGL(k_gather_scan, dim3(chunks.B), dim3(kScanThreads), 0, st, chunks, C, keep,
+                     chunk_out, counts);
+  hipLaunchKernelGGL(k_gather_write, dim3(total_blocks), dim3(kWriteThreads), 0, st, chunks, blocks,
+                     C, keep, chunk_out, counts, ids, kept_ids, kept_pos, kept_offsets);
+  return hipGetLastError();
+}
+
+}  // namespace sp

@@ -1,0 +1,169 @@
+// Token importance, two-pass form: a statistics pass computes each softmax
+// row's log-sum-exp over all keys it sees; a second pass recomputes the
+// logits, turns them into probabilities, and reduces max over heads and
+// layers and the mean over lookahead steps. K is read from HBM twice.
+//
+// Method: "SpecPrefill — Implementation Guide", How It Works / Token
+// Importance (max over heads, then layers, then mean over lookahead steps),
+// and "Speculative prefill" (llama.cpp pull request 27692), Approach
+// steps 2-3. Causality: query j of a prompt sits at position N + j and sees
+// keys 0 .. N + j; only the N prompt columns receive importance.
+#include "score_common.h"
+
+namespace sp {
+namespace {
+
+// Logits of one 32-key tile of one (layer, KV group) for the lane; returns
+// the tile context through the out-parameters.
+struct TileCtx {
+  int b;          // prompt
+  int64_t N;      // prompt tokens
+  int64_t nkeys;  // N + L keys
+  int64_t key0;   // global key row of the prompt's key 0
+  int64_t kl;     // local key index of this lane's column
+};
+
+__device__ __forceinline__ TileCtx tile_ctx(const SegTable &tiles, int t, int col) {
+  TileCtx c;
+  c.b = seg_of(tiles, t);
+  c.N = tiles.tok_off[c.b + 1] - tiles.tok_off[c.b];
+  c.nkeys = c.N + tiles.L;
+  c.key0 = tiles.tok_off[c.b] + (int64_t)c.b * tiles.L;
+  c.kl = (int64_t)(t - tiles.unit_off[c.b]) * kTile + col;
+  return c;
+}
+
+template <typename T, int D>
+__device__ __forceinline__ f32x16 tile_logits(const AttnShape &s, const TileCtx &c,
+                                              int64_t total_keys, const T *q, const T *k, int l,
+                                              int g, int lane) {
+  const int half = lane >> 5, r = lane & 31;
+  Frag<T, D> a, bk;
+  if (r < s.L * s.G) a.load_cached(q_row_ptr(q, s, c.b, l, g, r), half); else a.zero();
+  if (c.kl < c.nkeys) bk.load(k_row_ptr(k, s, total_keys, l, c.key0 + c.kl, g), half); else bk.zero();
+  return mfma_tile<D>(a, bk);
+}
+
+// Pass 1: per (tile, layer, group), the base-2 max and sum of 2^(logit - max)
+// of each of the 32 rows over the tile's visible keys.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void k_stats(AttnShape s, SegTable tiles, int64_t total_keys,
+                                              int total_tiles, const T *__restrict__ q,
+                                              const T *__restrict__ k, float2 *__restrict__ part) {
+  const int t = blockIdx.x, prob = blockIdx.y;
+  const int l = prob / s.Hkv, g = prob - l * s.Hkv;
+  const int lane = threadIdx.x, half = lane >> 5, col = lane & 31;
+  const TileCtx c = tile_ctx(tiles, t, col);
+  const f32x16 acc = tile_logits<T, D>(s, c, total_keys, q, k, l, g, lane);
+  const int rows = s.L * s.G;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = acc_row(i, half);
+    const int j = row / s.G;
+    const bool vis = row < rows && c.kl < c.nkeys && c.kl <= c.N + j;
+    const float x = vis ? acc[i] * s.scale_log2 : -INFINITY;
+    const float m = wave_max32(x);
+    const float e = vis ? exp2f(x - m) : 0.f;
+    const float z = wave_sum32(e);
+    if (col == 0) part[((int64_t)prob * total_tiles + t) * kRows + row] = make_float2(m, z);
+  }
+}
+
+// Combine the tile statistics of each (prompt, layer, group, row) in a fixed
+// order: lse2 = m + log2(z) (base-2 log-sum-exp of the row's logits).
+__global__ __launch_bounds__(256) void k_lse(SegTable tiles, int n_prob, int total_tiles,
+                                             const float2 *__restrict__ part,
+                                             float *__restrict__ lse) {
+  __shared__ float2 sm[8][kRows];
+  const int b = blockIdx.x, prob = blockIdx.y;
+  const int row = threadIdx.x & 31, p = threadIdx.x >> 5;
+  const int t0 = tiles.unit_off[b], t1 = tiles.unit_off[b + 1];
+  const int per = (t1 - t0 + 7) / 8;
+  const int ta = t0 + p * per, tb = min(t1, ta + per);
+  float M = -INFINITY, Z = 0.f;
+  for (int t = ta; t < tb; ++t) {
+    const float2 v = part[((int64_t)prob * total_tiles + t) * kRows + row];
+    stats_merge(M, Z, v.x, v.y);
+  }
+  sm[p][row] = make_float2(M, Z);
+  __syncthreads();
+  if (p == 0) {
+    for (int i = 1; i < 8; ++i) stats_merge(M, Z, sm[i][row].x, sm[i][row].y);
+    lse[((int64_t)b * n_prob + prob) * kRows + row] = (Z > 0.f) ? M + log2f(Z) : INFINITY;
+  }
+}
+
+// Pass 2: per tile, loop over all layers and groups; p = 2^(x - lse2); the
+// step-max over (layer, head) lives in LDS as ordered uint (p >= 0, so the
+// float bits order like the values); then the mean over steps.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void k_score(AttnShape s, SegTable tiles, int64_t total_keys,
+                                              const T *__restrict__ q, const T *__restrict__ k,
+                                              const float *__restrict__ lse,
+                                              float *__restrict__ imp) {
+  __shared__ unsigned smax[kRows][kTile];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x, half = lane >> 5, col = lane & 31;
+  for (int i = lane; i < kRows * kTile; i += 64) (&smax[0][0])[i] = 0u;
+  __syncthreads();
+  const TileCtx c = tile_ctx(tiles, t, col);
+  const int n_prob = s.n_layers * s.Hkv, rows = s.L * s.G;
+  const bool prompt_key = c.kl < c.N;
+  for (int prob = 0; prob < n_prob; ++prob) {
+    const int l = prob / s.Hkv, g = prob - l * s.Hkv;
+    const f32x16 acc = tile_logits<T, D>(s, c, total_keys, q, k, l, g, lane);
+    const float *lrow = lse + ((int64_t)c.b * n_prob + prob) * kRows;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = acc_row(i, half);
+      if (row < rows && prompt_key) {
+        const float p = exp2f(acc[i] * s.scale_log2 - lrow[row]);
+        atomicMax(&smax[row / s.G][col], __float_as_uint(p));
+      }
+    }
+  }
+  __syncthreads();
+  if (lane < 32 && prompt_key) {
+    float acc = 0.f;
+    for (int j = 0; j < s.L; ++j) acc += __uint_as_float(smax[j][col]);
+    imp[tiles.tok_off[c.b] + c.kl] = acc / (float)s.L;
+  }
+}
+
+template <typename T, int D>
+hipError_t run(const AttnShape &s, const SegTable &tiles, int total_tiles, const void *q,
+               const void *k, float *imp, void *ws, hipStream_t st) {
+  const int n_prob = s.n_layers * s.Hkv;
+  const int64_t total_keys = tiles.tok_off[tiles.B] + (int64_t)tiles.B * tiles.L;
+  float2 *part = reinterpret_cast<float2 *>(ws);
+  float *lse = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) +
+                                         align_up((size_t)n_prob * total_tiles * kRows * sizeof(float2)));
+  hipLaunchKernelGGL((k_stats<T, D>), dim3(total_tiles, n_prob), dim3(64), 0, st, s, tiles,
+                     total_keys, total_tiles, (const T *)q, (const T *)k, part);
+  hipLaunchKernelGGL(k_lse, dim3(tiles.B, n_prob), dim3(256), 0, st, tiles, n_prob, total_tiles,
+                     part, lse);
+  hipLaunchKernelGGL((k_score<T, D>), dim3(total_tiles), dim3(64), 0, st, s, tiles, total_keys,
+                     (const T *)q, (const T *)k, lse, imp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t score_two_pass_ws(const AttnShape &s, int B, int total_tiles) {
+  const size_t n_prob = (size_t)s.n_layers * s.Hkv;
+  return align_up(n_prob * total_tiles * kRows * sizeof(float2)) +
+         align_up((size_t)B * n_prob * kRows * sizeof(float));
+}
+
+hipError_t launch_score_two_pass(const AttnShape &s, const SegTable &tiles, int total_tiles,
+                                 const void *q, const void *k, float *imp, void *ws,
+                                 hipStream_t st) {
+  if (s.dtype == SP_DTYPE_BF16) {
+    if (s.d == 128) return run<__bf16, 128>(s, tiles, total_tiles, q, k, imp, ws, st);
+    return run<__bf16, 64>(s, tiles, total_tiles, q, k, imp, ws, st);
+  }
+  if (s.d == 128) return run<float, 128>(s, tiles, total_tiles, q, k, imp, ws, st);
+  return run<float, 64>(s, tiles, total_tiles, q, k, imp, ws, st);
+}
+
+}  // namespace sp

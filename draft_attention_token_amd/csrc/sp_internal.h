@@ -1,0 +1,82 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "specprefill.h"
+
+namespace sp {
+
+constexpr int kTile = 32;          // keys per MFMA tile (the 32-wide N of 32x32 MFMA)
+constexpr int kRows = 32;          // query rows per MFMA tile: (lookahead step, head in group)
+constexpr size_t kAlign = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Per-prompt prefix table passed to kernels by value (about 1 KB). unit_off
+// holds a host-computed prefix of per-prompt unit counts (tiles, chunks or
+// token blocks, depending on the kernel); tok_off the prompt token offsets
+// (the library rejects batches of 2^31 tokens or more).
+struct SegTable {
+  int32_t B;
+  int32_t L;                          // lookahead keys per prompt (0 where unused)
+  int32_t unit_off[SP_MAX_PROMPTS + 1];
+  int32_t tok_off[SP_MAX_PROMPTS + 1];
+};
+
+// Prompt that owns global unit u (unit_off is non-decreasing, u < unit_off[B]).
+__device__ __forceinline__ int seg_of(const SegTable &t, int32_t u) {
+  int lo = 0, hi = t.B - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (t.unit_off[mid] <= u) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct AttnShape {
+  int n_layers, Hq, Hkv, d, L, G;
+  float scale_log2;                 // scale * log2(e): logits kept in base-2 units
+  int dtype;
+};
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_score_two_pass(const AttnShape &s, const SegTable &tiles, int total_tiles,
+                                 const void *q, const void *k, float *imp, void *ws,
+                                 hipStream_t st);
+size_t score_two_pass_ws(const AttnShape &s, int B, int total_tiles);
+
+hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, int total_tiles,
+                               const void *q, const void *k, float *imp, void *ws,
+                               size_t ws_bytes, hipStream_t st, bool *supported);
+size_t score_stream_ws(const AttnShape &s, int B, int total_tiles);
+bool score_stream_supported(const AttnShape &s, int B, int total_tiles);
+
+struct PoolParams {
+  int W, C, normalize, first_n, last_n;
+  float first_mult, last_mult;
+};
+hipError_t launch_pool_chunk(const PoolParams &p, const SegTable &blocks, int total_blocks,
+                             const SegTable &chunks, int total_chunks, const float *imp,
+                             float *token_scores, float *chunk_scores, void *ws, hipStream_t st);
+constexpr int kPoolBlockTokens = 1024;
+constexpr int kMaxPoolWindow = 129;
+size_t pool_ws(int B, int total_blocks, int64_t total_tokens);
+
+// Per-prompt top-p chunk budgets (host-computed), passed by value.
+struct SelectBudget {
+  int32_t kc[SP_MAX_PROMPTS];
+};
+hipError_t launch_select(int mode, double param, const SegTable &chunks, const SelectBudget &kc,
+                         int max_nc, const float *chunk_scores, uint8_t *keep, int32_t *n_kept,
+                         hipStream_t st);
+
+hipError_t launch_gather(const SegTable &chunks, const SegTable &blocks, int total_blocks, int C,
+                         const uint8_t *keep, const int32_t *ids, int32_t *kept_ids,
+                         int32_t *kept_pos, int64_t *kept_offsets, void *ws, hipStream_t st);
+constexpr int kGatherBlockTokens = 1024;
+size_t gather_ws(int B, int total_chunks);
+
+}  // namespace sp

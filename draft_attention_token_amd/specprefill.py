@@ -1,0 +1,327 @@
+"""Python binding of libspecprefill (ctypes; argument marshalling only).
+
+Every step of the path runs in the library's HIP kernels. torch is used for
+device memory and the current HIP stream. Importing this module does not need
+a GPU; calling a function does. If the shared library is missing, every call
+raises: there is no fallback path.
+
+Functions mirror the C ABI in ``include/specprefill.h``:
+
+* :func:`sp_score_attention` (Q, K -> importance)
+* :func:`sp_pool_chunk` (importance -> token scores, chunk scores)
+* :func:`sp_select_chunks` (chunk scores -> keep flags, kept-chunk counts)
+* :func:`sp_gather_kept` (keep flags, token ids -> kept ids, positions, offsets)
+
+``offsets`` is always the host-side ``[B + 1]`` int64 prompt-token offsets.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecprefill.so")
+
+SP_OK, SP_ERR_INVALID_ARGUMENT, SP_ERR_UNSUPPORTED, SP_ERR_WORKSPACE_TOO_SMALL, SP_ERR_DEVICE = range(5)
+SP_DTYPE_F32, SP_DTYPE_BF16 = 0, 1
+SP_SELECT_TOP_P, SP_SELECT_MASS = 0, 1
+SP_SCORE_AUTO, SP_SCORE_TWO_PASS, SP_SCORE_STREAM = 0, 1, 2
+SP_MAX_PROMPTS = 128
+
+EXPORTED = [
+    "sp_abi_version", "sp_status_string", "sp_score_workspace_bytes", "sp_pool_workspace_bytes",
+    "sp_select_workspace_bytes", "sp_gather_workspace_bytes", "sp_score_attention",
+    "sp_pool_chunk", "sp_select_chunks", "sp_gather_kept",
+]
+
+_ALGOS = {"auto": SP_SCORE_AUTO, "two_pass": SP_SCORE_TWO_PASS, "stream": SP_SCORE_STREAM}
+_MODES = {"top_p": SP_SELECT_TOP_P, "mass": SP_SELECT_MASS}
+
+
+class SpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class sp_batch(ctypes.Structure):
+    _fields_ = [("n_prompts", ctypes.c_int32), ("token_offsets", ctypes.POINTER(ctypes.c_int64))]
+
+
+class sp_attn_desc(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("n_lookahead", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("algo", ctypes.c_int32)]
+
+
+class sp_pool_desc(ctypes.Structure):
+    _fields_ = [("pool_window", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
+                ("normalize", ctypes.c_int32), ("boost_first_n", ctypes.c_int32),
+                ("boost_first_mult", ctypes.c_float), ("boost_last_n", ctypes.c_int32),
+                ("boost_last_mult", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded shared library; raises if it was not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libspecprefill.so not found at {LIB_PATH}; build it with "
+                               "`python -m draft_attention_token_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, szp = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)
+        bp = ctypes.POINTER(sp_batch)
+        L.sp_abi_version.restype = ctypes.c_int
+        L.sp_status_string.argtypes = [ctypes.c_int]
+        L.sp_status_string.restype = ctypes.c_char_p
+        L.sp_score_workspace_bytes.argtypes = [ctypes.POINTER(sp_attn_desc), bp, szp]
+        L.sp_pool_workspace_bytes.argtypes = [ctypes.POINTER(sp_pool_desc), bp, szp]
+        L.sp_select_workspace_bytes.argtypes = [bp, ctypes.c_int32, szp]
+        L.sp_gather_workspace_bytes.argtypes = [bp, ctypes.c_int32, szp]
+        L.sp_score_attention.argtypes = [ctypes.POINTER(sp_attn_desc), bp, vp, vp, vp, vp, sz, vp]
+        L.sp_pool_chunk.argtypes = [ctypes.POINTER(sp_pool_desc), bp, vp, vp, vp, vp, sz, vp]
+        L.sp_select_chunks.argtypes = [ctypes.c_int32, ctypes.c_double, bp, ctypes.c_int32, vp, vp,
+                                       vp, vp, sz, vp]
+        L.sp_gather_kept.argtypes = [bp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, sz, vp]
+        for name in EXPORTED[2:]:
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().sp_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != SP_OK:
+        raise SpError(status, where)
+
+
+class Batch:
+    """Host-side batch descriptor; keeps the offsets array alive."""
+
+    def __init__(self, offsets):
+        if isinstance(offsets, torch.Tensor):
+            offsets = offsets.detach().cpu().numpy()
+        self.offsets = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+        self.struct = sp_batch(len(self.offsets) - 1,
+                               self.offsets.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+
+    @property
+    def B(self) -> int:
+        return len(self.offsets) - 1
+
+    @property
+    def total(self) -> int:
+        return int(self.offsets[-1])
+
+    def n_chunks(self, C: int) -> int:
+        return int(sum((int(self.offsets[b + 1] - self.offsets[b]) + C - 1) // C for b in range(self.B)))
+
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype, scale=None,
+              algo="auto") -> sp_attn_desc:
+    dt = {torch.float32: SP_DTYPE_F32, torch.bfloat16: SP_DTYPE_BF16}.get(dtype, -1)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return sp_attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dt, float(scale),
+                        _ALGOS[algo] if isinstance(algo, str) else int(algo))
+
+
+def pool_desc(W=13, C=32, normalize=True, first_n=64, first_mult=1.5, last_n=128,
+              last_mult=1.3) -> sp_pool_desc:
+    return sp_pool_desc(W, C, int(bool(normalize)), first_n, first_mult, last_n, last_mult)
+
+
+def score_workspace_bytes(desc: sp_attn_desc, batch: Batch) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().sp_score_workspace_bytes(ctypes.byref(desc), batch.ref(), ctypes.byref(n)),
+           "sp_score_workspace_bytes")
+    return n.value
+
+
+def pool_workspace_bytes(desc: sp_pool_desc, batch: Batch) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().sp_pool_workspace_bytes(ctypes.byref(desc), batch.ref(), ctypes.byref(n)),
+           "sp_pool_workspace_bytes")
+    return n.value
+
+
+def select_workspace_bytes(batch: Batch, C: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().sp_select_workspace_bytes(batch.ref(), C, ctypes.byref(n)),
+           "sp_select_workspace_bytes")
+    return n.value
+
+
+def gather_workspace_bytes(batch: Batch, C: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().sp_gather_workspace_bytes(batch.ref(), C, ctypes.byref(n)),
+           "sp_gather_workspace_bytes")
+    return n.value
+
+
+def sp_score_attention(q: torch.Tensor, k: torch.Tensor, offsets, n_layers: int, n_q_heads: int,
+                       n_kv_heads: int, head_dim: int, n_lookahead: int, scale=None,
+                       algo="auto", out: Optional[torch.Tensor] = None,
+                       ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Token importance [sum N_b] fp32 (see the C header for layouts)."""
+    batch = offsets if isinstance(offsets, Batch) else Batch(offsets)
+    desc = attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, q.dtype, scale, algo)
+    if not (q.is_contiguous() and k.is_contiguous()):
+        raise ValueError("q and k must be contiguous")
+    if q.dtype != k.dtype:
+        raise ValueError("q and k must share a dtype")
+    if q.numel() != batch.B * n_layers * n_lookahead * n_q_heads * head_dim:
+        raise ValueError("q has the wrong number of elements")
+    if k.numel() != n_layers * (batch.total + batch.B * n_lookahead) * n_kv_heads * head_dim:
+        raise ValueError("k has the wrong number of elements")
+    dev = q.device
+    if out is None:
+        out = torch.empty(batch.total, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _ws(score_workspace_bytes(desc, batch), dev)
+    _check(lib().sp_score_attention(ctypes.byref(desc), batch.ref(), _ptr(q), _ptr(k), _ptr(out),
+                                    _ptr(ws), ws.numel(), _stream(dev)), "sp_score_attention")
+    return out
+
+
+def sp_pool_chunk(importance: torch.Tensor, offsets, W=13, C=32, normalize=True, first_n=64,
+                  first_mult=1.5, last_n=128, last_mult=1.3, token_scores: bool = True,
+                  out_tokens=None, out_chunks=None, ws=None):
+    """(token_scores [sum N_b] or None, chunk_scores [sum nc_b]) fp32."""
+    batch = offsets if isinstance(offsets, Batch) else Batch(offsets)
+    desc = pool_desc(W, C, normalize, first_n, first_mult, last_n, last_mult)
+    if importance.dtype != torch.float32 or importance.numel() != batch.total:
+        raise ValueError("importance must be fp32 [sum N_b]")
+    dev = importance.device
+    if token_scores and out_tokens is None:
+        out_tokens = torch.empty(batch.total, dtype=torch.float32, device=dev)
+    if out_chunks is None:
+        out_chunks = torch.empty(batch.n_chunks(C) if C > 0 else 1, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _ws(pool_workspace_bytes(desc, batch), dev)
+    _check(lib().sp_pool_chunk(ctypes.byref(desc), batch.ref(), _ptr(importance),
+                               _ptr(out_tokens if token_scores else None), _ptr(out_chunks),
+                               _ptr(ws), ws.numel(), _stream(dev)), "sp_pool_chunk")
+    return (out_tokens if token_scores else None), out_chunks
+
+
+def sp_select_chunks(chunk_scores: torch.Tensor, offsets, C: int, mode: str, param: float,
+                     out_keep=None, out_counts=None):
+    """(keep [sum nc_b] uint8, n_kept_chunks [B] int32)."""
+    batch = offsets if isinstance(offsets, Batch) else Batch(offsets)
+    if chunk_scores.dtype != torch.float32:
+        raise ValueError("chunk_scores must be fp32")
+    dev = chunk_scores.device
+    if out_keep is None:
+        out_keep = torch.empty(chunk_scores.numel(), dtype=torch.uint8, device=dev)
+    if out_counts is None:
+        out_counts = torch.empty(batch.B, dtype=torch.int32, device=dev)
+    m = _MODES[mode] if isinstance(mode, str) else int(mode)
+    _check(lib().sp_select_chunks(m, float(param), batch.ref(), C, _ptr(chunk_scores),
+                                  _ptr(out_keep), _ptr(out_counts), ctypes.c_void_p(0), 0,
+                                  _stream(dev)), "sp_select_chunks")
+    return out_keep, out_counts
+
+
+def sp_gather_kept(keep: torch.Tensor, token_ids: torch.Tensor, offsets, C: int,
+                   out_ids=None, out_pos=None, out_offsets=None, ws=None):
+    """(kept_ids [sum N_b] int32, kept_pos [sum N_b] int32, kept_offsets [B+1] int64).
+
+    Only the first kept_offsets[B] entries of kept_ids / kept_pos are written.
+    """
+    batch = offsets if isinstance(offsets, Batch) else Batch(offsets)
+    if token_ids.dtype != torch.int32 or keep.dtype != torch.uint8:
+        raise ValueError("token_ids must be int32 and keep uint8")
+    dev = token_ids.device
+    if out_ids is None:
+        out_ids = torch.empty(batch.total, dtype=torch.int32, device=dev)
+    if out_pos is None:
+        out_pos = torch.empty(batch.total, dtype=torch.int32, device=dev)
+    if out_offsets is None:
+        out_offsets = torch.empty(batch.B + 1, dtype=torch.int64, device=dev)
+    if ws is None:
+        ws = _ws(gather_workspace_bytes(batch, C), dev)
+    _check(lib().sp_gather_kept(batch.ref(), C, _ptr(keep), _ptr(token_ids), _ptr(out_ids),
+                                _ptr(out_pos), _ptr(out_offsets), _ptr(ws), ws.numel(),
+                                _stream(dev)), "sp_gather_kept")
+    return out_ids, out_pos, out_offsets
+
+
+class Pipeline:
+    """All four calls on preallocated buffers (what the benchmark times).
+
+    Holds device buffers for one batch shape; :meth:`run` enqueues the whole
+    path on the current stream and returns nothing (results stay in the
+    attributes ``importance``, ``token_scores``, ``chunk_scores``, ``keep``,
+    ``n_kept``, ``kept_ids``, ``kept_pos``, ``kept_offsets``).
+    """
+
+    def __init__(self, offsets, n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype,
+                 device, W=13, C=32, normalize=True, boost=True, mode="mass", param=0.85,
+                 algo="auto", scale=None, token_scores=True):
+        self.batch = offsets if isinstance(offsets, Batch) else Batch(offsets)
+        fm, lm = (1.5, 1.3) if boost else (1.0, 1.0)
+        self.adesc = attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype,
+                               scale, algo)
+        self.pdesc = pool_desc(W, C, normalize, 64, fm, 128, lm)
+        self.C, self.mode, self.param = C, _MODES[mode], float(param)
+        self.shape = (n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead)
+        B, T, nc = self.batch.B, self.batch.total, self.batch.n_chunks(C)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.importance = torch.empty(T, **f32)
+        self.token_scores = torch.empty(T, **f32) if token_scores else None
+        self.chunk_scores = torch.empty(nc, **f32)
+        self.keep = torch.empty(nc, dtype=torch.uint8, device=device)
+        self.n_kept = torch.empty(B, dtype=torch.int32, device=device)
+        self.kept_ids = torch.empty(T, dtype=torch.int32, device=device)
+        self.kept_pos = torch.empty(T, dtype=torch.int32, device=device)
+        self.kept_offsets = torch.empty(B + 1, dtype=torch.int64, device=device)
+        self.ws_score = _ws(score_workspace_bytes(self.adesc, self.batch), device)
+        self.ws_pool = _ws(pool_workspace_bytes(self.pdesc, self.batch), device)
+        self.ws_gather = _ws(gather_workspace_bytes(self.batch, C), device)
+        self.device = device
+
+    def run(self, q: torch.Tensor, k: torch.Tensor, token_ids: torch.Tensor):
+        L = lib()
+        st = _stream(self.device)
+        b = self.batch.ref()
+        _check(L.sp_score_attention(ctypes.byref(self.adesc), b, _ptr(q), _ptr(k),
+                                    _ptr(self.importance), _ptr(self.ws_score),
+                                    self.ws_score.numel(), st), "sp_score_attention")
+        _check(L.sp_pool_chunk(ctypes.byref(self.pdesc), b, _ptr(self.importance),
+                               _ptr(self.token_scores), _ptr(self.chunk_scores),
+                               _ptr(self.ws_pool), self.ws_pool.numel(), st), "sp_pool_chunk")
+        _check(L.sp_select_chunks(self.mode, self.param, b, self.C, _ptr(self.chunk_scores),
+                                  _ptr(self.keep), _ptr(self.n_kept), ctypes.c_void_p(0), 0, st),
+               "sp_select_chunks")
+        _check(L.sp_gather_kept(b, self.C, _ptr(self.keep), _ptr(token_ids), _ptr(self.kept_ids),
+                                _ptr(self.kept_pos), _ptr(self.kept_offsets),
+                                _ptr(self.ws_gather), self.ws_gather.numel(), st),
+               "sp_gather_kept")

@@ -1,0 +1,196 @@
+/*
+ * libspecprefill: token-importance hot path of Speculative Prefill on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * A small draft model's lookahead queries attend over the whole prompt; the
+ * attention they pay to each prompt token decides which 32-token chunks of the
+ * prompt the large model prefills. Four calls, one per stage, run on a
+ * caller-supplied HIP stream:
+ *
+ *   sp_score_attention  Q, K            -> importance[token]
+ *   sp_pool_chunk       importance      -> token_scores[token], chunk_scores[chunk]
+ *   sp_select_chunks    chunk_scores    -> keep[chunk], n_kept_chunks[prompt]
+ *   sp_gather_kept      keep, token ids -> kept ids + original positions
+ *
+ * Sources (web pages on SpecPrefill):
+ *   [G]  "SpecPrefill — Implementation Guide": How It Works (Core Algorithm,
+ *        Attention Capture, Token Importance, Chunk Selection, Sparse
+ *        Prefill); v3 Improvements 1-2; v3.1 Optimizations & Bug Fixes 5;
+ *        Configuration Reference; Implementation Details (Key Functions).
+ *   [PR] "Speculative prefill" (llama.cpp pull request 27692): Approach,
+ *        steps 1-4; Failure Mode Analysis & Operational Limits.
+ *
+ * Conventions for every call:
+ *   - Ownership: the caller owns every buffer. The library allocates and
+ *     frees nothing and keeps no pointer after a call returns. Work is
+ *     enqueued on `stream` (a hipStream_t; NULL = the default stream), so
+ *     the caller keeps inputs, outputs and the workspace alive until the
+ *     stream reaches that point.
+ *   - Memory: pointers named "host" are read during the call only; every
+ *     other buffer pointer is device memory.
+ *   - Errors: arguments are checked before anything is enqueued. A bad
+ *     argument returns SP_ERR_INVALID_ARGUMENT, a valid but unsupported shape
+ *     SP_ERR_UNSUPPORTED, a short workspace SP_ERR_WORKSPACE_TOO_SMALL; in each
+ *     case nothing was launched. SP_ERR_DEVICE reports a failed launch.
+ *     Faults during execution surface at the caller's next synchronisation.
+ *   - Thread safety: no global mutable state; calls on different streams with
+ *     different workspaces may run concurrently. The library prints nothing.
+ *   - Batches: B prompts, prompt b has N_b = token_offsets[b+1] -
+ *     token_offsets[b] >= 1 tokens; per-token arrays are packed over the
+ *     batch ([sum_b N_b]), per-chunk arrays likewise ([sum_b ceil(N_b / C)],
+ *     prompt b's chunks first at sum_{b' < b} ceil(N_b' / C)).
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef SPECPREFILL_H
+#define SPECPREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SP_ABI_VERSION 1
+#define SP_MAX_PROMPTS 128          /* prompts per batch */
+#define SP_MAX_CHUNKS_PER_PROMPT 16384
+
+typedef enum {
+  SP_OK = 0,
+  SP_ERR_INVALID_ARGUMENT = 1,
+  SP_ERR_UNSUPPORTED = 2,
+  SP_ERR_WORKSPACE_TOO_SMALL = 3,
+  SP_ERR_DEVICE = 4
+} sp_status;
+
+typedef enum { SP_DTYPE_F32 = 0, SP_DTYPE_BF16 = 1 } sp_dtype;
+
+typedef enum { SP_SELECT_TOP_P = 0, SP_SELECT_MASS = 1 } sp_select_mode;
+
+/* Scoring kernel choice: AUTO picks the fastest one that supports the shape. */
+typedef enum {
+  SP_SCORE_AUTO = 0,
+  SP_SCORE_TWO_PASS = 1,   /* stats pass, then a recompute pass: K read twice */
+  SP_SCORE_STREAM = 2      /* one persistent pass: K read once */
+} sp_score_algo;
+
+/* A batch of prompts. token_offsets is HOST memory, [n_prompts + 1],
+ * token_offsets[0] == 0, strictly increasing. */
+typedef struct {
+  int32_t n_prompts;               /* 1 .. SP_MAX_PROMPTS */
+  const int64_t *token_offsets;    /* host */
+} sp_batch;
+
+/* Draft attention shape ([G] Attention Capture; [PR] Approach steps 1-2).
+ * n_lookahead (L) queries per prompt sit at positions N_b .. N_b + L - 1. */
+typedef struct {
+  int32_t n_layers;     /* attention layers that give scores, >= 1 */
+  int32_t n_q_heads;    /* Hq >= 1 */
+  int32_t n_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0; G = Hq / Hkv */
+  int32_t head_dim;     /* d: 64 or 128 */
+  int32_t n_lookahead;  /* L >= 1; L * G <= 32 */
+  int32_t dtype;        /* sp_dtype of Q and K */
+  float scale;          /* logit scale, usually 1 / sqrt(d) */
+  int32_t algo;         /* sp_score_algo */
+} sp_attn_desc;
+
+/* Smoothing, normalisation, boosts and chunking ([PR] Approach step 3;
+ * [G] v3 item 2 and v3.1 item 5; [G] Configuration Reference defaults:
+ * W 13, C 32, first 64 x1.5, last 128 x1.3). */
+typedef struct {
+  int32_t pool_window;       /* W: odd, >= 1 */
+  int32_t chunk_size;        /* C: 1 .. 1024 */
+  int32_t normalize;         /* 0/1: min-max scale each prompt's scores to [0, 1] */
+  int32_t boost_first_n;     /* >= 0 */
+  float boost_first_mult;    /* > 0; 1.0 = off */
+  int32_t boost_last_n;      /* >= 0 */
+  float boost_last_mult;     /* > 0; 1.0 = off */
+} sp_pool_desc;
+
+int sp_abi_version(void);
+const char *sp_status_string(int status);
+
+/* Workspace sizes (bytes, device memory) each call needs for this batch;
+ * the result is written to *bytes. Alignment: 256 bytes. */
+sp_status sp_score_workspace_bytes(const sp_attn_desc *desc, const sp_batch *batch,
+                                   size_t *bytes);
+sp_status sp_pool_workspace_bytes(const sp_pool_desc *desc, const sp_batch *batch,
+                                  size_t *bytes);
+sp_status sp_select_workspace_bytes(const sp_batch *batch, int32_t chunk_size, size_t *bytes);
+sp_status sp_gather_workspace_bytes(const sp_batch *batch, int32_t chunk_size, size_t *bytes);
+
+/*
+ * Token importance ([G] Token Importance; [PR] Approach steps 1-3).
+ * For every prompt b, layer l, lookahead step j and query head h, the softmax
+ * row of query (b, l, j, h) over the keys it sees (its N_b prompt keys and
+ * lookahead keys 0..j, causal), with logits scale * <q, k> against the key
+ * head h / G. Only the prompt columns go forward ([G] capture callback).
+ *   importance[b][k] = (1/L) * sum_j max_{l, h} p[b][l][j][h][k],  k < N_b
+ *
+ *   q:  [B][n_layers][L][Hq][d] of dtype, contiguous.
+ *   k:  [n_layers][sum_b (N_b + L)][Hkv][d] of dtype, contiguous; prompt b's
+ *       key rows start at token_offsets[b] + b * L: its N_b prompt keys, then
+ *       its L lookahead keys.
+ *   importance: [sum_b N_b] fp32 out.
+ *   ws: device workspace of at least sp_score_workspace_bytes().
+ */
+sp_status sp_score_attention(const sp_attn_desc *desc, const sp_batch *batch, const void *q,
+                             const void *k, float *importance, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/*
+ * Token and chunk scores ([PR] Approach step 3; [G] v3.1 item 5, v3 item 2,
+ * Chunk Selection). Per prompt: centred average pooling of width W over the
+ * positions inside the prompt; if normalize, min-max scaling to [0, 1] (a
+ * prompt whose max - min <= 1e-6 * max gets 1.0 everywhere); then the boost
+ * multipliers (both apply where the two ranges overlap); then the mean of
+ * each C-token chunk over the tokens it holds.
+ *
+ *   importance:   [sum N_b] fp32 in.
+ *   token_scores: [sum N_b] fp32 out (the boosted scores), or NULL.
+ *   chunk_scores: [sum ceil(N_b / C)] fp32 out.
+ */
+sp_status sp_pool_chunk(const sp_pool_desc *desc, const sp_batch *batch, const float *importance,
+                        float *token_scores, float *chunk_scores, void *ws, size_t ws_bytes,
+                        void *stream);
+
+/*
+ * Chunk selection per prompt ([PR] Approach step 4; [G] v3 item 1).
+ * The final chunk (prompt boundary) is always kept; the other chunks are
+ * visited by score, highest first, ties to the lower index.
+ *   SP_SELECT_TOP_P: param = p in (0, 1]; keeps kc = max(1, min(nc,
+ *     ceil(p * nc - 1e-9))) chunks (computed in double), the final one
+ *     included.
+ *   SP_SELECT_MASS: param = mass in (0, 1]; keeps the final chunk, then
+ *     chunks in visiting order while the kept score sum (fp64) is below
+ *     mass * (sum of all chunk scores); the chunk that reaches it is kept.
+ *
+ *   chunk_scores:  [sum nc_b] fp32 in (finite, >= 0).
+ *   keep:          [sum nc_b] uint8 out (0/1).
+ *   n_kept_chunks: [B] int32 out.
+ */
+sp_status sp_select_chunks(int32_t mode, double param, const sp_batch *batch, int32_t chunk_size,
+                           const float *chunk_scores, uint8_t *keep, int32_t *n_kept_chunks,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Kept-token compaction ([G] Sparse Prefill; [PR] Approach step 4): the
+ * first token (BOS) and every token of a kept chunk, ascending, with its
+ * token id and its original position inside the prompt (gaps preserved).
+ *
+ *   keep:         [sum nc_b] uint8 in.
+ *   token_ids:    [sum N_b] int32 in.
+ *   kept_ids:     [sum N_b] int32 out (capacity); prompt b's kept tokens at
+ *                 kept_offsets[b] .. kept_offsets[b+1].
+ *   kept_pos:     [sum N_b] int32 out, same layout.
+ *   kept_offsets: [B + 1] int64 out.
+ */
+sp_status sp_gather_kept(const sp_batch *batch, int32_t chunk_size, const uint8_t *keep,
+                         const int32_t *token_ids, int32_t *kept_ids, int32_t *kept_pos,
+                         int64_t *kept_offsets, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECPREFILL_H */

@@ -1,0 +1,175 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from draft_attention_token_amd import specprefill as sp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specprefill.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:sp_status|int|const char \*|size_t)\s*\*?\s*(sp_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_expected_functions():
+    assert _declared() == sorted(sp.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = sp.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert L.sp_abi_version() == 1
+
+
+def test_status_strings():
+    assert sp.status_string(0) == "ok"
+    assert "invalid" in sp.status_string(1)
+    assert "unsupported" in sp.status_string(2)
+    assert "workspace" in sp.status_string(3)
+    assert sp.status_string(99) == "unknown status"
+
+
+def _score(desc, batch, q=1, k=1, out=1, ws=1, ws_bytes=1 << 30):
+    # Non-null fake pointers: validation must reject before touching them.
+    vp = lambda v: ctypes.c_void_p(v * 4096 if v else 0)
+    return sp.lib().sp_score_attention(ctypes.byref(desc), batch.ref() if batch else None,
+                                       vp(q), vp(k), vp(out), vp(ws), ws_bytes, None)
+
+
+def _desc(**kw):
+    base = dict(n_layers=6, n_q_heads=16, n_kv_heads=4, head_dim=128, n_lookahead=8,
+                dtype=torch.bfloat16, scale=None, algo="two_pass")
+    base.update(kw)
+    return sp.attn_desc(**base)
+
+
+@pytest.mark.parametrize("kw, want", [
+    (dict(n_layers=0), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(n_q_heads=0), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(n_kv_heads=3), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(n_lookahead=0), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(dtype=torch.float16), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(algo=7), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(head_dim=96), sp.SP_ERR_UNSUPPORTED),
+    (dict(n_lookahead=9), sp.SP_ERR_UNSUPPORTED),           # L * G = 36 > 32
+    (dict(n_q_heads=64, n_kv_heads=4), sp.SP_ERR_UNSUPPORTED),
+])
+def test_score_rejects_bad_descriptors(kw, want):
+    assert _score(_desc(**kw), sp.Batch([0, 100])) == want
+
+
+@pytest.mark.parametrize("offsets, want", [
+    ([5, 10], sp.SP_ERR_INVALID_ARGUMENT),          # does not start at 0
+    ([0, 10, 10], sp.SP_ERR_INVALID_ARGUMENT),      # empty prompt
+    ([0, 10, 7], sp.SP_ERR_INVALID_ARGUMENT),       # decreasing
+    ([0], sp.SP_ERR_INVALID_ARGUMENT),              # no prompts
+    (list(range(0, 130)), sp.SP_ERR_UNSUPPORTED),    # 129 prompts > SP_MAX_PROMPTS
+    ([0, 1 << 30], sp.SP_ERR_UNSUPPORTED),           # too many tokens
+])
+def test_score_rejects_bad_batches(offsets, want):
+    assert _score(_desc(), sp.Batch(offsets)) == want
+
+
+def test_score_rejects_null_and_misaligned_pointers_and_small_workspace():
+    b = sp.Batch([0, 100])
+    assert _score(_desc(), None) == sp.SP_ERR_INVALID_ARGUMENT
+    assert _score(_desc(), b, q=0) == sp.SP_ERR_INVALID_ARGUMENT
+    assert _score(_desc(), b, k=0) == sp.SP_ERR_INVALID_ARGUMENT
+    assert _score(_desc(), b, out=0) == sp.SP_ERR_INVALID_ARGUMENT
+    L = sp.lib()
+    d = _desc()
+    assert L.sp_score_attention(ctypes.byref(d), b.ref(), ctypes.c_void_p(4100),
+                                ctypes.c_void_p(4096), ctypes.c_void_p(4096),
+                                ctypes.c_void_p(4096), 1 << 30, None) == sp.SP_ERR_INVALID_ARGUMENT
+    need = sp.score_workspace_bytes(d, b)
+    assert need > 0
+    assert _score(d, b, ws_bytes=need - 1) == sp.SP_ERR_WORKSPACE_TOO_SMALL
+    assert _score(d, b, ws=0) == sp.SP_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_workspace_sizes_grow_with_the_batch():
+    d = _desc()
+    small = sp.score_workspace_bytes(d, sp.Batch([0, 1000]))
+    big = sp.score_workspace_bytes(d, sp.Batch([0, 100000]))
+    assert 0 < small < big
+    pd = sp.pool_desc()
+    assert sp.pool_workspace_bytes(pd, sp.Batch([0, 5000])) >= 5000 * 4
+    assert sp.select_workspace_bytes(sp.Batch([0, 5000]), 32) == 0
+    assert sp.gather_workspace_bytes(sp.Batch([0, 5000]), 32) >= 157 * 4
+
+
+def _pool(desc, batch, imp=1, cs=1, ws=1, ws_bytes=1 << 30):
+    vp = lambda v: ctypes.c_void_p(v * 4096 if v else 0)
+    return sp.lib().sp_pool_chunk(ctypes.byref(desc), batch.ref(), vp(imp), None, vp(cs), vp(ws),
+                                  ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw, want", [
+    (dict(W=12), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(W=0), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(W=131), sp.SP_ERR_UNSUPPORTED),
+    (dict(C=0), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(C=2048), sp.SP_ERR_UNSUPPORTED),
+    (dict(first_n=-1), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(first_mult=0.0), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(last_mult=float("inf")), sp.SP_ERR_INVALID_ARGUMENT),
+])
+def test_pool_rejects_bad_descriptors(kw, want):
+    assert _pool(sp.pool_desc(**kw), sp.Batch([0, 100])) == want
+
+
+def test_pool_rejects_null_outputs_and_small_workspace():
+    b = sp.Batch([0, 100])
+    assert _pool(sp.pool_desc(), b, imp=0) == sp.SP_ERR_INVALID_ARGUMENT
+    assert _pool(sp.pool_desc(), b, cs=0) == sp.SP_ERR_INVALID_ARGUMENT
+    assert _pool(sp.pool_desc(), b, ws_bytes=8) == sp.SP_ERR_WORKSPACE_TOO_SMALL
+
+
+def _select(mode, param, batch, C=32, cs=1, keep=1, cnt=1):
+    vp = lambda v: ctypes.c_void_p(v * 4096 if v else 0)
+    return sp.lib().sp_select_chunks(mode, param, batch.ref(), C, vp(cs), vp(keep), vp(cnt), None,
+                                     0, None)
+
+
+@pytest.mark.parametrize("mode, param, C, want", [
+    (5, 0.5, 32, sp.SP_ERR_INVALID_ARGUMENT),
+    (sp.SP_SELECT_TOP_P, 0.0, 32, sp.SP_ERR_INVALID_ARGUMENT),
+    (sp.SP_SELECT_TOP_P, 1.01, 32, sp.SP_ERR_INVALID_ARGUMENT),
+    (sp.SP_SELECT_MASS, -0.5, 32, sp.SP_ERR_INVALID_ARGUMENT),
+    (sp.SP_SELECT_MASS, float("nan"), 32, sp.SP_ERR_INVALID_ARGUMENT),
+    (sp.SP_SELECT_MASS, 0.85, 0, sp.SP_ERR_INVALID_ARGUMENT),
+    (sp.SP_SELECT_MASS, 0.85, 1, sp.SP_ERR_UNSUPPORTED),     # 100000 chunks > 16384
+])
+def test_select_rejects_bad_arguments(mode, param, C, want):
+    assert _select(mode, param, sp.Batch([0, 100000]), C) == want
+
+
+def test_select_and_gather_reject_null_pointers():
+    b = sp.Batch([0, 100])
+    assert _select(sp.SP_SELECT_MASS, 0.85, b, cs=0) == sp.SP_ERR_INVALID_ARGUMENT
+    assert _select(sp.SP_SELECT_MASS, 0.85, b, keep=0) == sp.SP_ERR_INVALID_ARGUMENT
+    assert _select(sp.SP_SELECT_MASS, 0.85, b, cnt=0) == sp.SP_ERR_INVALID_ARGUMENT
+    vp = lambda v: ctypes.c_void_p(v)
+    L = sp.lib()
+    args = [vp(4096)] * 5
+    assert L.sp_gather_kept(b.ref(), 32, vp(0), *args[:4], vp(4096), 1 << 20, None) == \
+        sp.SP_ERR_INVALID_ARGUMENT
+    assert L.sp_gather_kept(b.ref(), 32, *args, vp(4096), 4, None) == sp.SP_ERR_WORKSPACE_TOO_SMALL
+    assert L.sp_gather_kept(b.ref(), 0, *args, vp(4096), 1 << 20, None) == sp.SP_ERR_INVALID_ARGUMENT
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(sp, "_lib", None)
+    monkeypatch.setattr(sp, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not found"):
+        sp.lib()

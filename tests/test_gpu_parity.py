@@ -1,0 +1,220 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Small shapes cover several tiles, ragged tails, every supported dtype /
+head size / group size, both scoring kernels and the batch edge cases; the
+named workloads run at their full sizes (the ragged batch compares a sample
+of its prompts end to end, the rest through properties).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from draft_attention_token_amd import specprefill as sp
+
+from parity import assert_scores_close, check_prompt
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    sp.lib()
+
+
+def run_gpu(inp, mode, param, algo="auto"):
+    w = inp.workload
+    print(f"[gpu] {w.name} lengths={inp.lengths[:4]}{'...' if len(inp.lengths) > 4 else ''} "
+          f"mode={mode} p={param} algo={algo}", flush=True)
+    pipe = sp.Pipeline(inp.offsets, w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                       w.n_lookahead, w.dtype, DEV, W=w.pool_window, C=w.chunk_size,
+                       normalize=w.normalize, boost=w.boost, mode=mode, param=param, algo=algo)
+    q, k, ids = inp.q.to(DEV), inp.k.to(DEV), inp.token_ids.to(DEV)
+    pipe.run(q, k, ids)
+    torch.cuda.synchronize()
+    return pipe
+
+
+def per_prompt(pipe, inp):
+    off = inp.offsets.numpy()
+    C = inp.workload.chunk_size
+    coff = np.concatenate([[0], np.cumsum([(n + C - 1) // C for n in inp.lengths])])
+    koff = pipe.kept_offsets.cpu().numpy()
+    cs, keep = pipe.chunk_scores.cpu().numpy(), pipe.keep.cpu().numpy()
+    kid, kpos = pipe.kept_ids.cpu().numpy(), pipe.kept_pos.cpu().numpy()
+    imp = pipe.importance.cpu().numpy()
+    ts = pipe.token_scores.cpu().numpy()
+    out = []
+    for b in range(len(inp.lengths)):
+        out.append(dict(imp=imp[off[b]:off[b + 1]], token_scores=ts[off[b]:off[b + 1]],
+                        chunk_scores=cs[coff[b]:coff[b + 1]], keep=keep[coff[b]:coff[b + 1]],
+                        kept_ids=kid[koff[b]:koff[b + 1]], kept_pos=kpos[koff[b]:koff[b + 1]]))
+    assert koff[0] == 0 and np.all(np.diff(koff) > 0)
+    return out
+
+
+def compare(inp, pipe, mode, param, prompts=None, ora=None):
+    w = inp.workload
+    if prompts is None:
+        prompts = range(len(inp.lengths))
+    if ora is None:
+        ora = oracle.pipeline(inp, mode, param)
+    gp = per_prompt(pipe, inp)
+    ids = inp.token_ids.numpy()
+    off = inp.offsets.numpy()
+    excused = 0
+    for b in prompts:
+        assert_scores_close(gp[b]["imp"], ora["imp"][off[b]:off[b + 1]], f"importance, prompt {b}")
+        assert_scores_close(gp[b]["token_scores"], ora["token_scores"][b], f"token scores, prompt {b}")
+        excused += check_prompt(gp[b], ora, b, mode, param, w.chunk_size, ids[off[b]:off[b + 1]])
+    n_kept = pipe.n_kept.cpu().numpy()
+    for b in prompts:
+        assert n_kept[b] == gp[b]["keep"].sum()
+    return excused, gp
+
+
+SMALL = [
+    # (name, base workload, overrides)
+    ("fp32_d64_g4", "n800_fp32", dict(lengths=(333,))),
+    ("fp32_d64_one_token", "n800_fp32", dict(lengths=(1,))),
+    ("fp32_d64_ragged", "n800_fp32", dict(lengths=(31, 32, 33, 97))),
+    ("fp32_d128_g2_l3", "n800_fp32", dict(lengths=(250, 71), head_dim=128, n_q_heads=4,
+                                           n_kv_heads=2, n_lookahead=3)),
+    ("bf16_d128_g4", "n3212_bf16", dict(lengths=(1000,))),
+    ("bf16_d128_ragged", "n3212_bf16", dict(lengths=(65, 1, 640, 129))),
+    ("bf16_d64_g8_l4", "n3212_bf16", dict(lengths=(500,), head_dim=64, n_q_heads=16,
+                                          n_kv_heads=2, n_lookahead=4)),
+    ("bf16_d128_g1_l1", "n3212_bf16", dict(lengths=(300, 45), n_q_heads=4, n_kv_heads=4,
+                                           n_lookahead=1)),
+    ("bf16_d128_g32_l1", "n3212_bf16", dict(lengths=(200,), n_q_heads=32, n_kv_heads=1,
+                                            n_lookahead=1, n_layers=2)),
+    ("bf16_no_norm", "n3212_bf16", dict(lengths=(800,), normalize=False, boost=False)),
+]
+
+
+@pytest.mark.parametrize("algo", ["two_pass", "auto"])
+@pytest.mark.parametrize("name, base, kw", SMALL, ids=[s[0] for s in SMALL])
+def test_small_shapes(name, base, kw, algo):
+    w = workloads.small_workload(base, seed=500 + len(name), n_spans=2, **kw)
+    inp = workloads.make_inputs(w)
+    for mode, param in (("top_p", 0.3), ("mass", 0.85)):
+        pipe = run_gpu(inp, mode, param, algo)
+        compare(inp, pipe, mode, param)
+
+
+@pytest.mark.parametrize("name", ["n800_fp32", "n3212_bf16"])
+def test_named_small_workloads(name):
+    w = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(w)
+    for mode, param in (w.select,) + tuple(w.also_select):
+        pipe = run_gpu(inp, mode, param)
+        compare(inp, pipe, mode, param)
+        keep = pipe.keep.cpu().numpy()
+        for c in inp.spans[0]:
+            assert keep[c] == 1, f"planted chunk {c} dropped"
+
+
+def test_all_zero_queries_give_equal_chunk_scores():
+    w = workloads.small_workload("n3212_bf16", lengths=(900,), normalize=False, boost=False)
+    inp = workloads.make_inputs(w)
+    inp.q.zero_()
+    pipe = run_gpu(inp, "top_p", 0.3)
+    imp = pipe.importance.cpu().numpy().astype(np.float64)
+    want = sum(1.0 / (900 + j + 1) for j in range(8)) / 8
+    np.testing.assert_allclose(imp, want, rtol=1e-6)
+    cs = pipe.chunk_scores.cpu().numpy()
+    np.testing.assert_allclose(cs, cs[0], rtol=1e-6)
+
+
+def test_results_are_bitwise_deterministic():
+    w = workloads.small_workload("n3212_bf16", lengths=(2000, 3000), seed=9)
+    inp = workloads.make_inputs(w)
+    a = run_gpu(inp, "mass", 0.85)
+    imp1, cs1 = a.importance.clone(), a.chunk_scores.clone()
+    ids1 = a.kept_ids.clone()
+    b = run_gpu(inp, "mass", 0.85)
+    assert torch.equal(imp1, b.importance)
+    assert torch.equal(cs1, b.chunk_scores)
+    n = int(b.kept_offsets[-1])
+    assert torch.equal(ids1[:n], b.kept_ids[:n])
+
+
+def test_pool_select_gather_stages_on_oracle_importance():
+    """Stages after scoring, fed the oracle's importance (rounded to fp32)."""
+    w = workloads.small_workload("n3212_bf16", lengths=(3212, 100, 5000), seed=21)
+    inp = workloads.make_inputs(w)
+    imp = oracle.importance(inp.offsets.numpy(), inp.q, inp.k, w.n_layers, w.n_q_heads,
+                            w.n_kv_heads, w.head_dim, w.n_lookahead, inp.scale)
+    imp32 = imp.astype(np.float32)
+    ora = oracle.pipeline(inp, "top_p", 0.3, imp=imp32.astype(np.float64))
+    batch = sp.Batch(inp.offsets)
+    ts, cs = sp.sp_pool_chunk(torch.from_numpy(imp32).to(DEV), batch)
+    keep, cnt = sp.sp_select_chunks(cs, batch, 32, "top_p", 0.3)
+    kid, kpos, koff = sp.sp_gather_kept(keep, inp.token_ids.to(DEV), batch, 32)
+    torch.cuda.synchronize()
+    off = inp.offsets.numpy()
+    ts, cs, keep = ts.cpu().numpy(), cs.cpu().numpy(), keep.cpu().numpy()
+    koff, kid, kpos = koff.cpu().numpy(), kid.cpu().numpy(), kpos.cpu().numpy()
+    c0 = 0
+    for b, n in enumerate(inp.lengths):
+        nc = (n + 31) // 32
+        assert_scores_close(ts[off[b]:off[b + 1]], ora["token_scores"][b], f"token scores {b}")
+        assert_scores_close(cs[c0:c0 + nc], ora["chunk_scores"][b], f"chunk scores {b}")
+        gpu = dict(chunk_scores=cs[c0:c0 + nc], keep=keep[c0:c0 + nc],
+                   kept_ids=kid[koff[b]:koff[b + 1]], kept_pos=kpos[koff[b]:koff[b + 1]])
+        check_prompt(gpu, ora, b, "top_p", 0.3, 32, inp.token_ids.numpy()[off[b]:off[b + 1]])
+        c0 += nc
+
+
+@pytest.mark.parametrize("name", ["n32k_bf16", "n128k_bf16", "n128k_diffuse_bf16"])
+def test_full_size_single_prompt(name):
+    w = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(w)
+    imp = oracle.importance(inp.offsets.numpy(), inp.q, inp.k, w.n_layers, w.n_q_heads,
+                            w.n_kv_heads, w.head_dim, w.n_lookahead, inp.scale)
+    for mode, param in (w.select,) + tuple(w.also_select):
+        pipe = run_gpu(inp, mode, param)
+        ora = oracle.pipeline(inp, mode, param, imp=imp)
+        excused, _ = compare(inp, pipe, mode, param, ora=ora)
+        print(f"[gpu] {name} {mode}: excused differing chunks = {excused}", flush=True)
+        keep = pipe.keep.cpu().numpy()
+        for c in inp.spans[0]:
+            assert keep[c] == 1, f"planted chunk {c} dropped"
+
+
+def test_ragged_batch_sampled_prompts():
+    """16 prompts, 2K-64K tokens: the four shortest prompts are compared end
+    to end (oracle on a sub-batch of their own Q/K); every prompt is checked
+    for planted spans, valid compaction and row-sum bounds."""
+    w = workloads.WORKLOADS["ragged16_bf16"]
+    inp = workloads.make_inputs(w)
+    L = w.n_lookahead
+    order = np.argsort(inp.lengths)[:4]
+    koffs = inp.key_offsets
+    for mode, param in (w.select,) + tuple(w.also_select):
+        pipe = run_gpu(inp, mode, param)
+        gp = per_prompt(pipe, inp)
+        for b in order:
+            n = inp.lengths[b]
+            sub = workloads.Inputs(w, [n], torch.tensor([0, n], dtype=torch.int64),
+                                   inp.q[b:b + 1], inp.k[:, koffs[b]:koffs[b] + n + L],
+                                   inp.token_ids[inp.offsets[b]:inp.offsets[b + 1]], [inp.spans[b]],
+                                   [inp.strengths[b]])
+            ora = oracle.pipeline(sub, mode, param)
+            assert_scores_close(gp[b]["imp"], ora["imp"], f"importance, prompt {b}")
+            check_prompt(gp[b], ora, 0, mode, param, w.chunk_size, sub.token_ids.numpy())
+        for b in range(len(inp.lengths)):
+            n = inp.lengths[b]
+            # each step's max-probability row is at most 1 per token and sums to >= 1 over
+            # the prompt minus what the lookahead keys took; so 0 < imp <= 1
+            assert np.all(gp[b]["imp"] > 0) and np.all(gp[b]["imp"] <= 1)
+            for c in inp.spans[b]:
+                assert gp[b]["keep"][c] == 1, f"prompt {b}: planted chunk {c} dropped"
+            ids = inp.token_ids.numpy()[inp.offsets[b]:inp.offsets[b + 1]]
+            want_ids, want_pos = oracle.gather(gp[b]["keep"], ids, w.chunk_size)
+            assert np.array_equal(gp[b]["kept_ids"], want_ids)
+            assert np.array_equal(gp[b]["kept_pos"], want_pos)
