@@ -168,6 +168,15 @@ sp_status sp_score_attention(const sp_attn_desc *desc, const sp_batch *batch, co
   return launched(launch_score_two_pass(s, tiles, total_tiles, q, k, importance, ws, hs));
 }
 
+sp_status sp_score_status(const void *ws, int32_t *status_host, void *stream) {
+  if (!ws || !status_host) return SP_ERR_INVALID_ARGUMENT;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(status_host, ws, sizeof(int32_t), hipMemcpyDeviceToHost, hs) != hipSuccess ||
+      hipStreamSynchronize(hs) != hipSuccess)
+    return SP_ERR_DEVICE;
+  return SP_OK;
+}
+
 sp_status sp_pool_workspace_bytes(const sp_pool_desc *desc, const sp_batch *batch,
                                   size_t *bytes) {
   if (!bytes) return SP_ERR_INVALID_ARGUMENT;

@@ -73,7 +73,8 @@ __global__ __launch_bounds__(64) void k_stats(AttnShape s, SegTable tiles, int64
 // order: lse2 = m + log2(z) (base-2 log-sum-exp of the row's logits).
 __global__ __launch_bounds__(256) void k_lse(SegTable tiles, int n_prob, int total_tiles,
                                              const float2 *__restrict__ part,
-                                             float *__restrict__ lse) {
+                                             float *__restrict__ lse, int *__restrict__ status) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = 0;
   __shared__ float2 sm[8][kRows];
   const int b = blockIdx.x, prob = blockIdx.y;
   const int row = threadIdx.x & 31, p = threadIdx.x >> 5;
@@ -135,13 +136,14 @@ hipError_t run(const AttnShape &s, const SegTable &tiles, int total_tiles, const
                const void *k, float *imp, void *ws, hipStream_t st) {
   const int n_prob = s.n_layers * s.Hkv;
   const int64_t total_keys = tiles.tok_off[tiles.B] + (int64_t)tiles.B * tiles.L;
-  float2 *part = reinterpret_cast<float2 *>(ws);
-  float *lse = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) +
+  int *status = reinterpret_cast<int *>(ws);
+  float2 *part = reinterpret_cast<float2 *>(reinterpret_cast<char *>(ws) + kStatusBytes);
+  float *lse = reinterpret_cast<float *>(reinterpret_cast<char *>(part) +
                                          align_up((size_t)n_prob * total_tiles * kRows * sizeof(float2)));
   hipLaunchKernelGGL((k_stats<T, D>), dim3(total_tiles, n_prob), dim3(64), 0, st, s, tiles,
                      total_keys, total_tiles, (const T *)q, (const T *)k, part);
   hipLaunchKernelGGL(k_lse, dim3(tiles.B, n_prob), dim3(256), 0, st, tiles, n_prob, total_tiles,
-                     part, lse);
+                     part, lse, status);
   hipLaunchKernelGGL((k_score<T, D>), dim3(total_tiles), dim3(64), 0, st, s, tiles, total_keys,
                      (const T *)q, (const T *)k, lse, imp);
   return hipGetLastError();
@@ -151,7 +153,7 @@ hipError_t run(const AttnShape &s, const SegTable &tiles, int total_tiles, const
 
 size_t score_two_pass_ws(const AttnShape &s, int B, int total_tiles) {
   const size_t n_prob = (size_t)s.n_layers * s.Hkv;
-  return align_up(n_prob * total_tiles * kRows * sizeof(float2)) +
+  return kStatusBytes + align_up(n_prob * total_tiles * kRows * sizeof(float2)) +
          align_up((size_t)B * n_prob * kRows * sizeof(float));
 }
 

@@ -11,6 +11,9 @@ namespace sp {
 constexpr int kTile = 32;          // keys per MFMA tile (the 32-wide N of 32x32 MFMA)
 constexpr int kRows = 32;          // query rows per MFMA tile: (lookahead step, head in group)
 constexpr size_t kAlign = 256;
+// Both scoring kernels keep a 256-byte status header at the start of their
+// workspace: int 0 is 0 after a good run, 1 if a cross-block wait timed out.
+constexpr size_t kStatusBytes = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Per-prompt prefix table passed to kernels by value (about 1 KB). unit_off

@@ -36,7 +36,7 @@ SP_MAX_PROMPTS = 128
 EXPORTED = [
     "sp_abi_version", "sp_status_string", "sp_score_workspace_bytes", "sp_pool_workspace_bytes",
     "sp_select_workspace_bytes", "sp_gather_workspace_bytes", "sp_score_attention",
-    "sp_pool_chunk", "sp_select_chunks", "sp_gather_kept",
+    "sp_pool_chunk", "sp_select_chunks", "sp_gather_kept", "sp_score_status",
 ]
 
 _ALGOS = {"auto": SP_SCORE_AUTO, "two_pass": SP_SCORE_TWO_PASS, "stream": SP_SCORE_STREAM}
@@ -92,6 +92,7 @@ def lib():
         L.sp_select_chunks.argtypes = [ctypes.c_int32, ctypes.c_double, bp, ctypes.c_int32, vp, vp,
                                        vp, vp, sz, vp]
         L.sp_gather_kept.argtypes = [bp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.sp_score_status.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
         for name in EXPORTED[2:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -211,6 +212,14 @@ def sp_score_attention(q: torch.Tensor, k: torch.Tensor, offsets, n_layers: int,
     return out
 
 
+def score_status(ws: torch.Tensor) -> int:
+    """Status word of the last finished sp_score_attention on this workspace
+    (0 = ok; 1 = a cross-block wait timed out and the importance is invalid)."""
+    out = ctypes.c_int32(-1)
+    _check(lib().sp_score_status(_ptr(ws), ctypes.byref(out), _stream(ws.device)), "sp_score_status")
+    return out.value
+
+
 def sp_pool_chunk(importance: torch.Tensor, offsets, W=13, C=32, normalize=True, first_n=64,
                   first_mult=1.5, last_n=128, last_mult=1.3, token_scores: bool = True,
                   out_tokens=None, out_chunks=None, ws=None):
@@ -307,6 +316,9 @@ class Pipeline:
         self.ws_pool = _ws(pool_workspace_bytes(self.pdesc, self.batch), device)
         self.ws_gather = _ws(gather_workspace_bytes(self.batch, C), device)
         self.device = device
+
+    def score_status(self) -> int:
+        return score_status(self.ws_score)
 
     def run(self, q: torch.Tensor, k: torch.Tensor, token_ids: torch.Tensor):
         L = lib()

@@ -132,11 +132,19 @@ sp_status sp_gather_workspace_bytes(const sp_batch *batch, int32_t chunk_size, s
  *       key rows start at token_offsets[b] + b * L: its N_b prompt keys, then
  *       its L lookahead keys.
  *   importance: [sum_b N_b] fp32 out.
- *   ws: device workspace of at least sp_score_workspace_bytes().
+ *   ws: device workspace of at least sp_score_workspace_bytes(). When the
+ *       enqueued work has finished, the first int32 of ws is 0, or 1 if the
+ *       single-pass kernel gave up waiting on another block (it waits at most
+ *       about 2 s, then finishes so the device never hangs); importance is
+ *       then not valid. sp_score_status() reads it.
  */
 sp_status sp_score_attention(const sp_attn_desc *desc, const sp_batch *batch, const void *q,
                              const void *k, float *importance, void *ws, size_t ws_bytes,
                              void *stream);
+
+/* Copies the status word of a finished sp_score_attention call (first int32
+ * of its workspace) to *status_host. Synchronises `stream`. */
+sp_status sp_score_status(const void *ws, int32_t *status_host, void *stream);
 
 /*
  * Token and chunk scores ([PR] Approach step 3; [G] v3.1 item 5, v3 item 2,

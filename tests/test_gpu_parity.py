@@ -36,6 +36,7 @@ def run_gpu(inp, mode, param, algo="auto"):
     q, k, ids = inp.q.to(DEV), inp.k.to(DEV), inp.token_ids.to(DEV)
     pipe.run(q, k, ids)
     torch.cuda.synchronize()
+    assert pipe.score_status() == 0, "scoring kernel reported a timed-out wait"
     return pipe
 
 
