@@ -19,31 +19,36 @@
 //    computes logits with 32x32x16 bf16 MFMA, K as the A operand (MFMA row =
 //    key) and Q as the B operand (MFMA column = query row): a lane holds one
 //    query row and 16 keys of each tile, so a row's max and sum over the
-//    wave's keys reduce inside the lane plus one swap of wave halves. As soon as a
-//    tile's MFMAs have consumed its K registers, the wave refills them with
-//    the next problem's tile: the K stream never waits for synchronisation.
-//  * One control wave per block does all cross-block work, so no compute
-//    wave ever waits on a fence or an atomic (on this hardware, waiting on
-//    any memory operation also waits on every load issued before it, which
-//    would drain the K prefetch). Per problem it merges the compute waves'
-//    (m, z), posts it, and takes a ticket; the last block of the prompt to
-//    arrive merges every block's (m, z) in block order and publishes the row
-//    lse. It also stages the next problem's Q and an earlier problem's lse in
-//    LDS for the compute waves.
+//    wave's keys reduce inside the lane plus one swap of wave halves. As
+//    soon as a tile's MFMAs have consumed its K registers, the wave refills
+//    them with the next problem's tile: the K stream never waits for
+//    synchronisation. Statistics are accumulated tile by tile (online max,
+//    rescaled sum); each tile's e = 2^(x - m) is relative to the running max
+//    m at that tile, kept per tile.
+//  * Two control waves per block do all cross-block work, so no compute
+//    wave ever waits on a memory operation other than its own K loads (on
+//    this hardware a wait on any load also waits on every load issued
+//    before it, which would drain the K prefetch). They take alternate
+//    problems: for its problem x a control wave merges the compute waves'
+//    statistics into the block's partial base-2 lse of each row and posts
+//    it (one float per row), stages Q(x + 1), then reads every block's
+//    partials of x (plain loads, shared through the L2 of its chip die),
+//    merges them in block order and stages the row lse of x in LDS.
+//    Compute and control waves hand data over through LDS flags rather than
+//    block barriers, so a slow cross-block read only stalls the compute
+//    waves when they need its result.
 //  * The compute waves fold problem i - 2 while working on problem i: they
-//    park e in LDS (two problem slots) and later turn it into probabilities
-//    p = e * 2^(m_tile - lse), kept as a running max per (row, key) in
-//    registers (max over layers and KV groups). Two problems of lag give the
-//    ticket, merge and publish a full problem's time to land. The row
-//    statistics are accumulated tile by tile (online max and rescaled sum),
-//    and each tile's e is relative to the running max at that tile, so only
-//    one tile's logits are live at a time.
+//    park e in LDS (two problem slots) and turn it into probabilities
+//    p = e * 2^(m_tile - lse) once the lse is staged, kept as a running max
+//    per (row, key) in registers (max over layers and KV groups).
 //  * Finally: max over the G heads of a step (lanes of a group), mean over
 //    the L steps (a fixed tree across groups of lanes), store.
-// Every wait is bounded (about 2 s); on time-out the kernel records it in the
-// workspace status word and runs to completion, so the grid always drains.
-// No cache-wide fence is used: cross-block slots are relaxed agent-scope
-// atomics that validate themselves (see StreamWs).
+//
+// Partial slots start as a NaN pattern (written before the launch); a real
+// partial is never NaN, so a slot read before its block posted is detected
+// and read again with a load that bypasses this die's L2. Every wait is
+// bounded (about 2 s); on time-out the kernel records it in the workspace
+// status word and runs to completion, so the grid always drains.
 #include <string.h>
 
 #include <algorithm>
@@ -54,14 +59,15 @@ namespace sp {
 namespace {
 
 constexpr int kCompute = 6;                       // compute waves per block
-constexpr int kThreads = (kCompute + 1) * 64;     // plus one control wave
+constexpr int kControl = 2;                       // control waves (even / odd problems)
+constexpr int kThreads = (kCompute + kControl) * 64;
 constexpr int kTPW = 3;                           // tiles per compute wave
 constexpr int kTilesPerCta = kCompute * kTPW;     // 18
 constexpr int kLag = 2;                           // problems between logits and fold
-constexpr int kStatusWords = kStatusBytes / sizeof(int);
 constexpr uint64_t kWaitTicks = 200000000ull;     // wall clock runs at 100 MHz: 2 s
 constexpr int kQPad = 8;                          // bf16 padding per staged Q row
-constexpr int kMaxCtas = 1024;                    // blocks per launch (one per CU)
+constexpr int kMaxCtas = 256;                     // blocks per launch (one per CU)
+constexpr unsigned kEmpty = 0xffffffffu;          // unwritten partial slot (a NaN)
 
 struct StreamTable {
   int32_t B;        // prompts in this launch
@@ -70,18 +76,9 @@ struct StreamTable {
   int32_t cta_off[SP_MAX_PROMPTS + 1];   // block prefix within this launch
 };
 
-// Cross-block data lives in 64-bit slots written and read with relaxed
-// agent-scope atomics (coherent across the chip's L2s without cache-wide
-// fences), and every slot tells by itself whether it has been written, so no
-// ordering between different slots is needed:
-//   part slot = (m, z) float bits; all-zero bits mean "not yet written" (a
-//     written slot has z > 0, or m = -inf for a row with no visible keys);
-//   lse slot  = float bits | 1 << 32 once published.
-// The launcher zeroes status, tickets, lse and part before each launch.
 struct StreamWs {
-  int *status;                 // [kStatusWords]; status[0] != 0: a wait timed out
-  unsigned long long *lse;     // [B_total][P][32] tagged base-2 lse of each row
-  unsigned long long *part;    // [P][n_cta][32] block (m, z)
+  int *status;      // status[0] != 0: a wait timed out
+  float *part;      // [P][n_cta][32] each block's partial base-2 lse per row
 };
 
 template <int D>
@@ -89,8 +86,41 @@ struct Smem {
   f32x4 eprev[kLag][kCompute][kTPW][4][64];   // parked e values (16-byte slots per lane)
   __bf16 q[kRows][D + kQPad];                 // staged Q rows of the next problem
   float2 red[2][kCompute][kRows];             // per-wave (m, z) of a problem
-  float lse[kRows];                           // staged lse of the problem being folded
+  float lse[2][kRows];                        // staged row lse, by problem parity
+  // Hand-offs between the compute waves and the control wave (no block
+  // barrier inside the main loop, so neither side waits for the other
+  // unless it needs the other's data):
+  int q_seq;         // Q of problems < q_seq has been staged (one at a time)
+  int q_used;        // compute waves that have read the staged Q (cumulative)
+  int stats_cnt;     // compute waves that have written their statistics (cumulative)
+  int lse_ready[2];  // lse[s] holds problem lse_ready[s] - 1 (0: nothing yet)
+  int lse_used;      // compute waves that have folded with a staged lse (cumulative)
 };
+
+__device__ __forceinline__ int lds_get(const int *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_set(int *p, int v) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // data written before the flag
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_inc(int *p) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// Wait (bounded) until *p >= v.
+__device__ __forceinline__ void lds_wait_ge(const int *p, int v, int *status) {
+  if (lds_get(p) >= v) return;
+  const uint64_t t0 = wall_clock64();
+  while (lds_get(p) < v) {
+    if (wall_clock64() - t0 > kWaitTicks) {
+      __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ int cta_prompt(const StreamTable &t, int c) {
   int lo = 0, hi = t.B - 1;
@@ -101,13 +131,18 @@ __device__ __forceinline__ int cta_prompt(const StreamTable &t, int c) {
   return lo;
 }
 
-__device__ __forceinline__ unsigned long long pack2(float m, float z) {
-  return (unsigned long long)__float_as_uint(m) | ((unsigned long long)__float_as_uint(z) << 32);
-}
-
 __device__ __forceinline__ void timeout(int *status) {
   __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// 16-byte load that bypasses this die's L2 (coherent across the chip); the
+// caller waits with vm_wait().
+__device__ __forceinline__ f32x4 load_coherent_x4(const void *p) {
+  f32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Q rows of one problem, one wave: lane -> (row = lane / 2, half of the
 // row); 16-byte vectors.
@@ -136,59 +171,64 @@ __device__ __forceinline__ void store_q(Smem<D> &sm, const QRegs<D> &qr, int lan
   for (int i = 0; i < D / 16; ++i) dst[i] = qr.v[i];
 }
 
-// Reducer of one row of one problem: merge the row's (m, z) from every block
-// of the prompt in a fixed order (lane l takes blocks l, l + 64, ...; lanes
-// then merge in a fixed binary tree, lower lane first), and publish lse. A
-// slot that is still empty (its block has not posted yet) is read again.
-__device__ void reduce_row(const StreamWs &ws, int prob, int row, int n_cta, int c_lo, int n_c,
-                           int b, int P, int lane) {
-  const unsigned long long *base = ws.part + ((int64_t)prob * n_cta + c_lo) * kRows + row;
-  constexpr int kPer = kMaxCtas / 64;
-  unsigned long long v[kPer];
-  const uint64_t t0 = wall_clock64();
-  for (;;) {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int c = u * 64 + lane;
-      v[u] = c < n_c ? __hip_atomic_load(base + (int64_t)c * kRows, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT)
-                     : 1ull;
-    }
-    bool ok = true;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) ok &= v[u] != 0ull;
-    if (__all(ok)) break;
-    if (wall_clock64() - t0 > kWaitTicks) { timeout(ws.status); break; }
-    __builtin_amdgcn_s_sleep(1);
-  }
-  float M = -INFINITY, Z = 0.f;
-#pragma unroll
-  for (int u = 0; u < kPer; ++u)
-    if (u * 64 + lane < n_c)
-      stats_merge(M, Z, __uint_as_float((unsigned)v[u]), __uint_as_float((unsigned)(v[u] >> 32)));
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float mo = __shfl_xor(M, off, 64), zo = __shfl_xor(Z, off, 64);
-    if (lane & off) {           // lower lane's value first
-      float a = mo, bz = zo;
-      stats_merge(a, bz, M, Z);
-      M = a; Z = bz;
-    } else {
-      stats_merge(M, Z, mo, zo);
-    }
-  }
-  if (lane == 0) {
-    const float l2 = Z > 0.f ? M + log2f(Z) : INFINITY;
-    __hip_atomic_store(ws.lse + ((int64_t)b * P + prob) * kRows + row,
-                       (1ull << 32) | __float_as_uint(l2), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  }
+// Base-2 lse of a set given by its max and its sum of 2^(x - max).
+__device__ __forceinline__ float lse_of(float m, float z) {
+  return (m == -INFINITY || !(z > 0.f)) ? -INFINITY : m + log2f(z);
 }
 
-// Block that reduces row `row` of problem `prob`: spread over the prompt's
-// blocks and rotated from problem to problem.
-__device__ __forceinline__ int reducer_of(int prob, int row, int n_c) {
-  return (row * 37 + prob * 11) % n_c;
+// Merge every block's partial lse of one problem: lane l takes rows
+// 4(l%8) .. 4(l%8)+3 of blocks l/8, l/8 + 8, ... (in block order), then the
+// eight lanes of a row quad merge by an xor tree (each merge is symmetric,
+// so every lane ends with identical bits). Lanes 0..7 return the row lse of
+// rows 4l .. 4l+3. Empty slots (not yet posted, or a stale copy in this
+// die's L2) are read again bypassing the L2.
+__device__ f32x4 gather_lse(const StreamWs &ws, int prob, int n_cta, int c_lo, int n_c, int lane) {
+  const float *base = ws.part + ((int64_t)prob * n_cta + c_lo) * kRows + 4 * (lane & 7);
+  constexpr int kPer = kMaxCtas / 8;
+  const int c0 = lane >> 3;
+  f32x4 v[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c = c0 + 8 * u;
+    v[u] = c < n_c ? *reinterpret_cast<const f32x4 *>(base + (int64_t)c * kRows)
+                   : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  }
+  const uint64_t t0 = wall_clock64();
+  for (;;) {
+    bool ok = true;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ok &= __float_as_uint(v[u][e]) != kEmpty;
+    if (__all(ok)) break;
+    if (wall_clock64() - t0 > kWaitTicks) { timeout(ws.status); break; }
+    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int c = c0 + 8 * u;
+      if (c < n_c) v[u] = load_coherent_x4(base + (int64_t)c * kRows);
+    }
+    vm_wait();
+  }
+  f32x4 out;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) M = fmaxf(M, v[u][e]);
+    float Z = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) Z += __builtin_amdgcn_exp2f(v[u][e] - M);
+    }
+#pragma unroll
+    for (int off = 8; off < 64; off <<= 1) {
+      const float mo = __shfl_xor(M, off, 64), zo = __shfl_xor(Z, off, 64);
+      stats_merge(M, Z, mo, zo);
+    }
+    out[e] = lse_of(M, Z);
+  }
+  return out;
 }
 
 template <int D>
@@ -199,8 +239,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
                                                         float *__restrict__ imp, StreamWs ws) {
   __shared__ Smem<D> sm;
   const int cta = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, r = lane & 31;
-  const bool control = wave == kCompute;
+  // The wave index is uniform across a wave; saying so keeps every value
+  // derived from it in scalar registers and every branch on it scalar.
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, r = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool control = wave >= kCompute;
   const int bb = cta_prompt(tb, cta), b = tb.p0 + bb;
   const int c_lo = tb.cta_off[bb], n_c = tb.cta_off[bb + 1] - c_lo, ci = cta - c_lo;
   const int N = tb.tok_off[bb + 1] - tb.tok_off[bb];
@@ -208,69 +251,78 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
   const int tiles = (NK + kTile - 1) / kTile;
   const int ta = (int)((int64_t)tiles * ci / n_c);
   const int nt = (int)((int64_t)tiles * (ci + 1) / n_c) - ta;
-  const int w_t0 = ta + (nt * wave) / kCompute;
-  const int w_nt = control ? 0 : ta + (nt * (wave + 1)) / kCompute - w_t0;
   const int64_t key0 = (int64_t)tb.tok_off[bb] + (int64_t)b * s.L;
   const int P = s.n_layers * s.Hkv;
-  const int rows = s.L * s.G;
-  const bool row_ok = r < rows;
-  const int jr = row_ok ? r / s.G : 0;
 
   if (control) {
-    // ---------------- control wave: all cross-block work ----------------
-    // Per iteration (after the second barrier): post this problem's block
-    // statistics; start reading the previous problem's lse (needed at the
-    // next iteration); reduce the rows of this problem this block is the
-    // reducer of; load the Q of problem it + 2. Between the two barriers it
-    // only writes LDS from registers.
+    // ---------------- control waves: all cross-block work ----------------
+    // Control wave c takes the problems x = c, c + 2, ...: once the compute
+    // waves' statistics of x are in, it posts the block's partial lse of x,
+    // stages Q(x + 1) (prefetched into its registers), then reads every
+    // block's partials of x, merges them and stages the row lse of x. Each
+    // control wave thus has two problems' time for one such round.
+    const int cw = wave - kCompute;
     QRegs<D> qn;
-    float lse_next = 0.f;
-    load_q(qn, s, q, b, 0, lane);
-    store_q(sm, qn, lane);
-    if (P > 1) load_q(qn, s, q, b, 1, lane);
+    if (cw == 0) {
+      load_q(qn, s, q, b, 0, lane);
+      store_q(sm, qn, lane);
+      if (lane == 0) {
+        sm.q_used = 0;
+        sm.stats_cnt = 0;
+        sm.lse_ready[0] = 0;
+        sm.lse_ready[1] = 0;
+        sm.lse_used = 0;
+        lds_set(&sm.q_seq, 1);
+      }
+    }
+    if (cw + 1 < P) load_q(qn, s, q, b, cw + 1, lane);
     __syncthreads();
-    for (int it = 0; it < P + kLag; ++it) {
-      __syncthreads();   // B1: wave statistics of problem it are in LDS
-      if (it >= kLag && lane < kRows) sm.lse[lane] = lse_next;
-      if (it + 1 < P) store_q(sm, qn, lane);
-      __syncthreads();   // B2: lse of problem it - kLag and Q of problem it + 1 are in LDS
-      if (it < P && lane < kRows) {
+    for (int x = cw; x < P; x += kControl) {
+      lds_wait_ge(&sm.stats_cnt, kCompute * (x + 1), ws.status);
+      if (lane < kRows) {
         float M = -INFINITY, Z = 0.f;
 #pragma unroll
         for (int w = 0; w < kCompute; ++w)
-          stats_merge(M, Z, sm.red[it & 1][w][lane].x, sm.red[it & 1][w][lane].y);
-        __hip_atomic_store(ws.part + ((int64_t)it * n_cta + cta) * kRows + lane, pack2(M, Z),
+          stats_merge(M, Z, sm.red[x & 1][w][lane].x, sm.red[x & 1][w][lane].y);
+        __hip_atomic_store(ws.part + ((int64_t)x * n_cta + cta) * kRows + lane, lse_of(M, Z),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      // Previous problem's lse: published by its reducers one period ago.
-      const int pf = it + 1 - kLag;
-      unsigned long long lv = 0ull;
-      const unsigned long long *lslot =
-          ws.lse + ((int64_t)b * P + (pf >= 0 ? pf : 0)) * kRows + (lane & 31);
-      const bool need = pf >= 0 && pf < P && lane < s.L * s.G;   // padding rows: no lse
-      if (need) lv = __hip_atomic_load(lslot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (it < P) {
-        for (int row = 0; row < kRows; ++row)
-          if (row < s.L * s.G && reducer_of(it, row, n_c) == ci)
-            reduce_row(ws, it, row, n_cta, c_lo, n_c, b, P, lane);
+      if (x + 1 < P) {
+        lds_wait_ge(&sm.q_used, kCompute * (x + 1), ws.status);   // Q(x) read by all
+        store_q(sm, qn, lane);
+        if (lane == 0) lds_set(&sm.q_seq, x + 2);
+        if (x + 1 + kControl < P) load_q(qn, s, q, b, x + 1 + kControl, lane);
       }
-      if (it + 2 < P) load_q(qn, s, q, b, it + 2, lane);
-      if (pf >= 0 && pf < P) {
-        if (need) {
-          const uint64_t t0 = wall_clock64();
-          while (!(lv >> 32)) {
-            if (wall_clock64() - t0 > kWaitTicks) { timeout(ws.status); break; }
-            __builtin_amdgcn_s_sleep(1);
-            lv = __hip_atomic_load(lslot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-        lse_next = __uint_as_float((unsigned)lv);
-      }
+      const f32x4 lq = gather_lse(ws, x, n_cta, c_lo, n_c, lane);
+      if (x >= 2) lds_wait_ge(&sm.lse_used, kCompute * (x - 1), ws.status);   // slot is free
+      if (lane < 8) *reinterpret_cast<f32x4 *>(&sm.lse[x & 1][4 * lane]) = lq;
+      if (lane == 0) lds_set(&sm.lse_ready[x & 1], x + 1);
     }
     return;
   }
 
   // ---------------- compute waves ----------------
+  const int w_t0 = ta + (nt * wave) / kCompute;
+  const int w_nt = ta + (nt * (wave + 1)) / kCompute - w_t0;
+  const int rows = s.L * s.G;
+  const bool row_ok = r < rows;
+  const int jr = row_ok ? r / s.G : 0;
+  const float sl2 = s.scale_log2;
+  // K addressing: a per-problem base pointer plus a 32-bit per-lane element
+  // offset of each tile's key row (clamped into the prompt; keys outside the
+  // wave's tiles are masked later). Loads are unconditional, which keeps
+  // the compiler's wait counts exact: a tile's MFMAs wait for its loads only.
+  const int64_t kstride_l = total_keys * s.Hkv * D;   // elements per layer
+  uint32_t koff[kTPW];
+#pragma unroll
+  for (int t = 0; t < kTPW; ++t) {
+    const int key = min((w_t0 + t) * kTile + r, NK - 1);
+    koff[t] = (uint32_t)((int64_t)key * s.Hkv * D) + 8u * half;
+  }
+  const __bf16 *kprompt = k + key0 * s.Hkv * D;
+  // A tile is "full" when all its keys are prompt keys: no masking needed.
+  const int full_tiles = max(0, min((N - w_t0 * kTile) / kTile, w_nt));
+
   Frag<__bf16, D> kf[kTPW];
   f32x16 E[kTPW], run[kTPW];
 #pragma unroll
@@ -283,21 +335,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
 #pragma unroll
     for (int t = 0; t < kTPW; ++t) mref[a][t] = -INFINITY;
 
-  // Loads are unconditional (addresses clamped into the prompt; keys outside
-  // the wave's tiles are masked later), which keeps the compiler's wait
-  // counts exact: a tile's MFMAs wait for that tile's loads only.
-  auto load_k = [&](int prob, int t) {
-    const int l = prob / s.Hkv, g = prob - l * s.Hkv;
-    const int key = min((w_t0 + t) * kTile + r, NK - 1);
-    kf[t].load(k_row_ptr(k, s, total_keys, l, key0 + key, g), half);
+  auto load_k = [&](const __bf16 *kb, int t) {
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(kb + koff[t]);
+#pragma unroll
+    for (int st = 0; st < Frag<__bf16, D>::kSteps; ++st)
+      kf[t].v[st] = __builtin_nontemporal_load(p + 2 * st);
   };
 
 #pragma unroll
-  for (int t = 0; t < kTPW; ++t) load_k(0, t);
+  for (int t = 0; t < kTPW; ++t) load_k(kprompt, t);
   __syncthreads();
 
-  // Q operand rows in LDS: lane r reads its row's 8 bf16 of each k-step.
   const u32x4 *qs = reinterpret_cast<const u32x4 *>(&sm.q[r][0]) + half;
+  int ln = 0, gn = 0;     // (layer, group) of the next problem to load
 
   for (int it = 0; it < P + kLag; ++it) {
     const int slot = it % kLag;
@@ -306,53 +356,79 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
 #pragma unroll
       for (int t = 0; t < kTPW; ++t) mref[a][t] = mref[a - 1][t];
     if (it < P) {
-      // Tile by tile: logits, online max / sum; e relative to the running
-      // max at that tile (kept in mref).
-      float m = -INFINITY, z = 0.f;
+      // Q of this problem is read from LDS at each k-step of each tile (a
+      // register copy would not fit), so the staging buffer is released
+      // after the last tile's MFMAs.
+      lds_wait_ge(&sm.q_seq, it + 1, ws.status);
+      // Base of the next problem's K (the last problem reloads its own).
+      if (it + 1 < P && ++gn == s.Hkv) { gn = 0; ++ln; }
+      const __bf16 *kb_next = kprompt + ln * kstride_l + gn * D;
+      float m = -INFINITY, z = 0.f;    // base-2 running max and sum of this lane's keys
 #pragma unroll
       for (int t = 0; t < kTPW; ++t) {
+        asm volatile("" ::: "memory");   // keep the Q reads inside the tile
         f32x16 x = {};
 #pragma unroll
         for (int st = 0; st < Frag<__bf16, D>::kSteps; ++st)
           x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[t].v[st]),
                                                      __builtin_bit_cast(bf16x8, qs[2 * st]), x, 0,
                                                      0, 0);
-        load_k(it + 1 < P ? it + 1 : it, t);   // the last problem reloads its own tile
-        float mt = -INFINITY;
+        if (t == kTPW - 1 && lane == 0) lds_inc(&sm.q_used);
+        load_k(kb_next, t);
+        if (t < full_tiles) {
+          // All keys are prompt keys, seen by every row: no masks. (Padding
+          // rows compute harmless values that are never folded.)
+          float mt = x[0];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = (w_t0 + t) * kTile + acc_row(i, half);
-          const bool ok = row_ok && t < w_nt && key <= N + jr;   // causal; implies key < NK
-          x[i] = ok ? x[i] * s.scale_log2 : -INFINITY;
-          mt = fmaxf(mt, x[i]);
-        }
-        const float mn = fmaxf(m, mt);
-        if (mn != -INFINITY) {
+          for (int i = 1; i < 16; ++i) mt = fmaxf(mt, x[i]);
+          const float mn = fmaxf(m, mt * sl2);
           z = m == -INFINITY ? 0.f : z * __builtin_amdgcn_exp2f(m - mn);
           m = mn;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], sl2, -m));
+            z += e;
+            E[t][i] = e;
+          }
+        } else {
+          // Tail tile: invalid keys, causal lookahead keys, padding rows.
+          float mt = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = (w_t0 + t) * kTile + acc_row(i, half);
+            const bool ok = row_ok && t < w_nt && key <= N + jr;   // causal; implies key < NK
+            x[i] = ok ? x[i] * sl2 : -INFINITY;
+            mt = fmaxf(mt, x[i]);
+          }
+          const float mn = fmaxf(m, mt);
+          if (mn != -INFINITY) {
+            z = m == -INFINITY ? 0.f : z * __builtin_amdgcn_exp2f(m - mn);
+            m = mn;
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float e = x[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[i] - m);
+            z += e;
+            const int key = (w_t0 + t) * kTile + acc_row(i, half);
+            E[t][i] = key < N ? e : 0.f;    // lookahead keys get no importance
+          }
         }
         mref[0][t] = m;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float e = x[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[i] - m);
-          z += e;
-          const int key = (w_t0 + t) * kTile + acc_row(i, half);
-          E[t][i] = key < N ? e : 0.f;    // lookahead keys get no importance
-        }
       }
-      // Merge the two wave halves (same row, different keys).
+      // Merge the two wave halves (same row, different keys) and hand the
+      // wave's statistics to the control wave.
       const float mo = __shfl_xor(m, 32, 64), zo = __shfl_xor(z, 32, 64);
-      float M = m, Z = z;
-      if (half) { M = mo; Z = zo; stats_merge(M, Z, m, z); }
-      else stats_merge(M, Z, mo, zo);
-      if (lane < 32) sm.red[it & 1][wave][r] = make_float2(M, Z);
+      stats_merge(m, z, mo, zo);
+      if (lane < 32) sm.red[it & 1][wave][r] = make_float2(m, z);
+      if (lane == 0) lds_inc(&sm.stats_cnt);
     }
-    __syncthreads();   // B1
-    __syncthreads();   // B2
     if (it >= kLag) {
-      // Fold problem it - kLag: p = e * 2^(m_tile - lse), max into run;
-      // then its LDS slot takes this problem's e (same lane, in order).
-      const float l2 = sm.lse[r];
+      // Fold problem it - kLag once its lse is staged: p = e * 2^(m_tile -
+      // lse), max into run; then its LDS slot takes this problem's e (same
+      // lane, in order).
+      lds_wait_ge(&sm.lse_ready[(it - kLag) & 1], it - kLag + 1, ws.status);
+      const float l2 = sm.lse[(it - kLag) & 1][r];
+      if (lane == 0) lds_inc(&sm.lse_used);
 #pragma unroll
       for (int t = 0; t < kTPW; ++t) {
         const float mr = mref[kLag][t];
@@ -377,34 +453,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
 
   // Max over the G heads of each step (lanes j*G .. j*G+G-1), then the mean
   // over the steps (groups of lanes; padding rows hold 0).
-  {
+#pragma unroll
+  for (int t = 0; t < kTPW; ++t) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float v = run[t][i];
+      for (int off = 1; off < s.G; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+      for (int off = s.G; off < kRows; off <<= 1) v += __shfl_xor(v, off, 64);
+      run[t][i] = v;
+    }
+  }
+  if (r == 0) {
+    float *out = imp + tb.tok_off[bb];
 #pragma unroll
     for (int t = 0; t < kTPW; ++t) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float v = run[t][i];
-        for (int off = 1; off < s.G; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-        for (int off = s.G; off < kRows; off <<= 1) v += __shfl_xor(v, off, 64);
-        run[t][i] = v;
-      }
-    }
-    if (r == 0) {
-      float *out = imp + tb.tok_off[bb];
-#pragma unroll
-      for (int t = 0; t < kTPW; ++t) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = (w_t0 + t) * kTile + acc_row(i, half);
-          if (t < w_nt && key < N) out[key] = run[t][i] / (float)s.L;
-        }
+        const int key = (w_t0 + t) * kTile + acc_row(i, half);
+        if (t < w_nt && key < N) out[key] = run[t][i] / (float)s.L;
       }
     }
   }
 }
 
-__global__ void k_zero(u32x4 *p, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
-    p[i] = u32x4{0u, 0u, 0u, 0u};
+// Status word to 0 and every partial slot to the empty (NaN) pattern.
+__global__ void k_prepare(int *status, u32x4 *part, int n16) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += gridDim.x * blockDim.x)
+    part[i] = u32x4{kEmpty, kEmpty, kEmpty, kEmpty};
 }
 
 struct DeviceInfo {
@@ -497,22 +573,10 @@ int stream_ctas(const AttnShape &s) {
   const DeviceInfo &d = device_info();
   const int occ = s.d == 128 ? d.occ128 : d.occ64;
   if (!d.coop || occ < 1 || d.cus < 1) return 0;
-  return d.cus;
+  return std::min(d.cus, kMaxCtas);
 }
 
-
-StreamWs carve(void *ws, int B, int P, size_t *zero_bytes) {
-  char *p = reinterpret_cast<char *>(ws);
-  StreamWs w;
-  w.status = reinterpret_cast<int *>(p);
-  p += align_up(kStatusWords * sizeof(int));
-  w.lse = reinterpret_cast<unsigned long long *>(p);
-  p += align_up((size_t)B * P * kRows * sizeof(unsigned long long));
-  w.part = reinterpret_cast<unsigned long long *>(p);
-  p += align_up((size_t)P * kMaxCtas * kRows * sizeof(unsigned long long));
-  *zero_bytes = (size_t)(p - reinterpret_cast<char *>(ws));
-  return w;
-}
+size_t part_bytes(int P) { return align_up((size_t)P * kMaxCtas * kRows * sizeof(float)); }
 
 }  // namespace
 
@@ -525,11 +589,9 @@ bool score_stream_supported(const AttnShape &s, int B, int total_tiles) {
 }
 
 size_t score_stream_ws(const AttnShape &s, int B, int total_tiles) {
+  (void)B;
   (void)total_tiles;
-  const int P = s.n_layers * s.Hkv;
-  return align_up(kStatusWords * sizeof(int)) +
-         align_up((size_t)B * P * kRows * sizeof(unsigned long long)) +
-         align_up((size_t)P * kMaxCtas * kRows * sizeof(unsigned long long));
+  return kStatusBytes + part_bytes(s.n_layers * s.Hkv);
 }
 
 hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, int total_tiles,
@@ -538,26 +600,24 @@ hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, int to
   *supported = false;
   if (!score_stream_supported(s, tiles.B, total_tiles)) return hipSuccess;
   const int n_cta = stream_ctas(s);
-  if (n_cta < 1 || n_cta > kMaxCtas) return hipSuccess;
+  if (n_cta < 1) return hipSuccess;
   static thread_local Plan plan;
   if (!make_plan(tiles, s.L, n_cta, plan)) return hipSuccess;
   if (ws_bytes < score_stream_ws(s, tiles.B, total_tiles)) return hipSuccess;
   *supported = true;
   const int P = s.n_layers * s.Hkv;
-  size_t zb = 0;
-  StreamWs w = carve(ws, tiles.B, P, &zb);
-  // Only the part slots the launches use need clearing, not all kMaxCtas.
-  const size_t used = (size_t)((char *)(w.part + (size_t)P * n_cta * kRows) - (char *)w.status);
-  (void)zb;
-  const int nzero = (int)(used / sizeof(u32x4));
-  hipLaunchKernelGGL(k_zero, dim3(std::min(1024, (nzero + 255) / 256)), dim3(256), 0, st,
-                     reinterpret_cast<u32x4 *>(w.status), nzero);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  StreamWs w;
+  w.status = reinterpret_cast<int *>(ws);
+  w.part = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + kStatusBytes);
   const int64_t total_keys = (int64_t)tiles.tok_off[tiles.B] + (int64_t)tiles.B * tiles.L;
   const __bf16 *qp = reinterpret_cast<const __bf16 *>(q);
   const __bf16 *kp = reinterpret_cast<const __bf16 *>(k);
+  const int n16 = (int)((size_t)P * n_cta * kRows * sizeof(float) / sizeof(u32x4));
   for (int li = 0; li < plan.n_launch; ++li) {
+    hipLaunchKernelGGL(k_prepare, dim3(std::min(256, (n16 + 255) / 256)), dim3(256), 0, st,
+                       w.status, reinterpret_cast<u32x4 *>(w.part), n16);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     StreamTable tb = plan.t[li];
     int ncta = n_cta;
     AttnShape sh = s;
