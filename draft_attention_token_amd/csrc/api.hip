@@ -5,6 +5,21 @@
 
 #include "sp_internal.h"
 
+#include <atomic>
+
+namespace sp {
+
+uint32_t reserve_tags(int n) {
+  static std::atomic<uint32_t> next{1u};
+  for (;;) {
+    const uint32_t base = next.fetch_add((uint32_t)n);
+    // Tag 0 marks a never-written slot: skip a range that wraps through it.
+    if (base != 0u && (uint32_t)(base + (uint32_t)(n - 1)) >= base) return base;
+  }
+}
+
+}  // namespace sp
+
 using namespace sp;
 
 namespace {
@@ -100,6 +115,13 @@ sp_status check_chunks(const sp_batch *batch, int32_t C, int *max_nc) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Scoring workspace: header, single-pass slots, two-pass region (one layout
+// for every algorithm, so calls with different algorithms can share it).
+size_t score_ws_bytes(const AttnShape &s, const SegTable &tiles) {
+  return kStatusBytes + score_stream_slot_bytes(s) +
+         score_two_pass_region_bytes(s, tiles.B, tiles.unit_off[tiles.B]);
+}
+
 sp_status launched(hipError_t e) { return e == hipSuccess ? SP_OK : SP_ERR_DEVICE; }
 
 }  // namespace
@@ -128,14 +150,7 @@ sp_status sp_score_workspace_bytes(const sp_attn_desc *desc, const sp_batch *bat
   if (st != SP_OK) return st;
   if ((st = check_batch(batch, &total)) != SP_OK) return st;
   const SegTable tiles = make_table(batch, s.L, kTile, s.L);
-  const int total_tiles = tiles.unit_off[tiles.B];
-  // Enough for whichever kernel the call may run (AUTO can fall back).
-  size_t need = score_two_pass_ws(s, tiles.B, total_tiles);
-  if (desc->algo != SP_SCORE_TWO_PASS && score_stream_supported(s, tiles.B, total_tiles)) {
-    const size_t ss = score_stream_ws(s, tiles.B, total_tiles);
-    need = desc->algo == SP_SCORE_STREAM ? ss : (ss > need ? ss : need);
-  }
-  *bytes = need;
+  *bytes = score_ws_bytes(s, tiles);
   return SP_OK;
 }
 
@@ -148,32 +163,31 @@ sp_status sp_score_attention(const sp_attn_desc *desc, const sp_batch *batch, co
   if (st != SP_OK) return st;
   if ((st = check_batch(batch, &total)) != SP_OK) return st;
   if (!q || !k || !importance) return SP_ERR_INVALID_ARGUMENT;
-  if (!aligned16(q) || !aligned16(k)) return SP_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(ws)) return SP_ERR_INVALID_ARGUMENT;
   const SegTable tiles = make_table(batch, s.L, kTile, s.L);
   const int total_tiles = tiles.unit_off[tiles.B];
+  if (!ws || ws_bytes < score_ws_bytes(s, tiles)) return SP_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  const bool stream_ok = score_stream_supported(s, tiles.B, total_tiles);
-  if (desc->algo == SP_SCORE_STREAM && !stream_ok) return SP_ERR_UNSUPPORTED;
-  if (desc->algo != SP_SCORE_TWO_PASS && stream_ok) {
-    const size_t need = score_stream_ws(s, tiles.B, total_tiles);
-    if (ws_bytes < need || (need && !ws)) return SP_ERR_WORKSPACE_TOO_SMALL;
-    bool supported = true;
-    hipError_t e = launch_score_stream(s, tiles, total_tiles, q, k, importance, ws, ws_bytes, hs,
-                                       &supported);
+  if (desc->algo == SP_SCORE_STREAM && !score_stream_supported(s)) return SP_ERR_UNSUPPORTED;
+  if (desc->algo != SP_SCORE_TWO_PASS) {
+    bool supported = false;
+    const hipError_t e = launch_score_stream(s, tiles, q, k, importance, ws, hs, &supported);
     if (supported) return launched(e);
     if (desc->algo == SP_SCORE_STREAM) return SP_ERR_UNSUPPORTED;
   }
-  const size_t need = score_two_pass_ws(s, tiles.B, total_tiles);
-  if (ws_bytes < need || !ws) return SP_ERR_WORKSPACE_TOO_SMALL;
-  return launched(launch_score_two_pass(s, tiles, total_tiles, q, k, importance, ws, hs));
+  char *region = reinterpret_cast<char *>(ws) + kStatusBytes + score_stream_slot_bytes(s);
+  return launched(launch_score_two_pass(s, tiles, total_tiles, q, k, importance,
+                                        reinterpret_cast<uint32_t *>(ws), region, hs));
 }
 
 sp_status sp_score_status(const void *ws, int32_t *status_host, void *stream) {
   if (!ws || !status_host) return SP_ERR_INVALID_ARGUMENT;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  if (hipMemcpyAsync(status_host, ws, sizeof(int32_t), hipMemcpyDeviceToHost, hs) != hipSuccess ||
+  uint32_t hdr[2] = {0u, 0u};
+  if (hipMemcpyAsync(hdr, ws, sizeof(hdr), hipMemcpyDeviceToHost, hs) != hipSuccess ||
       hipStreamSynchronize(hs) != hipSuccess)
     return SP_ERR_DEVICE;
+  *status_host = (hdr[1] != 0u && hdr[0] == hdr[1]) ? 1 : 0;
   return SP_OK;
 }
 

@@ -10,9 +10,10 @@
 // row sees, so no probability is final before all of K has been read. Rather
 // than read K twice, the logits stay on chip and the lse arrives later:
 //
-//  * Persistent grid, one block per CU, all blocks co-resident (cooperative
-//    launch). A block owns <= 18 contiguous 32-key tiles of one prompt for
-//    the whole kernel (prompt keys and lookahead keys alike).
+//  * Persistent grid, one block per CU (a block's shared memory admits only
+//    one per unit), all blocks resident at once. A block owns <= 18
+//    contiguous 32-key tiles of one prompt for the whole kernel (prompt keys
+//    and lookahead keys alike).
 //  * The work is a sequence of problems (layer l, KV group g), each with
 //    L * G <= 32 query rows (step j, head-in-group hh), padded to 32.
 //  * Six compute waves per block, <= 3 tiles each. Per problem a wave
@@ -25,33 +26,44 @@
 //    synchronisation. Statistics are accumulated tile by tile (online max,
 //    rescaled sum); each tile's e = 2^(x - m) is relative to the running max
 //    m at that tile, kept per tile.
-//  * Two control waves per block do all cross-block work, so no compute
-//    wave ever waits on a memory operation other than its own K loads (on
-//    this hardware a wait on any load also waits on every load issued
-//    before it, which would drain the K prefetch). They take alternate
-//    problems: for its problem x a control wave merges the compute waves'
+//  * The last compute wave to finish a problem merges the six waves'
 //    statistics into the block's partial base-2 lse of each row and posts
-//    it (one float per row), stages Q(x + 1), then reads every block's
-//    partials of x (plain loads, shared through the L2 of its chip die),
-//    merges them in block order and stages the row lse of x in LDS.
-//    Compute and control waves hand data over through LDS flags rather than
-//    block barriers, so a slow cross-block read only stalls the compute
-//    waves when they need its result.
+//    it to the workspace (one float per row) at once.
+//  * Two control waves do the rest of the cross-block work, so no compute
+//    wave ever waits on a load other than its own K (on this hardware a
+//    wait on any load also waits on every load issued before it, which
+//    would drain the K prefetch). They take alternate problems: for its
+//    problem x a control wave stages Q(x + 1) (prefetched into its
+//    registers), then reads every block's partials of x (plain loads,
+//    shared through the L2 of its chip die), merges them in block order and
+//    stages the row lse of x in LDS. Compute and control waves hand data
+//    over through LDS flags rather than block barriers, so a slow
+//    cross-block read only stalls the compute waves when they need its
+//    result.
 //  * The compute waves fold problem i - 2 while working on problem i: they
 //    park e in LDS (two problem slots) and turn it into probabilities
 //    p = e * 2^(m_tile - lse) once the lse is staged, kept as a running max
 //    per (row, key) in registers (max over layers and KV groups).
 //  * Finally: max over the G heads of a step (lanes of a group), mean over
-//    the L steps (a fixed tree across groups of lanes), store.
+//    the L steps (a butterfly across groups of lanes), store.
 //
-// Partial slots start as a NaN pattern (written before the launch); a real
-// partial is never NaN, so a slot read before its block posted is detected
-// and read again with a load that bypasses this die's L2. Every wait is
-// bounded (about 2 s); on time-out the kernel records it in the workspace
-// status word and runs to completion, so the grid always drains.
+// Partial slots. A slot holding all-zero bits has not been posted (a posted
+// value is never +0.0: it is stored as -0.0). A block that reads an empty
+// slot (not posted yet, or a stale copy in its die's L2) reads it again with
+// a load that bypasses the L2. Slots are left empty for the next launch:
+// once a block has merged every block's partials of problem x, every block
+// has finished reading the partials of problem x - 3 (a block posts x only
+// after folding x - 2, which needs its merge of x - 2 and, before that, of
+// x - 3), so the block clears its own slots of x - 3; the last block to
+// finish clears the final three problems' slots of every block. A zero-filled
+// workspace is therefore ready for the first launch and stays ready.
+//
+// Every wait is bounded (about 2 s); on time-out the kernel records it in the
+// workspace header and runs to completion, so the grid always drains.
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "score_common.h"
 
@@ -64,10 +76,10 @@ constexpr int kThreads = (kCompute + kControl) * 64;
 constexpr int kTPW = 3;                           // tiles per compute wave
 constexpr int kTilesPerCta = kCompute * kTPW;     // 18
 constexpr int kLag = 2;                           // problems between logits and fold
+constexpr int kClearLag = 3;                      // slots of x - 3 are free after merging x
 constexpr uint64_t kWaitTicks = 200000000ull;     // wall clock runs at 100 MHz: 2 s
 constexpr int kQPad = 8;                          // bf16 padding per staged Q row
 constexpr int kMaxCtas = 256;                     // blocks per launch (one per CU)
-constexpr unsigned kEmpty = 0xffffffffu;          // unwritten partial slot (a NaN)
 
 struct StreamTable {
   int32_t B;        // prompts in this launch
@@ -77,24 +89,28 @@ struct StreamTable {
 };
 
 struct StreamWs {
-  int *status;      // status[0] != 0: a wait timed out
-  float *part;      // [P][n_cta][32] each block's partial base-2 lse per row
+  uint32_t *hdr;    // [0]: tag of a call that timed out; [1]: tag of the latest
+                    // call; [2]: blocks of the running launch that have finished
+  uint32_t *slot;   // [P][n_cta][32]: bits of each block's partial lse per row
+  uint32_t call_tag;
 };
 
 template <int D>
 struct Smem {
   f32x4 eprev[kLag][kCompute][kTPW][4][64];   // parked e values (16-byte slots per lane)
   __bf16 q[kRows][D + kQPad];                 // staged Q rows of the next problem
-  float2 red[2][kCompute][kRows];             // per-wave (m, z) of a problem
+  float2 red[2][kCompute][kRows];             // per-wave (m, z) of a problem, by parity
   float lse[2][kRows];                        // staged row lse, by problem parity
-  // Hand-offs between the compute waves and the control wave (no block
+  // Hand-offs between the compute waves and the control waves (no block
   // barrier inside the main loop, so neither side waits for the other
-  // unless it needs the other's data):
+  // unless it needs the other's data). Counters are cumulative.
   int q_seq;         // Q of problems < q_seq has been staged (one at a time)
-  int q_used;        // compute waves that have read the staged Q (cumulative)
-  int stats_cnt;     // compute waves that have written their statistics (cumulative)
+  int q_used;        // compute waves that have read the staged Q
+  int stats_cnt;     // compute waves that have written their statistics
+  int posted;        // problems this block has posted
   int lse_ready[2];  // lse[s] holds problem lse_ready[s] - 1 (0: nothing yet)
-  int lse_used;      // compute waves that have folded with a staged lse (cumulative)
+  int lse_used;      // compute waves that have folded with a staged lse
+  int ctl_done;      // control waves that have finished
 };
 
 __device__ __forceinline__ int lds_get(const int *p) {
@@ -104,17 +120,21 @@ __device__ __forceinline__ void lds_set(int *p, int v) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // data written before the flag
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void lds_inc(int *p) {
+__device__ __forceinline__ int lds_inc(int *p) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
+__device__ __forceinline__ void timeout(const StreamWs &ws) {
+  __hip_atomic_store(ws.hdr, ws.call_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Wait (bounded) until *p >= v.
-__device__ __forceinline__ void lds_wait_ge(const int *p, int v, int *status) {
+__device__ __forceinline__ void lds_wait_ge(const int *p, int v, const StreamWs &ws) {
   if (lds_get(p) >= v) return;
   const uint64_t t0 = wall_clock64();
   while (lds_get(p) < v) {
     if (wall_clock64() - t0 > kWaitTicks) {
-      __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      timeout(ws);
       break;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -130,19 +150,6 @@ __device__ __forceinline__ int cta_prompt(const StreamTable &t, int c) {
   }
   return lo;
 }
-
-__device__ __forceinline__ void timeout(int *status) {
-  __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// 16-byte load that bypasses this die's L2 (coherent across the chip); the
-// caller waits with vm_wait().
-__device__ __forceinline__ f32x4 load_coherent_x4(const void *p) {
-  f32x4 v;
-  asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
-__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Q rows of one problem, one wave: lane -> (row = lane / 2, half of the
 // row); 16-byte vectors.
@@ -177,57 +184,76 @@ __device__ __forceinline__ float lse_of(float m, float z) {
 }
 
 // Merge every block's partial lse of one problem: lane l takes rows
-// 4(l%8) .. 4(l%8)+3 of blocks l/8, l/8 + 8, ... (in block order), then the
-// eight lanes of a row quad merge by an xor tree (each merge is symmetric,
-// so every lane ends with identical bits). Lanes 0..7 return the row lse of
-// rows 4l .. 4l+3. Empty slots (not yet posted, or a stale copy in this
-// die's L2) are read again bypassing the L2.
+// 4 (l % 8) .. 4 (l % 8) + 3 of blocks l / 8, l / 8 + 8, ... (in block order),
+// then the eight lanes of a row quad merge by an xor tree (each merge is
+// symmetric, so every lane ends with identical bits). Lanes 0..7 return the
+// row lse of rows 4 l .. 4 l + 3. Empty slots are read again bypassing the L2.
+//
+// Buffer loads: the resource covers exactly this prompt's slots of the
+// problem, so the loads of blocks past its last one return zeros without
+// touching memory, and each load's block offset is a scalar operand (no
+// per-load address registers).
 __device__ f32x4 gather_lse(const StreamWs &ws, int prob, int n_cta, int c_lo, int n_c, int lane) {
-  const float *base = ws.part + ((int64_t)prob * n_cta + c_lo) * kRows + 4 * (lane & 7);
   constexpr int kPer = kMaxCtas / 8;
+  constexpr int kStride = 8 * kRows * (int)sizeof(float);   // bytes between a lane's blocks
+  const uint32_t *base = ws.slot + ((int64_t)prob * n_cta + c_lo) * kRows;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t *>(base), 0, n_c * kRows * (int)sizeof(float), 0x00020000);
   const int c0 = lane >> 3;
-  f32x4 v[kPer];
+  const int voff = c0 * kRows * (int)sizeof(float) + (lane & 7) * 16;
+  u32x4 v[kPer];
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int c = c0 + 8 * u;
-    v[u] = c < n_c ? *reinterpret_cast<const f32x4 *>(base + (int64_t)c * kRows)
-                   : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  }
+  for (int u = 0; u < kPer; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, u * kStride, 0);
   const uint64_t t0 = wall_clock64();
   for (;;) {
     bool ok = true;
 #pragma unroll
     for (int u = 0; u < kPer; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ok &= __float_as_uint(v[u][e]) != kEmpty;
+      ok &= (c0 + 8 * u >= n_c) | ((v[u][0] != 0u) & (v[u][1] != 0u) & (v[u][2] != 0u) & (v[u][3] != 0u));
     if (__all(ok)) break;
-    if (wall_clock64() - t0 > kWaitTicks) { timeout(ws.status); break; }
-    __builtin_amdgcn_s_sleep(2);
+    if (wall_clock64() - t0 > kWaitTicks) { timeout(ws); break; }
+    __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");   // the slots change behind the compiler's back: reload
+    // Only the quads with an empty slot; cache policy 16: device-coherent
+    // (bypasses this die's L2).
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int c = c0 + 8 * u;
-      if (c < n_c) v[u] = load_coherent_x4(base + (int64_t)c * kRows);
-    }
-    vm_wait();
+    for (int u = 0; u < kPer; ++u)
+      if ((v[u][0] == 0u) | (v[u][1] == 0u) | (v[u][2] == 0u) | (v[u][3] == 0u))
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, u * kStride, 16);
   }
+  // Row max first (exact, so the order does not matter), across the lanes
+  // of the row quad too; then one exp per partial and a sum tree. Every
+  // combination is of two values, so all lanes of a quad end with the same
+  // bits (a + b == b + a).
+  f32x4 M = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const bool in = c0 + 8 * u < n_c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) M[e] = fmaxf(M[e], in ? __uint_as_float(v[u][e]) : -INFINITY);
+  }
+#pragma unroll
+  for (int off = 8; off < 64; off <<= 1)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) M[e] = fmaxf(M[e], __shfl_xor(M[e], off, 64));
+  f32x4 Z = {0.f, 0.f, 0.f, 0.f};
+  f32x4 Ms;   // M, or 0 where the row has no keys (keeps the exps finite)
+#pragma unroll
+  for (int e = 0; e < 4; ++e) Ms[e] = M[e] == -INFINITY ? 0.f : M[e];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const bool in = c0 + 8 * u < n_c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      Z[e] += in ? __builtin_amdgcn_exp2f(__uint_as_float(v[u][e]) - Ms[e]) : 0.f;
+  }
+#pragma unroll
+  for (int off = 8; off < 64; off <<= 1)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Z[e] += __shfl_xor(Z[e], off, 64);
   f32x4 out;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) M = fmaxf(M, v[u][e]);
-    float Z = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) Z += __builtin_amdgcn_exp2f(v[u][e] - M);
-    }
-#pragma unroll
-    for (int off = 8; off < 64; off <<= 1) {
-      const float mo = __shfl_xor(M, off, 64), zo = __shfl_xor(Z, off, 64);
-      stats_merge(M, Z, mo, zo);
-    }
-    out[e] = lse_of(M, Z);
-  }
+  for (int e = 0; e < 4; ++e) out[e] = lse_of(M[e], Z[e]);
   return out;
 }
 
@@ -255,12 +281,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
   const int P = s.n_layers * s.Hkv;
 
   if (control) {
-    // ---------------- control waves: all cross-block work ----------------
+    // ---------------- control waves: merges, Q staging ----------------
     // Control wave c takes the problems x = c, c + 2, ...: once the compute
-    // waves' statistics of x are in, it posts the block's partial lse of x,
-    // stages Q(x + 1) (prefetched into its registers), then reads every
-    // block's partials of x, merges them and stages the row lse of x. Each
-    // control wave thus has two problems' time for one such round.
+    // waves' statistics of x are in, it stages Q(x + 1) (prefetched into its
+    // registers), then reads every block's partials of x, merges them and
+    // stages the row lse of x. Each control wave thus has two problems'
+    // time for one such round.
     const int cw = wave - kCompute;
     QRegs<D> qn;
     if (cw == 0) {
@@ -269,34 +295,51 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
       if (lane == 0) {
         sm.q_used = 0;
         sm.stats_cnt = 0;
+        sm.posted = 0;
         sm.lse_ready[0] = 0;
         sm.lse_ready[1] = 0;
         sm.lse_used = 0;
+        sm.ctl_done = 0;
         lds_set(&sm.q_seq, 1);
+        __hip_atomic_store(ws.hdr + 1, ws.call_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     if (cw + 1 < P) load_q(qn, s, q, b, cw + 1, lane);
     __syncthreads();
     for (int x = cw; x < P; x += kControl) {
-      lds_wait_ge(&sm.stats_cnt, kCompute * (x + 1), ws.status);
-      if (lane < kRows) {
-        float M = -INFINITY, Z = 0.f;
-#pragma unroll
-        for (int w = 0; w < kCompute; ++w)
-          stats_merge(M, Z, sm.red[x & 1][w][lane].x, sm.red[x & 1][w][lane].y);
-        __hip_atomic_store(ws.part + ((int64_t)x * n_cta + cta) * kRows + lane, lse_of(M, Z),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      lds_wait_ge(&sm.stats_cnt, kCompute * (x + 1), ws);
       if (x + 1 < P) {
-        lds_wait_ge(&sm.q_used, kCompute * (x + 1), ws.status);   // Q(x) read by all
+        lds_wait_ge(&sm.q_used, kCompute * (x + 1), ws);   // Q(x) read by all
         store_q(sm, qn, lane);
         if (lane == 0) lds_set(&sm.q_seq, x + 2);
-        if (x + 1 + kControl < P) load_q(qn, s, q, b, x + 1 + kControl, lane);
       }
+      lds_wait_ge(&sm.posted, x + 1, ws);                   // our own partial is out
       const f32x4 lq = gather_lse(ws, x, n_cta, c_lo, n_c, lane);
-      if (x >= 2) lds_wait_ge(&sm.lse_used, kCompute * (x - 1), ws.status);   // slot is free
+      // The Q prefetch goes out after the gather's loads, so their wait
+      // does not include it.
+      if (x + 1 + kControl < P) load_q(qn, s, q, b, x + 1 + kControl, lane);
+      if (x >= 2) lds_wait_ge(&sm.lse_used, kCompute * (x - 1), ws);   // slot is free
       if (lane < 8) *reinterpret_cast<f32x4 *>(&sm.lse[x & 1][4 * lane]) = lq;
       if (lane == 0) lds_set(&sm.lse_ready[x & 1], x + 1);
+      // Every block has read our partials of x - 3: leave them empty.
+      if (x >= kClearLag && lane < kRows)
+        ws.slot[((int64_t)(x - kClearLag) * n_cta + cta) * kRows + lane] = 0u;
+    }
+    // The last control wave of the last block out empties the slots of the
+    // final problems, which no block can clear earlier.
+    const int order = __builtin_amdgcn_readfirstlane(lane == 0 ? lds_inc(&sm.ctl_done) : 0);
+    if (order == kControl - 1) {
+      const uint32_t done = __builtin_amdgcn_readfirstlane(
+          lane == 0 ? __hip_atomic_fetch_add(ws.hdr + 2, 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)
+                    : 0u);
+      if (done == gridDim.x - 1) {
+        const int x0 = P > kClearLag ? P - kClearLag : 0;
+        const int n16 = (P - x0) * n_cta * kRows / 4;
+        u32x4 *tail = reinterpret_cast<u32x4 *>(ws.slot + (int64_t)x0 * n_cta * kRows);
+        for (int i = lane; i < n16; i += 64) tail[i] = u32x4{0u, 0u, 0u, 0u};
+        if (lane == 0) __hip_atomic_store(ws.hdr + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     return;
   }
@@ -335,11 +378,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
 #pragma unroll
     for (int t = 0; t < kTPW; ++t) mref[a][t] = -INFINITY;
 
+  // Ordinary cached loads: one load instruction reads 32 bytes of each of
+  // the tile's 32 key rows, so four consecutive instructions share every
+  // 128-byte line; a streaming (non-temporal) hint lets the line go between
+  // them and costs a refetch each time.
   auto load_k = [&](const __bf16 *kb, int t) {
     const u32x4 *p = reinterpret_cast<const u32x4 *>(kb + koff[t]);
 #pragma unroll
     for (int st = 0; st < Frag<__bf16, D>::kSteps; ++st)
-      kf[t].v[st] = __builtin_nontemporal_load(p + 2 * st);
+      kf[t].v[st] = p[2 * st];
   };
 
 #pragma unroll
@@ -359,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
       // Q of this problem is read from LDS at each k-step of each tile (a
       // register copy would not fit), so the staging buffer is released
       // after the last tile's MFMAs.
-      lds_wait_ge(&sm.q_seq, it + 1, ws.status);
+      lds_wait_ge(&sm.q_seq, it + 1, ws);
       // Base of the next problem's K (the last problem reloads its own).
       if (it + 1 < P && ++gn == s.Hkv) { gn = 0; ++ln; }
       const __bf16 *kb_next = kprompt + ln * kstride_l + gn * D;
@@ -420,13 +467,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
       const float mo = __shfl_xor(m, 32, 64), zo = __shfl_xor(z, 32, 64);
       stats_merge(m, z, mo, zo);
       if (lane < 32) sm.red[it & 1][wave][r] = make_float2(m, z);
-      if (lane == 0) lds_inc(&sm.stats_cnt);
+      // The last wave to finish the problem posts the block's partials.
+      const int arrived = __builtin_amdgcn_readfirstlane(lane == 0 ? lds_inc(&sm.stats_cnt) : 0);
+      if (arrived == kCompute * (it + 1) - 1) {
+        if (lane < kRows) {
+          float M = -INFINITY, Z = 0.f;
+#pragma unroll
+          for (int w = 0; w < kCompute; ++w)
+            stats_merge(M, Z, sm.red[it & 1][w][lane].x, sm.red[it & 1][w][lane].y);
+          const uint32_t bits = __float_as_uint(lse_of(M, Z));
+          __hip_atomic_store(ws.slot + ((int64_t)it * n_cta + cta) * kRows + lane,
+                             bits ? bits : 0x80000000u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (lane == 0) lds_set(&sm.posted, it + 1);
+      }
     }
     if (it >= kLag) {
       // Fold problem it - kLag once its lse is staged: p = e * 2^(m_tile -
       // lse), max into run; then its LDS slot takes this problem's e (same
       // lane, in order).
-      lds_wait_ge(&sm.lse_ready[(it - kLag) & 1], it - kLag + 1, ws.status);
+      lds_wait_ge(&sm.lse_ready[(it - kLag) & 1], it - kLag + 1, ws);
       const float l2 = sm.lse[(it - kLag) & 1][r];
       if (lane == 0) lds_inc(&sm.lse_used);
 #pragma unroll
@@ -451,17 +512,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
     }
   }
 
-  // Max over the G heads of each step (lanes j*G .. j*G+G-1), then the mean
-  // over the steps (groups of lanes; padding rows hold 0).
+  // Max over the G heads of each step (lanes j*G .. j*G+G-1), then the sum
+  // over the steps (the other lane bits; padding rows hold 0): one butterfly
+  // over the five lane bits of the row, each level a max or a sum.
 #pragma unroll
-  for (int t = 0; t < kTPW; ++t) {
+  for (int lvl = 0; lvl < 5; ++lvl) {
+    const int off = 1 << lvl;
+    const bool head = off < s.G;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float v = run[t][i];
-      for (int off = 1; off < s.G; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-      for (int off = s.G; off < kRows; off <<= 1) v += __shfl_xor(v, off, 64);
-      run[t][i] = v;
-    }
+    for (int t = 0; t < kTPW; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float o = __shfl_xor(run[t][i], off, 64);
+        run[t][i] = head ? fmaxf(run[t][i], o) : run[t][i] + o;
+      }
   }
   if (r == 0) {
     float *out = imp + tb.tok_off[bb];
@@ -476,35 +540,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
   }
 }
 
-// Status word to 0 and every partial slot to the empty (NaN) pattern.
-__global__ void k_prepare(int *status, u32x4 *part, int n16) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += gridDim.x * blockDim.x)
-    part[i] = u32x4{kEmpty, kEmpty, kEmpty, kEmpty};
-}
-
 struct DeviceInfo {
   int cus = 0;
   int occ64 = 0, occ128 = 0;
-  bool coop = false;
 };
 
 const DeviceInfo &device_info() {
   static DeviceInfo info[64];
   static bool done[64];
+  static std::mutex mu;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return info[0];
+  std::lock_guard<std::mutex> lock(mu);
   if (!done[dev]) {
     DeviceInfo d;
-    int coop = 0;
     if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.occ64, k_stream<64>, kThreads, 0) !=
             hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.occ128, k_stream<128>, kThreads, 0) !=
             hipSuccess)
       d = DeviceInfo();
-    d.coop = coop != 0;
     info[dev] = d;
     done[dev] = true;
   }
@@ -572,59 +627,48 @@ bool make_plan(const SegTable &tok, int L, int n_cta, Plan &plan) {
 int stream_ctas(const AttnShape &s) {
   const DeviceInfo &d = device_info();
   const int occ = s.d == 128 ? d.occ128 : d.occ64;
-  if (!d.coop || occ < 1 || d.cus < 1) return 0;
+  if (occ < 1 || d.cus < 1) return 0;
   return std::min(d.cus, kMaxCtas);
 }
 
-size_t part_bytes(int P) { return align_up((size_t)P * kMaxCtas * kRows * sizeof(float)); }
-
 }  // namespace
 
-bool score_stream_supported(const AttnShape &s, int B, int total_tiles) {
-  (void)B;
-  (void)total_tiles;
+bool score_stream_supported(const AttnShape &s) {
   if (s.dtype != SP_DTYPE_BF16) return false;
   if (s.G & (s.G - 1)) return false;                 // head groups of 2^k lanes
   return true;
 }
 
-size_t score_stream_ws(const AttnShape &s, int B, int total_tiles) {
-  (void)B;
-  (void)total_tiles;
-  return kStatusBytes + part_bytes(s.n_layers * s.Hkv);
+size_t score_stream_slot_bytes(const AttnShape &s) {
+  if (!score_stream_supported(s)) return 0;
+  return align_up((size_t)s.n_layers * s.Hkv * kMaxCtas * kRows * sizeof(uint32_t));
 }
 
-hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, int total_tiles,
-                               const void *q, const void *k, float *imp, void *ws,
-                               size_t ws_bytes, hipStream_t st, bool *supported) {
+hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const void *q,
+                               const void *k, float *imp, void *ws, hipStream_t st,
+                               bool *supported) {
   *supported = false;
-  if (!score_stream_supported(s, tiles.B, total_tiles)) return hipSuccess;
+  if (!score_stream_supported(s)) return hipSuccess;
   const int n_cta = stream_ctas(s);
   if (n_cta < 1) return hipSuccess;
   static thread_local Plan plan;
   if (!make_plan(tiles, s.L, n_cta, plan)) return hipSuccess;
-  if (ws_bytes < score_stream_ws(s, tiles.B, total_tiles)) return hipSuccess;
   *supported = true;
-  const int P = s.n_layers * s.Hkv;
   StreamWs w;
-  w.status = reinterpret_cast<int *>(ws);
-  w.part = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + kStatusBytes);
+  w.hdr = reinterpret_cast<uint32_t *>(ws);
+  w.slot = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(ws) + kStatusBytes);
+  w.call_tag = reserve_tags(1);
   const int64_t total_keys = (int64_t)tiles.tok_off[tiles.B] + (int64_t)tiles.B * tiles.L;
   const __bf16 *qp = reinterpret_cast<const __bf16 *>(q);
   const __bf16 *kp = reinterpret_cast<const __bf16 *>(k);
-  const int n16 = (int)((size_t)P * n_cta * kRows * sizeof(float) / sizeof(u32x4));
   for (int li = 0; li < plan.n_launch; ++li) {
-    hipLaunchKernelGGL(k_prepare, dim3(std::min(256, (n16 + 255) / 256)), dim3(256), 0, st,
-                       w.status, reinterpret_cast<u32x4 *>(w.part), n16);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    StreamTable tb = plan.t[li];
-    int ncta = n_cta;
-    AttnShape sh = s;
-    void *args[] = {(void *)&sh, (void *)&tb, (void *)&total_keys, (void *)&ncta, (void *)&qp,
-                    (void *)&kp, (void *)&imp, (void *)&w};
-    const void *fn = s.d == 128 ? (const void *)k_stream<128> : (const void *)k_stream<64>;
-    e = hipLaunchCooperativeKernel(fn, dim3(plan.grid[li]), dim3(kThreads), args, 0, st);
+    if (s.d == 128)
+      hipLaunchKernelGGL(k_stream<128>, dim3(plan.grid[li]), dim3(kThreads), 0, st, s, plan.t[li],
+                         total_keys, n_cta, qp, kp, imp, w);
+    else
+      hipLaunchKernelGGL(k_stream<64>, dim3(plan.grid[li]), dim3(kThreads), 0, st, s, plan.t[li],
+                         total_keys, n_cta, qp, kp, imp, w);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -73,8 +73,9 @@ __global__ __launch_bounds__(64) void k_stats(AttnShape s, SegTable tiles, int64
 // order: lse2 = m + log2(z) (base-2 log-sum-exp of the row's logits).
 __global__ __launch_bounds__(256) void k_lse(SegTable tiles, int n_prob, int total_tiles,
                                              const float2 *__restrict__ part,
-                                             float *__restrict__ lse, int *__restrict__ status) {
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = 0;
+                                             float *__restrict__ lse, uint32_t *__restrict__ hdr,
+                                             uint32_t call_tag) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) hdr[1] = call_tag;   // no waits here
   __shared__ float2 sm[8][kRows];
   const int b = blockIdx.x, prob = blockIdx.y;
   const int row = threadIdx.x & 31, p = threadIdx.x >> 5;
@@ -133,17 +134,16 @@ __global__ __launch_bounds__(64) void k_score(AttnShape s, SegTable tiles, int64
 
 template <typename T, int D>
 hipError_t run(const AttnShape &s, const SegTable &tiles, int total_tiles, const void *q,
-               const void *k, float *imp, void *ws, hipStream_t st) {
+               const void *k, float *imp, uint32_t *hdr, void *region, hipStream_t st) {
   const int n_prob = s.n_layers * s.Hkv;
   const int64_t total_keys = tiles.tok_off[tiles.B] + (int64_t)tiles.B * tiles.L;
-  int *status = reinterpret_cast<int *>(ws);
-  float2 *part = reinterpret_cast<float2 *>(reinterpret_cast<char *>(ws) + kStatusBytes);
+  float2 *part = reinterpret_cast<float2 *>(region);
   float *lse = reinterpret_cast<float *>(reinterpret_cast<char *>(part) +
                                          align_up((size_t)n_prob * total_tiles * kRows * sizeof(float2)));
   hipLaunchKernelGGL((k_stats<T, D>), dim3(total_tiles, n_prob), dim3(64), 0, st, s, tiles,
                      total_keys, total_tiles, (const T *)q, (const T *)k, part);
   hipLaunchKernelGGL(k_lse, dim3(tiles.B, n_prob), dim3(256), 0, st, tiles, n_prob, total_tiles,
-                     part, lse, status);
+                     part, lse, hdr, reserve_tags(1));
   hipLaunchKernelGGL((k_score<T, D>), dim3(total_tiles), dim3(64), 0, st, s, tiles, total_keys,
                      (const T *)q, (const T *)k, lse, imp);
   return hipGetLastError();
@@ -151,21 +151,21 @@ hipError_t run(const AttnShape &s, const SegTable &tiles, int total_tiles, const
 
 }  // namespace
 
-size_t score_two_pass_ws(const AttnShape &s, int B, int total_tiles) {
+size_t score_two_pass_region_bytes(const AttnShape &s, int B, int total_tiles) {
   const size_t n_prob = (size_t)s.n_layers * s.Hkv;
-  return kStatusBytes + align_up(n_prob * total_tiles * kRows * sizeof(float2)) +
+  return align_up(n_prob * total_tiles * kRows * sizeof(float2)) +
          align_up((size_t)B * n_prob * kRows * sizeof(float));
 }
 
 hipError_t launch_score_two_pass(const AttnShape &s, const SegTable &tiles, int total_tiles,
-                                 const void *q, const void *k, float *imp, void *ws,
-                                 hipStream_t st) {
+                                 const void *q, const void *k, float *imp, uint32_t *hdr,
+                                 void *region, hipStream_t st) {
   if (s.dtype == SP_DTYPE_BF16) {
-    if (s.d == 128) return run<__bf16, 128>(s, tiles, total_tiles, q, k, imp, ws, st);
-    return run<__bf16, 64>(s, tiles, total_tiles, q, k, imp, ws, st);
+    if (s.d == 128) return run<__bf16, 128>(s, tiles, total_tiles, q, k, imp, hdr, region, st);
+    return run<__bf16, 64>(s, tiles, total_tiles, q, k, imp, hdr, region, st);
   }
-  if (s.d == 128) return run<float, 128>(s, tiles, total_tiles, q, k, imp, ws, st);
-  return run<float, 64>(s, tiles, total_tiles, q, k, imp, ws, st);
+  if (s.d == 128) return run<float, 128>(s, tiles, total_tiles, q, k, imp, hdr, region, st);
+  return run<float, 64>(s, tiles, total_tiles, q, k, imp, hdr, region, st);
 }
 
 }  // namespace sp

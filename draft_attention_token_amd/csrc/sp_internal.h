@@ -11,8 +11,9 @@ namespace sp {
 constexpr int kTile = 32;          // keys per MFMA tile (the 32-wide N of 32x32 MFMA)
 constexpr int kRows = 32;          // query rows per MFMA tile: (lookahead step, head in group)
 constexpr size_t kAlign = 256;
-// Both scoring kernels keep a 256-byte status header at the start of their
-// workspace: int 0 is 0 after a good run, 1 if a cross-block wait timed out.
+// The scoring workspace starts with a 256-byte header of two uint32 tags:
+// [1] is the tag of the latest call, [0] the tag of a call in which a
+// cross-block wait timed out. Every call gets fresh tags (reserve_tags).
 constexpr size_t kStatusBytes = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -45,17 +46,24 @@ struct AttnShape {
   int dtype;
 };
 
-// Launchers (return hipError_t of the launch).
-hipError_t launch_score_two_pass(const AttnShape &s, const SegTable &tiles, int total_tiles,
-                                 const void *q, const void *k, float *imp, void *ws,
-                                 hipStream_t st);
-size_t score_two_pass_ws(const AttnShape &s, int B, int total_tiles);
+// n consecutive nonzero tags, unique within the process (until 2^32 calls).
+uint32_t reserve_tags(int n);
 
-hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, int total_tiles,
-                               const void *q, const void *k, float *imp, void *ws,
-                               size_t ws_bytes, hipStream_t st, bool *supported);
-size_t score_stream_ws(const AttnShape &s, int B, int total_tiles);
-bool score_stream_supported(const AttnShape &s, int B, int total_tiles);
+// Launchers (return hipError_t of the launch).
+// Scoring workspace: header, then the single-pass kernel's slots (for shapes
+// it supports), then the two-pass kernel's region; one layout for every algo.
+hipError_t launch_score_two_pass(const AttnShape &s, const SegTable &tiles, int total_tiles,
+                                 const void *q, const void *k, float *imp, uint32_t *hdr,
+                                 void *region, hipStream_t st);
+size_t score_two_pass_region_bytes(const AttnShape &s, int B, int total_tiles);
+
+bool score_stream_supported(const AttnShape &s);
+size_t score_stream_slot_bytes(const AttnShape &s);
+// Sets *supported = false (and launches nothing) when the device or the
+// batch does not fit the kernel.
+hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const void *q,
+                               const void *k, float *imp, void *ws, hipStream_t st,
+                               bool *supported);
 
 struct PoolParams {
   int W, C, normalize, first_n, last_n;

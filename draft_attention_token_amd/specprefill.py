@@ -142,7 +142,9 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 def _ws(nbytes: int, device) -> torch.Tensor:
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    # Zero-filled: the scoring workspace must start out zeroed (calls leave it
+    # ready for the next call); the others do not care.
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 def attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype, scale=None,

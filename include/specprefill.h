@@ -33,8 +33,9 @@
  *     SP_ERR_UNSUPPORTED, a short workspace SP_ERR_WORKSPACE_TOO_SMALL; in each
  *     case nothing was launched. SP_ERR_DEVICE reports a failed launch.
  *     Faults during execution surface at the caller's next synchronisation.
- *   - Thread safety: no global mutable state; calls on different streams with
- *     different workspaces may run concurrently. The library prints nothing.
+ *   - Thread safety: calls on different streams with different workspaces
+ *     may run concurrently (the global state is an atomic call counter and a
+ *     per-device attribute cache). The library prints nothing.
  *   - Batches: B prompts, prompt b has N_b = token_offsets[b+1] -
  *     token_offsets[b] >= 1 tokens; per-token arrays are packed over the
  *     batch ([sum_b N_b]), per-chunk arrays likewise ([sum_b ceil(N_b / C)],
@@ -111,7 +112,7 @@ int sp_abi_version(void);
 const char *sp_status_string(int status);
 
 /* Workspace sizes (bytes, device memory) each call needs for this batch;
- * the result is written to *bytes. Alignment: 256 bytes. */
+ * the result is written to *bytes. Alignment: 256 bytes (at least 16). */
 sp_status sp_score_workspace_bytes(const sp_attn_desc *desc, const sp_batch *batch,
                                    size_t *bytes);
 sp_status sp_pool_workspace_bytes(const sp_pool_desc *desc, const sp_batch *batch,
@@ -132,18 +133,27 @@ sp_status sp_gather_workspace_bytes(const sp_batch *batch, int32_t chunk_size, s
  *       key rows start at token_offsets[b] + b * L: its N_b prompt keys, then
  *       its L lookahead keys.
  *   importance: [sum_b N_b] fp32 out.
- *   ws: device workspace of at least sp_score_workspace_bytes(). When the
- *       enqueued work has finished, the first int32 of ws is 0, or 1 if the
- *       single-pass kernel gave up waiting on another block (it waits at most
- *       about 2 s, then finishes so the device never hangs); importance is
- *       then not valid. sp_score_status() reads it.
+ *   ws: device workspace of at least sp_score_workspace_bytes() bytes. It
+ *       carries state from call to call: zero-fill all of it once before its
+ *       first use (e.g. hipMemsetAsync) and leave it alone between calls.
+ *       Each call leaves it ready for the next one with the same n_layers and
+ *       n_kv_heads, whatever the batch or algorithm. Calls that share a
+ *       workspace must not overlap in time.
+ *   The single-pass kernel runs one block per compute unit and needs all of
+ *   them resident together. Blocks exchange partial results through the
+ *   workspace, tagged with the call, so nothing needs clearing between calls.
+ *   A block waits at most about 2 s for another one, then finishes without
+ *   hanging the device and marks the call as failed (importance is then not
+ *   valid); sp_score_status() reports it. Only other work that keeps compute
+ *   units busy that long can cause this.
  */
 sp_status sp_score_attention(const sp_attn_desc *desc, const sp_batch *batch, const void *q,
                              const void *k, float *importance, void *ws, size_t ws_bytes,
                              void *stream);
 
-/* Copies the status word of a finished sp_score_attention call (first int32
- * of its workspace) to *status_host. Synchronises `stream`. */
+/* Whether the latest sp_score_attention call on this workspace completed:
+ * *status_host = 0 if so (or if there was none), 1 if a wait timed out and
+ * the importance it wrote is not valid. Synchronises `stream`. */
 sp_status sp_score_status(const void *ws, int32_t *status_host, void *stream);
 
 /*

@@ -144,6 +144,39 @@ def test_results_are_bitwise_deterministic():
     assert torch.equal(ids1[:n], b.kept_ids[:n])
 
 
+def test_score_workspace_reused_across_batches_and_algorithms():
+    """One zero-filled scoring workspace serves calls with different batches and
+    both kernels in any order: each call's cross-block slots are tagged with the
+    call, so what an earlier call left behind is never taken for a result."""
+    w = workloads.small_workload("n3212_bf16", lengths=(2500, 700), seed=33)
+    base = workloads.make_inputs(w)
+    other = workloads.make_inputs(w, lengths=(4100,))
+    big = max(sp.score_workspace_bytes(sp.attn_desc(w.n_layers, w.n_q_heads, w.n_kv_heads,
+                                                    w.head_dim, w.n_lookahead, w.dtype), sp.Batch(x.offsets))
+              for x in (base, other))
+    ws = torch.zeros(big, dtype=torch.uint8, device=DEV)
+
+    def score(inp, algo, ws_):
+        return sp.sp_score_attention(inp.q.to(DEV), inp.k.to(DEV), inp.offsets, w.n_layers,
+                                     w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_lookahead,
+                                     algo=algo, ws=ws_)
+
+    fresh = {}
+    for name, inp in (("base", base), ("other", other)):
+        for algo in ("stream", "two_pass"):
+            fresh[name, algo] = score(inp, algo, None).cpu()
+    order = [("base", "stream"), ("other", "stream"), ("base", "two_pass"), ("base", "stream"),
+             ("other", "two_pass"), ("other", "stream"), ("base", "stream")]
+    for name, algo in order:
+        got = score(base if name == "base" else other, algo, ws)
+        torch.cuda.synchronize()
+        assert sp.score_status(ws) == 0
+        assert torch.equal(got.cpu(), fresh[name, algo]), (name, algo)
+    ora = oracle.importance(base.offsets.numpy(), base.q, base.k, w.n_layers, w.n_q_heads,
+                            w.n_kv_heads, w.head_dim, w.n_lookahead, base.scale)
+    assert_scores_close(fresh["base", "stream"].numpy(), ora, "importance")
+
+
 def test_pool_select_gather_stages_on_oracle_importance():
     """Stages after scoring, fed the oracle's importance (rounded to fp32)."""
     w = workloads.small_workload("n3212_bf16", lengths=(3212, 100, 5000), seed=21)
