@@ -2,17 +2,20 @@
 
 One step = the whole path on one batch: sp_score_attention, sp_pool_chunk,
 sp_select_chunks and sp_gather_kept, from Q/K/token ids resident in HBM to
-the kept-token list. Prints one JSON line (rank 0) with whole-path throughput
-in prompt tokens per second, the scoring kernel's achieved HBM bandwidth
-against the 8 TB/s peak, and the CPU oracle timed on the host as a baseline.
+the kept-token list. Prints one JSON line with whole-path throughput in
+prompt tokens per second, the scoring kernel's achieved HBM bandwidth against
+the 8 TB/s peak, and the CPU oracle timed on the host as a baseline.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--algo auto|two_pass|stream]
+    python bench.py --copy-calibration   # plain device copies of known size (for counters)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -22,10 +25,53 @@ if ROOT not in sys.path:
 
 METRIC = "prompt tokens scored+selected/s at N=131072; % of HBM bandwidth roofline"
 HBM_PEAK_GBS = 8000.0
+# HBM traffic of the scoring kernel from hardware counters (two rocprofv3 --pmc
+# passes, FETCH_SIZE and WRITE_SIZE, scaled by a copy of known size). Valid
+# only for the kernel sources it was measured on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_stream_n128k_traffic.md")
+KERNEL_SOURCES = ("draft_attention_token_amd/csrc/score_stream.hip",
+                  "draft_attention_token_amd/csrc/score_common.h")
+COPY_BYTES = 1 << 30
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """Bytes per scoring launch from the committed counter summary, or None if
+    it is missing, covers another workload or older kernel sources."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = dict(re.findall(r"^- (\w+): (\S+)$", text, re.M))
+    if fields.get("workload") != workload or fields.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """Plain device-to-device copies of COPY_BYTES (reads and writes that many
+    bytes each): the reference for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 5}), flush=True)
 
 
 def score_algorithmic_bytes(inp) -> int:
@@ -63,7 +109,11 @@ def main():
     ap.add_argument("--mode", default=None, help="top_p or mass (default: the workload's)")
     ap.add_argument("--param", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode "
@@ -107,25 +157,30 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
     log(f"whole path {ms_step * 1e3:.1f} us/step (host clock {t_host / args.steps * 1e6:.1f} us)")
 
-    # Scoring stage alone, same stream, same inputs: per-launch average.
-    adesc = pipe.adesc
+    # Scoring stage alone, same stream, same inputs: one pair of events around
+    # each launch (the scoring call is one kernel launch per batch of up to
+    # 256 blocks' worth of prompts), averaged.
     import ctypes
     L = sp.lib()
     st = ctypes.c_void_p(stream.cuda_stream)
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record(stream)
-    for _ in range(args.steps):
+    adesc = pipe.adesc
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for a, b in ev:
+        a.record(stream)
         rc = L.sp_score_attention(ctypes.byref(adesc), pipe.batch.ref(), ctypes.c_void_p(q.data_ptr()),
                                   ctypes.c_void_p(k.data_ptr()),
                                   ctypes.c_void_p(pipe.importance.data_ptr()),
                                   ctypes.c_void_p(pipe.ws_score.data_ptr()), pipe.ws_score.numel(), st)
         assert rc == 0, sp.status_string(rc)
-    s1.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
-    ms_score = s0.elapsed_time(s1) / args.steps
+    assert pipe.score_status() == 0, "scoring kernel reported a timed-out wait"
+    ms_score = sum(a.elapsed_time(b) for a, b in ev) / args.steps
     alg_bytes = score_algorithmic_bytes(inp)
     achieved = alg_bytes / (ms_score * 1e-3) / 1e9
-    log(f"scoring {ms_score * 1e3:.1f} us -> {achieved:.0f} GB/s algorithmic")
+    log(f"scoring {ms_score * 1e3:.1f} us per launch -> {achieved:.0f} GB/s algorithmic")
+    traffic = measured_traffic(w.name)
 
     kept = int(pipe.kept_offsets[-1])
     result = {
@@ -147,8 +202,8 @@ def main():
                    "chunk": w.chunk_size, "normalize": w.normalize, "boost": w.boost,
                    "select": f"{mode} {param}", "score_algo": args.algo, "kept_tokens": kept},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "sp_score_attention", "launch_us": ms_score * 1e3,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "k_stream<128> (sp_score_attention)", "launch_us": ms_score * 1e3,
                      "algorithmic_bytes": alg_bytes},
     }
     if not args.no_cpu_baseline:
