@@ -56,6 +56,21 @@ SegTable make_table(const sp_batch *batch, int extra, int per, int L) {
   return t;
 }
 
+PoolTable make_pool_table(const sp_batch *batch, int C) {
+  const int TB = pool_block_tokens(C);
+  PoolTable t;
+  memset(&t, 0, sizeof(t));
+  t.B = batch->n_prompts;
+  for (int b = 0; b < t.B; ++b) {
+    const int64_t n = batch->token_offsets[b + 1] - batch->token_offsets[b];
+    t.blk_off[b + 1] = t.blk_off[b] + (int32_t)((n + TB - 1) / TB);
+    t.chunk_off[b + 1] = t.chunk_off[b] + (int32_t)((n + C - 1) / C);
+    t.tok_off[b] = (int32_t)batch->token_offsets[b];
+  }
+  t.tok_off[t.B] = (int32_t)batch->token_offsets[t.B];
+  return t;
+}
+
 sp_status check_attn(const sp_attn_desc *d, AttnShape *s) {
   if (!d) return SP_ERR_INVALID_ARGUMENT;
   if (d->n_layers < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->n_lookahead < 1)
@@ -199,8 +214,8 @@ sp_status sp_pool_workspace_bytes(const sp_pool_desc *desc, const sp_batch *batc
   sp_status st = check_pool(desc, &p);
   if (st != SP_OK) return st;
   if ((st = check_batch(batch, &total)) != SP_OK) return st;
-  const SegTable blocks = make_table(batch, 0, kPoolBlockTokens, 0);
-  *bytes = pool_ws(blocks.B, blocks.unit_off[blocks.B], total);
+  const PoolTable t = make_pool_table(batch, p.C);
+  *bytes = pool_ws(t.B, t.blk_off[t.B]);
   return SP_OK;
 }
 
@@ -215,13 +230,11 @@ sp_status sp_pool_chunk(const sp_pool_desc *desc, const sp_batch *batch, const f
   if ((st = check_batch(batch, &total)) != SP_OK) return st;
   if ((st = check_chunks(batch, p.C, &max_nc)) != SP_OK) return st;
   if (!importance || !chunk_scores) return SP_ERR_INVALID_ARGUMENT;
-  const SegTable blocks = make_table(batch, 0, kPoolBlockTokens, 0);
-  const SegTable chunks = make_table(batch, 0, p.C, 0);
-  const size_t need = pool_ws(blocks.B, blocks.unit_off[blocks.B], total);
+  const PoolTable t = make_pool_table(batch, p.C);
+  const size_t need = pool_ws(t.B, t.blk_off[t.B]);
   if (ws_bytes < need || !ws) return SP_ERR_WORKSPACE_TOO_SMALL;
-  return launched(launch_pool_chunk(p, blocks, blocks.unit_off[blocks.B], chunks,
-                                    chunks.unit_off[chunks.B], importance, token_scores,
-                                    chunk_scores, ws, reinterpret_cast<hipStream_t>(stream)));
+  return launched(launch_pool_chunk(p, t, importance, token_scores, chunk_scores, ws,
+                                    reinterpret_cast<hipStream_t>(stream)));
 }
 
 sp_status sp_select_workspace_bytes(const sp_batch *batch, int32_t chunk_size, size_t *bytes) {
@@ -231,15 +244,14 @@ sp_status sp_select_workspace_bytes(const sp_batch *batch, int32_t chunk_size, s
   sp_status st = check_batch(batch, &total);
   if (st != SP_OK) return st;
   if ((st = check_chunks(batch, chunk_size, &max_nc)) != SP_OK) return st;
-  *bytes = 0;
+  const SegTable chunks = make_table(batch, 0, chunk_size, 0);
+  *bytes = select_ws(chunks.B, chunks.unit_off[chunks.B]);
   return SP_OK;
 }
 
 sp_status sp_select_chunks(int32_t mode, double param, const sp_batch *batch, int32_t chunk_size,
                            const float *chunk_scores, uint8_t *keep, int32_t *n_kept_chunks,
                            void *ws, size_t ws_bytes, void *stream) {
-  (void)ws;
-  (void)ws_bytes;
   int64_t total;
   int max_nc;
   if (mode != SP_SELECT_TOP_P && mode != SP_SELECT_MASS) return SP_ERR_INVALID_ARGUMENT;
@@ -249,17 +261,22 @@ sp_status sp_select_chunks(int32_t mode, double param, const sp_batch *batch, in
   if ((st = check_chunks(batch, chunk_size, &max_nc)) != SP_OK) return st;
   if (!chunk_scores || !keep || !n_kept_chunks) return SP_ERR_INVALID_ARGUMENT;
   const SegTable chunks = make_table(batch, 0, chunk_size, 0);
-  SelectBudget kc;
-  memset(&kc, 0, sizeof(kc));
+  const size_t need = select_ws(chunks.B, chunks.unit_off[chunks.B]);
+  if (need && (!ws || ws_bytes < need)) return SP_ERR_WORKSPACE_TOO_SMALL;
+  SelectTable t;
+  memset(&t, 0, sizeof(t));
+  t.B = chunks.B;
   for (int b = 0; b < chunks.B; ++b) {
-    const int64_t nc = chunks.unit_off[b + 1] - chunks.unit_off[b];
+    const int nc = chunks.unit_off[b + 1] - chunks.unit_off[b];
+    t.chunk_off[b + 1] = chunks.unit_off[b + 1];
+    t.blk_off[b + 1] = t.blk_off[b] + select_rank_blocks(nc);
     int64_t v = (int64_t)ceil(param * (double)nc - 1e-9);
     if (v > nc) v = nc;
     if (v < 1) v = 1;
-    kc.kc[b] = (int32_t)v;
+    t.kc[b] = (int32_t)v;
   }
-  return launched(launch_select(mode, param, chunks, kc, max_nc, chunk_scores, keep,
-                                n_kept_chunks, reinterpret_cast<hipStream_t>(stream)));
+  return launched(launch_select(mode, param, t, chunk_scores, keep, n_kept_chunks, ws,
+                                reinterpret_cast<hipStream_t>(stream)));
 }
 
 sp_status sp_gather_workspace_bytes(const sp_batch *batch, int32_t chunk_size, size_t *bytes) {

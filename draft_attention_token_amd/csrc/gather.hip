@@ -17,35 +17,42 @@ namespace sp {
 namespace {
 
 constexpr int kScanThreads = 1024;
-constexpr int kWriteThreads = 256;
+constexpr int kWriteThreads = 1024;
 
 __global__ __launch_bounds__(kScanThreads) void k_gather_scan(SegTable chunks, int C,
                                                               const uint8_t *__restrict__ keep,
                                                               int32_t *__restrict__ chunk_out,
                                                               int32_t *__restrict__ counts) {
-  __shared__ int part[kScanThreads];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  constexpr int kEPT = SP_MAX_CHUNKS_PER_PROMPT / kScanThreads;   // chunks per thread
+  __shared__ int wave_tot[kScanThreads / 64];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c0 = chunks.unit_off[b], nc = chunks.unit_off[b + 1] - c0;
   const int N = chunks.tok_off[b + 1] - chunks.tok_off[b];
-  const int per = (nc + kScanThreads - 1) / kScanThreads;
-  const int a0 = min(nc, tid * per), a1 = min(nc, a0 + per);
-  int s = 0;
-  for (int c = a0; c < a1; ++c)
-    if (keep[c0 + c]) s += min(C, N - c * C);
-  part[tid] = s;
+  // Thread tid owns chunks tid*kEPT .. tid*kEPT + kEPT - 1 (index order).
+  int sz[kEPT];
+  int mine = 0;
+#pragma unroll
+  for (int e = 0; e < kEPT; ++e) {
+    const int c = tid * kEPT + e;
+    sz[e] = (c < nc && keep[c0 + c]) ? min(C, N - c * C) : 0;
+    mine += sz[e];
+  }
+  int incl = mine;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  int run = incl - mine;
+  for (int w = 0; w < wave; ++w) run += wave_tot[w];
+#pragma unroll
+  for (int e = 0; e < kEPT; ++e) {
+    const int c = tid * kEPT + e;
+    if (c < nc) chunk_out[c0 + c] = run;
+    run += sz[e];
   }
-  int run = tid > 0 ? part[tid - 1] : 0;
-  for (int c = a0; c < a1; ++c) {
-    chunk_out[c0 + c] = run;
-    if (keep[c0 + c]) run += min(C, N - c * C);
-  }
-  if (tid == kScanThreads - 1) counts[b] = part[kScanThreads - 1] + (keep[c0] ? 0 : 1);
+  if (tid == kScanThreads - 1) counts[b] = run + (keep[c0] ? 0 : 1);
 }
 
 __global__ __launch_bounds__(kWriteThreads) void k_gather_write(

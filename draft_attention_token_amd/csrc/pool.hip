@@ -8,12 +8,18 @@
 // Improvements item 2 (first 64 tokens x1.5, last 128 x1.3), and Chunk
 // Selection (a chunk's score is the mean over the tokens it holds).
 //
-// k_pool: one block per 1024-token block of a prompt; the block stages its
-//   tokens plus a halo of (W-1)/2 on each side in LDS (clamped to the
-//   prompt), writes the pooled values and the block's min and max.
-// k_minmax: one block per prompt reduces its blocks' minima and maxima in a
-//   fixed order.
-// k_chunk: one thread per chunk normalises, boosts and averages its tokens.
+// Work is split into blocks of whole chunks, TB = C * floor(1024 / C) <= 1024
+// tokens of one prompt. A block stages its importance values plus a halo of
+// (W-1)/2 on each side (clamped to the prompt) in LDS and pools them there.
+// k_pool_stats: each block's min and max of the pooled values (only when
+//   normalising: the scale needs the prompt's min and max).
+// k_pool_minmax: per prompt, when a prompt has too many blocks for every
+//   block to reduce them itself.
+// k_pool_finish: pools again (cheaper than a round trip of the pooled values
+//   through memory), normalises, boosts, writes the token scores and takes
+//   the chunk means from LDS.
+#include <algorithm>
+
 #include "sp_internal.h"
 
 namespace sp {
@@ -21,117 +27,175 @@ namespace {
 
 constexpr int kPoolThreads = 256;
 constexpr int kMaxHalo = (kMaxPoolWindow - 1) / 2;
+constexpr int kMaxTB = 1024;
 
-__device__ __forceinline__ void block_minmax(float &mn, float &mx, float (*sh)[kPoolThreads]) {
-  const int t = threadIdx.x;
-  sh[0][t] = mn;
-  sh[1][t] = mx;
-  __syncthreads();
-  for (int w = kPoolThreads / 2; w > 0; w >>= 1) {
-    if (t < w) {
-      sh[0][t] = fminf(sh[0][t], sh[0][t + w]);
-      sh[1][t] = fmaxf(sh[1][t], sh[1][t + w]);
-    }
-    __syncthreads();
+struct BlockSpan {
+  int b;           // prompt
+  int64_t base;    // global offset of the prompt's token 0
+  int N;           // prompt tokens
+  int t0, t1;      // the block's tokens [t0, t1) within the prompt
+};
+
+__device__ __forceinline__ BlockSpan block_span(const PoolTable &pt, int blk, int TB) {
+  int lo = 0, hi = pt.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pt.blk_off[mid] <= blk) lo = mid; else hi = mid - 1;
   }
-  mn = sh[0][0];
-  mx = sh[1][0];
+  BlockSpan s;
+  s.b = lo;
+  s.base = pt.tok_off[s.b];
+  s.N = pt.tok_off[s.b + 1] - pt.tok_off[s.b];
+  s.t0 = (blk - pt.blk_off[s.b]) * TB;
+  s.t1 = min(s.N, s.t0 + TB);
+  return s;
 }
 
-__global__ __launch_bounds__(kPoolThreads) void k_pool(PoolParams p, SegTable blocks,
-                                                       const float *__restrict__ imp,
-                                                       float *__restrict__ pooled,
-                                                       float2 *__restrict__ block_mm) {
-  __shared__ float buf[kPoolBlockTokens + 2 * kMaxHalo];
-  __shared__ float red[2][kPoolThreads];
-  const int blk = blockIdx.x;
-  const int b = seg_of(blocks, blk);
-  const int64_t base = blocks.tok_off[b];
-  const int64_t N = blocks.tok_off[b + 1] - base;
-  const int64_t t0 = (int64_t)(blk - blocks.unit_off[b]) * kPoolBlockTokens;
-  const int64_t t1 = min(N, t0 + kPoolBlockTokens);
+// Pooled values of the block's tokens into out[0 .. t1 - t0) (LDS), from the
+// halo-extended importance staged in buf.
+__device__ __forceinline__ void pool_block(const PoolParams &p, const BlockSpan &s,
+                                           const float *__restrict__ imp, float *buf, float *out) {
   const int r = (p.W - 1) / 2;
-  const int64_t lo = max((int64_t)0, t0 - r), hi = min(N, t1 + r);
-  for (int64_t i = threadIdx.x; i < hi - lo; i += kPoolThreads) buf[i] = imp[base + lo + i];
+  const int lo = max(0, s.t0 - r), hi = min(s.N, s.t1 + r);
+  for (int i = threadIdx.x; i < hi - lo; i += kPoolThreads) buf[i] = imp[s.base + lo + i];
   __syncthreads();
-  float mn = INFINITY, mx = -INFINITY;
-  for (int64_t t = t0 + threadIdx.x; t < t1; t += kPoolThreads) {
-    const int64_t a = max((int64_t)0, t - r), e = min(N - 1, t + r);
-    float s = 0.f;
-    for (int64_t i = a; i <= e; ++i) s += buf[i - lo];
-    const float v = s / (float)(e - a + 1);
-    pooled[base + t] = v;
-    mn = fminf(mn, v);
-    mx = fmaxf(mx, v);
+  for (int t = s.t0 + threadIdx.x; t < s.t1; t += kPoolThreads) {
+    const int a = max(0, t - r), e = min(s.N - 1, t + r);
+    float sum = 0.f;
+    for (int i = a; i <= e; ++i) sum += buf[i - lo];
+    out[t - s.t0] = sum / (float)(e - a + 1);
   }
-  block_minmax(mn, mx, red);
-  if (threadIdx.x == 0) block_mm[blk] = make_float2(mn, mx);
+  __syncthreads();
 }
 
-__global__ __launch_bounds__(kPoolThreads) void k_minmax(SegTable blocks,
-                                                         const float2 *__restrict__ block_mm,
-                                                         float2 *__restrict__ prompt_mm) {
-  __shared__ float red[2][kPoolThreads];
+__device__ __forceinline__ float2 block_minmax(float mn, float mx, float2 *red) {
+  for (int off = 32; off > 0; off >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, off, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(mn, mx);
+  __syncthreads();
+  float2 v = red[0];
+  for (int w = 1; w < kPoolThreads / 64; ++w) {
+    v.x = fminf(v.x, red[w].x);
+    v.y = fmaxf(v.y, red[w].y);
+  }
+  __syncthreads();
+  return v;
+}
+
+__global__ __launch_bounds__(kPoolThreads) void k_pool_stats(PoolParams p, PoolTable blocks, int TB,
+                                                             const float *__restrict__ imp,
+                                                             float2 *__restrict__ block_mm) {
+  __shared__ float buf[kMaxTB + 2 * kMaxHalo];
+  __shared__ float pooled[kMaxTB];
+  __shared__ float2 red[kPoolThreads / 64];
+  const BlockSpan s = block_span(blocks, blockIdx.x, TB);
+  pool_block(p, s, imp, buf, pooled);
+  float mn = INFINITY, mx = -INFINITY;
+  for (int i = threadIdx.x; i < s.t1 - s.t0; i += kPoolThreads) {
+    mn = fminf(mn, pooled[i]);
+    mx = fmaxf(mx, pooled[i]);
+  }
+  const float2 v = block_minmax(mn, mx, red);
+  if (threadIdx.x == 0) block_mm[blockIdx.x] = v;
+}
+
+__global__ __launch_bounds__(kPoolThreads) void k_pool_minmax(PoolTable blocks,
+                                                              const float2 *__restrict__ block_mm,
+                                                              float2 *__restrict__ prompt_mm) {
+  __shared__ float2 red[kPoolThreads / 64];
   const int b = blockIdx.x;
   float mn = INFINITY, mx = -INFINITY;
-  for (int i = blocks.unit_off[b] + threadIdx.x; i < blocks.unit_off[b + 1]; i += kPoolThreads) {
+  for (int i = blocks.blk_off[b] + threadIdx.x; i < blocks.blk_off[b + 1]; i += kPoolThreads) {
     const float2 v = block_mm[i];
     mn = fminf(mn, v.x);
     mx = fmaxf(mx, v.y);
   }
-  block_minmax(mn, mx, red);
-  if (threadIdx.x == 0) prompt_mm[b] = make_float2(mn, mx);
+  const float2 v = block_minmax(mn, mx, red);
+  if (threadIdx.x == 0) prompt_mm[b] = v;
 }
 
-__global__ __launch_bounds__(kPoolThreads) void k_chunk(PoolParams p, SegTable chunks,
-                                                        const float *pooled,
-                                                        const float2 *__restrict__ prompt_mm,
-                                                        float *token_scores,
-                                                        float *__restrict__ chunk_scores) {
-  const int c = blockIdx.x * kPoolThreads + threadIdx.x;
-  if (c >= chunks.unit_off[chunks.B]) return;
-  const int b = seg_of(chunks, c);
-  const int64_t base = chunks.tok_off[b];
-  const int64_t N = chunks.tok_off[b + 1] - base;
-  const float2 mm = prompt_mm[b];
-  const float mn = mm.x, range = mm.y - mm.x;
-  const bool flat = range <= 1e-6f * mm.y;
-  const int64_t s0 = (int64_t)(c - chunks.unit_off[b]) * p.C, s1 = min(N, s0 + p.C);
-  float sum = 0.f;
-  for (int64_t t = s0; t < s1; ++t) {
-    float x = pooled[base + t];
+// prompt_mm: per-prompt (min, max), or null to reduce the prompt's block
+// entries here (few blocks per prompt).
+__global__ __launch_bounds__(kPoolThreads) void k_pool_finish(
+    PoolParams p, PoolTable blocks, int TB, const float *__restrict__ imp,
+    const float2 *__restrict__ block_mm, const float2 *__restrict__ prompt_mm,
+    float *__restrict__ token_scores, float *__restrict__ chunk_scores) {
+  __shared__ float buf[kMaxTB + 2 * kMaxHalo];
+  __shared__ float xs[kMaxTB];
+  __shared__ float2 red[kPoolThreads / 64];
+  const BlockSpan s = block_span(blocks, blockIdx.x, TB);
+  float mn = 0.f, range = 1.f;
+  bool flat = false;
+  if (p.normalize) {
+    float2 v;
+    if (prompt_mm) {
+      v = prompt_mm[s.b];
+    } else {
+      float lo = INFINITY, hi = -INFINITY;
+      for (int i = blocks.blk_off[s.b] + threadIdx.x; i < blocks.blk_off[s.b + 1];
+           i += kPoolThreads) {
+        const float2 w = block_mm[i];
+        lo = fminf(lo, w.x);
+        hi = fmaxf(hi, w.y);
+      }
+      v = block_minmax(lo, hi, red);
+    }
+    mn = v.x;
+    range = v.y - v.x;
+    flat = range <= 1e-6f * v.y;   // no signal: every score becomes 1
+  }
+  pool_block(p, s, imp, buf, xs);
+  for (int t = s.t0 + threadIdx.x; t < s.t1; t += kPoolThreads) {
+    float x = xs[t - s.t0];
     if (p.normalize) x = flat ? 1.f : (x - mn) / range;
     if (t < p.first_n) x *= p.first_mult;
-    if (t >= N - p.last_n) x *= p.last_mult;
-    if (token_scores) token_scores[base + t] = x;
-    sum += x;
+    if (t >= s.N - p.last_n) x *= p.last_mult;
+    xs[t - s.t0] = x;
+    if (token_scores) token_scores[s.base + t] = x;
   }
-  chunk_scores[c] = sum / (float)(s1 - s0);
+  __syncthreads();
+  // The block's chunks: it starts on a chunk boundary of its prompt.
+  const int nchunk = (s.t1 - s.t0 + p.C - 1) / p.C;
+  for (int c = threadIdx.x; c < nchunk; c += kPoolThreads) {
+    const int a = c * p.C, e = min(s.t1 - s.t0, a + p.C);
+    float sum = 0.f;
+    for (int i = a; i < e; ++i) sum += xs[i];
+    const int pc = (s.t0 + a) / p.C;   // chunk index within the prompt
+    chunk_scores[blocks.chunk_off[s.b] + pc] = sum / (float)(e - a);
+  }
 }
 
 }  // namespace
 
-size_t pool_ws(int B, int total_blocks, int64_t total_tokens) {
-  return align_up((size_t)total_blocks * sizeof(float2)) + align_up((size_t)B * sizeof(float2)) +
-         align_up((size_t)total_tokens * sizeof(float));
+int pool_block_tokens(int C) { return C * (kMaxTB / C); }
+
+size_t pool_ws(int B, int total_blocks) {
+  return align_up((size_t)total_blocks * sizeof(float2)) + align_up((size_t)B * sizeof(float2));
 }
 
-hipError_t launch_pool_chunk(const PoolParams &p, const SegTable &blocks, int total_blocks,
-                             const SegTable &chunks, int total_chunks, const float *imp,
+hipError_t launch_pool_chunk(const PoolParams &p, const PoolTable &blocks, const float *imp,
                              float *token_scores, float *chunk_scores, void *ws, hipStream_t st) {
-  char *w = reinterpret_cast<char *>(ws);
-  float2 *block_mm = reinterpret_cast<float2 *>(w);
-  w += align_up((size_t)total_blocks * sizeof(float2));
-  float2 *prompt_mm = reinterpret_cast<float2 *>(w);
-  w += align_up((size_t)blocks.B * sizeof(float2));
-  float *pooled = token_scores ? token_scores : reinterpret_cast<float *>(w);
-  hipLaunchKernelGGL(k_pool, dim3(total_blocks), dim3(kPoolThreads), 0, st, p, blocks, imp, pooled,
-                     block_mm);
-  hipLaunchKernelGGL(k_minmax, dim3(blocks.B), dim3(kPoolThreads), 0, st, blocks, block_mm,
-                     prompt_mm);
-  hipLaunchKernelGGL(k_chunk, dim3((total_chunks + kPoolThreads - 1) / kPoolThreads),
-                     dim3(kPoolThreads), 0, st, p, chunks, pooled, prompt_mm, token_scores,
-                     chunk_scores);
+  const int TB = pool_block_tokens(p.C);
+  const int total_blocks = blocks.blk_off[blocks.B];
+  float2 *block_mm = reinterpret_cast<float2 *>(ws);
+  float2 *prompt_mm = reinterpret_cast<float2 *>(reinterpret_cast<char *>(ws) +
+                                                 align_up((size_t)total_blocks * sizeof(float2)));
+  const float2 *mm_arg = nullptr;
+  if (p.normalize) {
+    hipLaunchKernelGGL(k_pool_stats, dim3(total_blocks), dim3(kPoolThreads), 0, st, p, blocks, TB,
+                       imp, block_mm);
+    int most = 0;
+    for (int b = 0; b < blocks.B; ++b) most = std::max(most, blocks.blk_off[b + 1] - blocks.blk_off[b]);
+    if (most > kPoolThreads) {
+      hipLaunchKernelGGL(k_pool_minmax, dim3(blocks.B), dim3(kPoolThreads), 0, st, blocks,
+                         block_mm, prompt_mm);
+      mm_arg = prompt_mm;
+    }
+  }
+  hipLaunchKernelGGL(k_pool_finish, dim3(total_blocks), dim3(kPoolThreads), 0, st, p, blocks, TB,
+                     imp, block_mm, mm_arg, token_scores, chunk_scores);
   return hipGetLastError();
 }
 

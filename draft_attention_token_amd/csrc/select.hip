@@ -6,120 +6,215 @@
 // (sort chunks by score and keep them from the highest down until the kept
 // share of the total attention mass reaches the threshold).
 //
-// One 1024-thread block per prompt. Each chunk gets a 64-bit key
-//   (~ordered(score) << 32) | (index + 1)
-// so an ascending sort visits chunks by score, highest first, and equal
-// scores by lower index; the final chunk gets key 0 and comes first (it is
-// always kept). A bitonic sort of the keys runs in LDS; top-p then keeps the
-// first kc sorted chunks, and mass mode finds the first sorted position whose
-// fp64 prefix sum reaches mass * total (fixed-order block scan).
-#include <limits.h>
-
+// The final chunk is always kept. The other chunks are visited by score,
+// highest first, equal scores by lower index: top-p keeps the first kc - 1
+// of them; mass mode keeps a chunk while the kept sum before it (final chunk
+// included) is below mass * total, so the chunk that reaches the threshold
+// is kept too.
+//
+// No sort. A chunk's place in that order is the number of chunks ahead of
+// it, and the mass walk only needs the sum of their scores, so both modes
+// reduce to: for every chunk, count and sum the chunks that precede it.
+// k_select computes these all-pairs counts and sums, 16 chunks per block
+// with 64 lane groups splitting the other chunks, and decides each chunk
+// from them; the block holding the last kept chunk writes the count. Scores
+// enter as 64-bit fixed point with a scale set by the prompt's largest score
+// (values below 2^48, so at most 2^14 of them sum below 2^62): every sum is
+// exact integer arithmetic, independent of the order of the additions, and
+// the sum ahead of a chunk grows along the order. The order compares the
+// top 32 bits of the fixed-point value (two scores closer than 2^-32 of the
+// largest tie and go by index; both then sit at the selection boundary).
 #include "sp_internal.h"
 
 namespace sp {
 namespace {
 
-constexpr int kSelThreads = 1024;
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kRankTile = 16;                   // chunks per block
+constexpr int kGroups = kThreads / kRankTile;   // lane groups splitting the other chunks (64)
+constexpr int kStage = 4096;                    // chunks staged in LDS at a time
+constexpr int kPerThread = SP_MAX_CHUNKS_PER_PROMPT / kThreads;   // scores held per thread
 
-__device__ __forceinline__ uint64_t chunk_key(float v, int i) {
-  const unsigned u = __float_as_uint(v);
-  const unsigned ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // ascending in v
-  return ((uint64_t)(~ord) << 32) | (uint64_t)(unsigned)(i + 1);
+__device__ __forceinline__ int fixed_shift(float mx) {
+  int e = 0;
+  if (mx > 0.f) frexpf(mx, &e);   // mx < 2^e
+  return 48 - e;
+}
+// floor(v * 2^shift) for finite v >= 0 with v * 2^shift < 2^63, from the
+// float's bits (exact; no floating-point rounding).
+__device__ __forceinline__ long long to_fixed(float v, int shift) {
+  const uint32_t u = __float_as_uint(v);
+  const int e = (int)((u >> 23) & 0xffu);
+  const unsigned long long m = (u & 0x7fffffu) | (e ? 0x800000u : 0u);
+  const int sh = (e ? e : 1) - 150 + shift;   // v = m * 2^((e ? e : 1) - 150)
+  if (sh >= 0) return (long long)(m << sh);
+  return sh <= -64 ? 0ll : (long long)(m >> (-sh));
+}
+// Ascending key = descending score.
+__device__ __forceinline__ uint32_t order_key(long long fx) {
+  return 0xffffffffu - (uint32_t)((unsigned long long)fx >> 16);
 }
 
-__device__ __forceinline__ float key_score(uint64_t key) {
-  const unsigned ord = ~(unsigned)(key >> 32);
-  const unsigned u = (ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord;
-  return __uint_as_float(u);
-}
-
-__global__ __launch_bounds__(kSelThreads) void k_select(int mode, double param, SegTable chunks,
-                                                        SelectBudget budget, int p2,
-                                                        const float *__restrict__ cs,
-                                                        uint8_t *__restrict__ keep,
-                                                        int32_t *__restrict__ n_kept) {
-  extern __shared__ uint64_t keys[];
-  __shared__ double part[kSelThreads];
-  __shared__ int found;
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int c0 = chunks.unit_off[b], nc = chunks.unit_off[b + 1] - c0;
-  for (int i = tid; i < p2; i += kSelThreads) {
-    uint64_t key;
-    if (i >= nc) key = ~0ull;
-    else if (i == nc - 1) key = 0ull;
-    else key = chunk_key(cs[c0 + i], i);
-    keys[i] = key;
-  }
-  if (tid == 0) found = INT_MAX;
+template <typename T, typename Op>
+__device__ __forceinline__ T block_reduce(T v, T *red, Op op) {
+  for (int off = 32; off > 0; off >>= 1) v = op(v, __shfl_xor(v, off, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  for (int k = 2; k <= p2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < p2; i += kSelThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint64_t a = keys[i], c = keys[ixj];
-          const bool up = (i & k) == 0;
-          if ((a > c) == up) {
-            keys[i] = c;
-            keys[ixj] = a;
-          }
-        }
-      }
-      __syncthreads();
-    }
+  v = red[0];
+  for (int w = 1; w < kWaves; ++w) v = op(v, red[w]);
+  __syncthreads();
+  return v;
+}
+
+__device__ __forceinline__ int table_prompt(const int32_t *off, int B, int u) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= u) lo = mid; else hi = mid - 1;
   }
-  const double final_score = (double)cs[c0 + nc - 1];
-  int cnt;
-  if (mode == SP_SELECT_TOP_P) {
-    cnt = budget.kc[b];
+  return lo;
+}
+
+template <bool kMass>
+__global__ __launch_bounds__(kThreads) void k_select(SelectTable t, double param,
+                                                     const float *__restrict__ cs,
+                                                     uint8_t *__restrict__ keep,
+                                                     int32_t *__restrict__ n_kept) {
+  __shared__ __align__(16) uint32_t skey[kStage];
+  __shared__ __align__(16) long long sfx[kMass ? kStage : 2];
+  __shared__ uint32_t rc[kWaves][kRankTile];
+  __shared__ long long rs[kWaves][kRankTile];
+  __shared__ float redf[kWaves];
+  __shared__ long long redl[kWaves];
+  const int b = table_prompt(t.blk_off, t.B, blockIdx.x);
+  const int tile = blockIdx.x - t.blk_off[b];
+  const int c0 = t.chunk_off[b], nc = t.chunk_off[b + 1] - c0, last = nc - 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // The prompt's scores, read once: chunk tid + kThreads * e in sc[e].
+  float sc[kPerThread];
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int j = tid + kThreads * e;
+    sc[e] = j < nc ? cs[c0 + j] : 0.f;
+  }
+  // The prompt's scale, and for mass mode the fixed-point sum the chunks
+  // ahead of a kept one must stay below: ceil(mass * total) - final.
+  float mx = 0.f;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) mx = fmaxf(mx, sc[e]);
+  mx = block_reduce(mx, redf, [](float a, float c) { return fmaxf(a, c); });
+  const int shift = fixed_shift(mx);
+  long long need;
+  if (kMass) {
+    long long tot = 0;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) tot += to_fixed(sc[e], shift);
+    tot = block_reduce(tot, redl, [](long long a, long long c) { return a + c; });
+    need = (long long)ceil(param * (double)tot) - to_fixed(cs[c0 + last], shift);
   } else {
-    const int per = (nc + kSelThreads - 1) / kSelThreads;
-    const int a0 = min(nc, tid * per), a1 = min(nc, a0 + per);
-    double s = 0.0;
-    for (int pos = a0; pos < a1; ++pos) s += pos == 0 ? final_score : (double)key_score(keys[pos]);
-    part[tid] = s;
+    need = t.kc[b] - 1;   // chunks ahead of a kept one
+  }
+
+  const int i = tile * kRankTile + (lane & (kRankTile - 1));
+  const int grp = wave * (64 / kRankTile) + (lane / kRankTile);
+  const bool mine = i < last;
+  const long long fxi = mine ? to_fixed(cs[c0 + i], shift) : 0ll;
+  const uint32_t ki = order_key(fxi);
+  uint32_t n = 0;
+  long long sum = 0;
+  // Every chunk except the final one, in LDS-sized stages; lane group g
+  // takes the g-th of kGroups equal slices of each stage (multiples of 4).
+  for (int j0 = 0; j0 < last; j0 += kStage) {
+    const int len = min(kStage, last - j0);
     __syncthreads();
-    for (int off = 1; off < kSelThreads; off <<= 1) {
-      const double v = tid >= off ? part[tid - off] : 0.0;
-      __syncthreads();
-      part[tid] += v;
-      __syncthreads();
+    // Stage j0 / kThreads .. + kStage / kThreads of the register copy.
+#pragma unroll
+    for (int e = 0; e < kStage / kThreads; ++e) {
+      const int j = tid + kThreads * e;              // within the stage
+      const int ej = j0 / kThreads + e;              // register slot
+      float v = 0.f;
+#pragma unroll
+      for (int r = 0; r < kPerThread; ++r) v = r == ej ? sc[r] : v;
+      const bool in = j < len;
+      const long long fx = in ? to_fixed(v, shift) : 0ll;
+      skey[j] = in ? order_key(fx) : 0xffffffffu;   // padding is never ahead
+      if (kMass) sfx[j] = fx;
     }
-    const double target = param * part[kSelThreads - 1];
-    double cum = tid > 0 ? part[tid - 1] : 0.0;
-    for (int pos = a0; pos < a1; ++pos) {
-      cum += pos == 0 ? final_score : (double)key_score(keys[pos]);
-      if (cum >= target) {
-        atomicMin(&found, pos);
-        break;
+    __syncthreads();
+    const int per = (len + 4 * kGroups - 1) / (4 * kGroups) * 4;
+    const int a = grp * per;
+    for (int j = a; j < a + per; j += 4) {
+      const uint4 k4 = *reinterpret_cast<const uint4 *>(&skey[j]);
+      const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
+      long long f[4] = {0, 0, 0, 0};
+      if (kMass) {
+        const longlong2 f01 = *reinterpret_cast<const longlong2 *>(&sfx[j]);
+        const longlong2 f23 = *reinterpret_cast<const longlong2 *>(&sfx[j + 2]);
+        f[0] = f01.x; f[1] = f01.y; f[2] = f23.x; f[3] = f23.y;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool ahead = kk[u] < ki || (kk[u] == ki && j0 + j + u < i);
+        n += ahead ? 1u : 0u;
+        if (kMass) sum += ahead ? f[u] : 0ll;
       }
     }
-    __syncthreads();
-    cnt = found == INT_MAX ? nc : found + 1;
   }
-  for (int i = tid; i < nc; i += kSelThreads) keep[c0 + i] = 0;
+  // Sum over the lane groups: the 4 of a wave by shuffles, the waves in LDS.
+  for (int off = kRankTile; off < 64; off <<= 1) {
+    n += __shfl_xor(n, off, 64);
+    if (kMass) sum += __shfl_xor(sum, off, 64);
+  }
+  if (lane < kRankTile) {
+    rc[wave][lane] = n;
+    rs[wave][lane] = sum;
+  }
   __syncthreads();
-  for (int pos = tid; pos < cnt; pos += kSelThreads) {
-    const int idx = pos == 0 ? nc - 1 : (int)(unsigned)(keys[pos] & 0xffffffffu) - 1;
-    keep[c0 + idx] = 1;
+  if (wave != 0 || lane >= kRankTile) return;
+  n = 0;
+  sum = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    n += rc[w][lane];
+    sum += rs[w][lane];
   }
-  if (tid == 0) n_kept[b] = cnt;
+  if (i > last) return;
+  bool k;
+  if (i == last) {
+    k = true;
+  } else if (kMass) {
+    k = sum < need;
+    // The last kept chunk (the next one in the order, with sum + fxi ahead
+    // of it, is not kept) writes the count; with none kept, the first one.
+    if (k && (sum + fxi >= need || (int)n == last - 1)) n_kept[b] = (int)n + 2;
+    if (!k && n == 0) n_kept[b] = 1;
+  } else {
+    k = (long long)n < need;
+  }
+  keep[c0 + i] = k ? 1 : 0;
+  if (tile == 0 && lane == 0 && (!kMass || last == 0)) n_kept[b] = kMass ? 1 : t.kc[b];
 }
 
 }  // namespace
 
-hipError_t launch_select(int mode, double param, const SegTable &chunks, const SelectBudget &kc,
-                         int max_nc, const float *chunk_scores, uint8_t *keep, int32_t *n_kept,
-                         hipStream_t st) {
-  int p2 = 1;
-  while (p2 < max_nc) p2 <<= 1;
-  const size_t lds = (size_t)p2 * sizeof(uint64_t);
-  hipError_t e = hipFuncSetAttribute((const void *)k_select,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_select, dim3(chunks.B), dim3(kSelThreads), lds, st, mode, param, chunks, kc,
-                     p2, chunk_scores, keep, n_kept);
+size_t select_ws(int B, int total_chunks) {
+  (void)B;
+  (void)total_chunks;
+  return 0;
+}
+
+int select_rank_blocks(int nc) { return (nc + kRankTile - 1) / kRankTile; }
+
+hipError_t launch_select(int mode, double param, const SelectTable &t, const float *chunk_scores,
+                         uint8_t *keep, int32_t *n_kept, void *ws, hipStream_t st) {
+  (void)ws;
+  if (mode == SP_SELECT_MASS)
+    hipLaunchKernelGGL(k_select<true>, dim3(t.blk_off[t.B]), dim3(kThreads), 0, st, t, param,
+                       chunk_scores, keep, n_kept);
+  else
+    hipLaunchKernelGGL(k_select<false>, dim3(t.blk_off[t.B]), dim3(kThreads), 0, st, t, param,
+                       chunk_scores, keep, n_kept);
   return hipGetLastError();
 }
 

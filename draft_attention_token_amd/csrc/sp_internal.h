@@ -69,20 +69,31 @@ struct PoolParams {
   int W, C, normalize, first_n, last_n;
   float first_mult, last_mult;
 };
-hipError_t launch_pool_chunk(const PoolParams &p, const SegTable &blocks, int total_blocks,
-                             const SegTable &chunks, int total_chunks, const float *imp,
-                             float *token_scores, float *chunk_scores, void *ws, hipStream_t st);
-constexpr int kPoolBlockTokens = 1024;
-constexpr int kMaxPoolWindow = 129;
-size_t pool_ws(int B, int total_blocks, int64_t total_tokens);
-
-// Per-prompt top-p chunk budgets (host-computed), passed by value.
-struct SelectBudget {
-  int32_t kc[SP_MAX_PROMPTS];
+// Pooling works on blocks of whole chunks of one prompt,
+// pool_block_tokens(C) = C * floor(1024 / C) tokens each.
+struct PoolTable {
+  int32_t B;
+  int32_t blk_off[SP_MAX_PROMPTS + 1];     // block prefix per prompt
+  int32_t chunk_off[SP_MAX_PROMPTS + 1];   // chunk prefix per prompt
+  int32_t tok_off[SP_MAX_PROMPTS + 1];     // token offsets
 };
-hipError_t launch_select(int mode, double param, const SegTable &chunks, const SelectBudget &kc,
-                         int max_nc, const float *chunk_scores, uint8_t *keep, int32_t *n_kept,
-                         hipStream_t st);
+int pool_block_tokens(int C);
+hipError_t launch_pool_chunk(const PoolParams &p, const PoolTable &blocks, const float *imp,
+                             float *token_scores, float *chunk_scores, void *ws, hipStream_t st);
+constexpr int kMaxPoolWindow = 129;
+size_t pool_ws(int B, int total_blocks);
+
+// Chunk selection tables (host-computed), passed by value.
+struct SelectTable {
+  int32_t B;
+  int32_t chunk_off[SP_MAX_PROMPTS + 1];   // chunk prefix per prompt
+  int32_t blk_off[SP_MAX_PROMPTS + 1];     // rank-kernel block prefix per prompt
+  int32_t kc[SP_MAX_PROMPTS];              // top-p budget per prompt
+};
+int select_rank_blocks(int nc);
+size_t select_ws(int B, int total_chunks);
+hipError_t launch_select(int mode, double param, const SelectTable &t, const float *chunk_scores,
+                         uint8_t *keep, int32_t *n_kept, void *ws, hipStream_t st);
 
 hipError_t launch_gather(const SegTable &chunks, const SegTable &blocks, int total_blocks, int C,
                          const uint8_t *keep, const int32_t *ids, int32_t *kept_ids,

@@ -244,7 +244,7 @@ def sp_pool_chunk(importance: torch.Tensor, offsets, W=13, C=32, normalize=True,
 
 
 def sp_select_chunks(chunk_scores: torch.Tensor, offsets, C: int, mode: str, param: float,
-                     out_keep=None, out_counts=None):
+                     out_keep=None, out_counts=None, ws=None):
     """(keep [sum nc_b] uint8, n_kept_chunks [B] int32)."""
     batch = offsets if isinstance(offsets, Batch) else Batch(offsets)
     if chunk_scores.dtype != torch.float32:
@@ -255,8 +255,10 @@ def sp_select_chunks(chunk_scores: torch.Tensor, offsets, C: int, mode: str, par
     if out_counts is None:
         out_counts = torch.empty(batch.B, dtype=torch.int32, device=dev)
     m = _MODES[mode] if isinstance(mode, str) else int(mode)
+    if ws is None:
+        ws = _ws(select_workspace_bytes(batch, C), dev)
     _check(lib().sp_select_chunks(m, float(param), batch.ref(), C, _ptr(chunk_scores),
-                                  _ptr(out_keep), _ptr(out_counts), ctypes.c_void_p(0), 0,
+                                  _ptr(out_keep), _ptr(out_counts), _ptr(ws), ws.numel(),
                                   _stream(dev)), "sp_select_chunks")
     return out_keep, out_counts
 
@@ -316,6 +318,7 @@ class Pipeline:
         self.kept_offsets = torch.empty(B + 1, dtype=torch.int64, device=device)
         self.ws_score = _ws(score_workspace_bytes(self.adesc, self.batch), device)
         self.ws_pool = _ws(pool_workspace_bytes(self.pdesc, self.batch), device)
+        self.ws_select = _ws(select_workspace_bytes(self.batch, C), device)
         self.ws_gather = _ws(gather_workspace_bytes(self.batch, C), device)
         self.device = device
 
@@ -333,7 +336,8 @@ class Pipeline:
                                _ptr(self.token_scores), _ptr(self.chunk_scores),
                                _ptr(self.ws_pool), self.ws_pool.numel(), st), "sp_pool_chunk")
         _check(L.sp_select_chunks(self.mode, self.param, b, self.C, _ptr(self.chunk_scores),
-                                  _ptr(self.keep), _ptr(self.n_kept), ctypes.c_void_p(0), 0, st),
+                                  _ptr(self.keep), _ptr(self.n_kept), _ptr(self.ws_select),
+                                  self.ws_select.numel(), st),
                "sp_select_chunks")
         _check(L.sp_gather_kept(b, self.C, _ptr(self.keep), _ptr(token_ids), _ptr(self.kept_ids),
                                 _ptr(self.kept_pos), _ptr(self.kept_offsets),

@@ -180,12 +180,18 @@ sp_status sp_pool_chunk(const sp_pool_desc *desc, const sp_batch *batch, const f
  *     ceil(p * nc - 1e-9))) chunks (computed in double), the final one
  *     included.
  *   SP_SELECT_MASS: param = mass in (0, 1]; keeps the final chunk, then
- *     chunks in visiting order while the kept score sum (fp64) is below
+ *     chunks in visiting order while the kept score sum is below
  *     mass * (sum of all chunk scores); the chunk that reaches it is kept.
+ * Arithmetic: scores are ranked and summed as 64-bit fixed point scaled to
+ * the prompt's largest score (resolution 2^-48 of it; exact, order-free
+ * sums), ranked on the top 32 bits of that value: scores closer than 2^-32
+ * of the largest count as equal and go by index.
  *
  *   chunk_scores:  [sum nc_b] fp32 in (finite, >= 0).
  *   keep:          [sum nc_b] uint8 out (0/1).
  *   n_kept_chunks: [B] int32 out.
+ *   ws: device workspace of sp_select_workspace_bytes() bytes (currently
+ *       0: may be NULL).
  */
 sp_status sp_select_chunks(int32_t mode, double param, const sp_batch *batch, int32_t chunk_size,
                            const float *chunk_scores, uint8_t *keep, int32_t *n_kept_chunks,

@@ -13,7 +13,7 @@ import oracle
 import workloads
 from draft_attention_token_amd import specprefill as sp
 
-from parity import assert_scores_close, check_prompt
+from parity import KEY_TOL, SUM_TOL, assert_scores_close, check_prompt, excused_chunks
 
 pytestmark = pytest.mark.gpu
 
@@ -175,6 +175,56 @@ def test_score_workspace_reused_across_batches_and_algorithms():
     ora = oracle.importance(base.offsets.numpy(), base.q, base.k, w.n_layers, w.n_q_heads,
                             w.n_kv_heads, w.head_dim, w.n_lookahead, base.scale)
     assert_scores_close(fresh["base", "stream"].numpy(), ora, "importance")
+
+
+SELECT_SCORE_KINDS = ["uniform", "ties", "equal", "zero", "spiky"]
+
+
+def _select_scores(kind, nc, rng):
+    if kind == "uniform":
+        return rng.random(nc).astype(np.float32)
+    if kind == "ties":
+        return rng.choice(np.array([0.0, 0.25, 0.5, 1.0], dtype=np.float32), nc)
+    if kind == "equal":
+        return np.full(nc, 0.7, dtype=np.float32)
+    if kind == "zero":
+        return np.zeros(nc, dtype=np.float32)
+    x = (rng.random(nc) ** 8).astype(np.float32)        # most mass in a few chunks
+    x[rng.integers(0, nc, 3)] = 50.0
+    return x
+
+
+@pytest.mark.parametrize("kind", SELECT_SCORE_KINDS)
+@pytest.mark.parametrize("mode, params", [("top_p", (0.01, 0.15, 0.5, 1.0)),
+                                          ("mass", (0.01, 0.5, 0.85, 1.0))])
+def test_select_chunks_edge_cases(kind, mode, params):
+    """The selection kernel alone on constructed chunk scores: ties, constant
+    and all-zero prompts, a few dominant chunks, 1 to 16384 chunks per prompt,
+    several prompts per batch; exact against the oracle's rule."""
+    rng = np.random.default_rng(7)
+    ncs = [1, 2, 3, 33, 1000, 4096, 16384]
+    offsets = np.concatenate([[0], np.cumsum([32 * n for n in ncs])]).astype(np.int64)
+    batch = sp.Batch(offsets)
+    scores = [_select_scores(kind, n, rng) for n in ncs]
+    cs = torch.from_numpy(np.concatenate(scores)).to(DEV)
+    coff = np.concatenate([[0], np.cumsum(ncs)])
+    for param in params:
+        keep, cnt = sp.sp_select_chunks(cs, batch, 32, mode, param)
+        keep, cnt = keep.cpu().numpy(), cnt.cpu().numpy()
+        for bi, n in enumerate(ncs):
+            got = keep[coff[bi]:coff[bi + 1]]
+            sc64 = scores[bi].astype(np.float64)
+            want = oracle.select(sc64, mode, param)
+            diff = np.flatnonzero(got != want)
+            if diff.size:
+                # Only where the kernel's fixed-point order and sums may
+                # legitimately differ from fp64 (see tests/parity.py).
+                assert kind in ("uniform", "spiky"), (kind, mode, param, n, diff[:10])
+                ex = excused_chunks(sc64, want, mode, param, cutoff_tol=KEY_TOL * sc64.max(),
+                                    mass_tol=SUM_TOL)
+                bad = [int(i) for i in diff if int(i) not in ex]
+                assert not bad, (kind, mode, param, n, bad[:10])
+            assert cnt[bi] == int(got.sum())
 
 
 def test_pool_select_gather_stages_on_oracle_importance():
