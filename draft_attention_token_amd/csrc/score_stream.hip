@@ -11,35 +11,40 @@
 // than read K twice, the logits stay on chip and the lse arrives later:
 //
 //  * Persistent grid, one block per CU (a block's shared memory admits only
-//    one per unit), all blocks resident at once. A block owns <= 18
-//    contiguous 32-key tiles of one prompt for the whole kernel (prompt keys
-//    and lookahead keys alike).
+//    one per unit), all blocks resident at once. Streaming blocks each own
+//    <= 18 contiguous 32-key tiles of one prompt for the whole kernel
+//    (prompt keys and lookahead keys alike). Eight more blocks, one per chip
+//    die (XCD), read no K at all: they do the cross-block merges (below).
 //  * The work is a sequence of problems (layer l, KV group g), each with
 //    L * G <= 32 query rows (step j, head-in-group hh), padded to 32.
-//  * Six compute waves per block, <= 3 tiles each. Per problem a wave
-//    computes logits with 32x32x16 bf16 MFMA, K as the A operand (MFMA row =
-//    key) and Q as the B operand (MFMA column = query row): a lane holds one
-//    query row and 16 keys of each tile, so a row's max and sum over the
-//    wave's keys reduce inside the lane plus one swap of wave halves. As
-//    soon as a tile's MFMAs have consumed its K registers, the wave refills
-//    them with the next problem's tile: the K stream never waits for
-//    synchronisation. Statistics are accumulated tile by tile (online max,
-//    rescaled sum); each tile's e = 2^(x - m) is relative to the running max
-//    m at that tile, kept per tile.
+//  * Six compute waves per streaming block, <= 3 tiles each. Per problem a
+//    wave computes logits with 32x32x16 bf16 MFMA, K as the A operand (MFMA
+//    row = key) and Q as the B operand (MFMA column = query row): a lane
+//    holds one query row and 16 keys of each tile, so a row's max and sum
+//    over the wave's keys reduce inside the lane plus one swap of wave
+//    halves. Statistics are accumulated tile by tile (online max, rescaled
+//    sum); each tile's e = 2^(x - m) is relative to the running max m at
+//    that tile, kept per tile. A tile's registers are refilled with the next
+//    problem's K right after its MFMAs, so the K stream never waits for the
+//    cross-block exchange.
 //  * The last compute wave to finish a problem merges the six waves'
 //    statistics into the block's partial base-2 lse of each row and posts
-//    it to the workspace (one float per row) at once.
-//  * Two control waves do the rest of the cross-block work, so no compute
-//    wave ever waits on a load other than its own K (on this hardware a
-//    wait on any load also waits on every load issued before it, which
-//    would drain the K prefetch). They take alternate problems: for its
+//    it to the workspace (one float per row).
+//  * Exchange, per problem and prompt, in two hops. The prompt's streaming
+//    blocks on one die form a group; the merge block of that die waits for
+//    the group's partials, merges them and posts the die partial. Every
+//    streaming block then merges the (at most eight) die partials itself,
+//    in die order, so all get the same bits. The merge blocks issue no K
+//    loads, so their reads and posts never queue behind a K stream (a CU
+//    serves its vector memory requests roughly in order). Under a full K
+//    stream each hop through device-coherent memory costs about two
+//    microseconds, which is why there are only two.
+//  * Two control waves per streaming block take alternate problems: for
 //    problem x a control wave stages Q(x + 1) (prefetched into its
-//    registers), then reads every block's partials of x (plain loads,
-//    shared through the L2 of its chip die), merges them in block order and
-//    stages the row lse of x in LDS. Compute and control waves hand data
-//    over through LDS flags rather than block barriers, so a slow
-//    cross-block read only stalls the compute waves when they need its
-//    result.
+//    registers), then merges the die partials of x and stages the row lse
+//    in LDS. Compute and control waves hand data over through LDS flags
+//    rather than block barriers, so a late lse only stalls the compute
+//    waves when they need it.
 //  * The compute waves fold problem i - 2 while working on problem i: they
 //    park e in LDS (two problem slots) and turn it into probabilities
 //    p = e * 2^(m_tile - lse) once the lse is staged, kept as a running max
@@ -47,16 +52,13 @@
 //  * Finally: max over the G heads of a step (lanes of a group), mean over
 //    the L steps (a butterfly across groups of lanes), store.
 //
-// Partial slots. A slot holding all-zero bits has not been posted (a posted
-// value is never +0.0: it is stored as -0.0). A block that reads an empty
-// slot (not posted yet, or a stale copy in its die's L2) reads it again with
-// a load that bypasses the L2. Slots are left empty for the next launch:
-// once a block has merged every block's partials of problem x, every block
-// has finished reading the partials of problem x - 3 (a block posts x only
-// after folding x - 2, which needs its merge of x - 2 and, before that, of
-// x - 3), so the block clears its own slots of x - 3; the last block to
-// finish clears the final three problems' slots of every block. A zero-filled
-// workspace is therefore ready for the first launch and stays ready.
+// Slots. A slot holding all-zero bits has not been posted (a posted value is
+// never +0.0: it is stored as -0.0). Slots are left empty for the next
+// launch: a streaming block empties its partial of x once it has merged the
+// die partials of x (the merge of its group came first), then counts itself
+// as a reader of the die partials of (x, prompt); the last reader empties
+// them and resets the count. A zero-filled workspace is therefore ready for
+// the first launch and stays ready.
 //
 // Every wait is bounded (about 2 s); on time-out the kernel records it in the
 // workspace header and runs to completion, so the grid always drains.
@@ -72,28 +74,47 @@ namespace {
 
 constexpr int kCompute = 6;                       // compute waves per block
 constexpr int kControl = 2;                       // control waves (even / odd problems)
-constexpr int kThreads = (kCompute + kControl) * 64;
+constexpr int kWaves = kCompute + kControl;
+constexpr int kThreads = kWaves * 64;
 constexpr int kTPW = 3;                           // tiles per compute wave
 constexpr int kTilesPerCta = kCompute * kTPW;     // 18
 constexpr int kLag = 2;                           // problems between logits and fold
-constexpr int kClearLag = 3;                      // slots of x - 3 are free after merging x
 constexpr uint64_t kWaitTicks = 200000000ull;     // wall clock runs at 100 MHz: 2 s
 constexpr int kQPad = 8;                          // bf16 padding per staged Q row
+constexpr int kDies = 8;                          // XCDs; block c runs on die c % 8
 constexpr int kMaxCtas = 256;                     // blocks per launch (one per CU)
+constexpr int kMaxStream = kMaxCtas - kDies;      // streaming blocks per launch
+constexpr int kMaxMembers = kMaxStream / kDies;   // streaming blocks per die (31)
+
 
 struct StreamTable {
   int32_t B;        // prompts in this launch
   int32_t p0;       // global index of the first one
+  int32_t n_stream; // streaming blocks 0 .. n_stream - 1
+  int32_t merge0;   // merge block of die d: merge0 + d (merge0 % 8 == 0)
   int32_t tok_off[SP_MAX_PROMPTS + 1];   // global token offsets of prompts p0 .. p0 + B
-  int32_t cta_off[SP_MAX_PROMPTS + 1];   // block prefix within this launch
+  int32_t cta_off[SP_MAX_PROMPTS + 1];   // streaming-block prefix within this launch
 };
 
+// Workspace slots, as uint32 bits of floats (0 = empty). Per problem x:
+//   slot, lslot [x][cta][32]          partial lse of each streaming block
+//   dslot       [x][prompt][die][32]  die partials
+//   readers     [x][prompt]           streaming blocks done with dslot[x][prompt]
 struct StreamWs {
-  uint32_t *hdr;    // [0]: tag of a call that timed out; [1]: tag of the latest
-                    // call; [2]: blocks of the running launch that have finished
-  uint32_t *slot;   // [P][n_cta][32]: bits of each block's partial lse per row
+  uint32_t *hdr;    // [0]: tag of a call that timed out; [1]: tag of the latest call
+  uint32_t *slot;   // device-coherent copy (read by a merge block elsewhere)
+  uint32_t *lslot;  // ordinary-store copy (kept in the die's L2)
+  uint32_t *dslot;
+  uint32_t *readers;
   uint32_t call_tag;
 };
+
+__host__ __device__ constexpr int64_t cta_slot(int x, int cta) {
+  return ((int64_t)x * kMaxCtas + cta) * kRows;
+}
+__host__ __device__ constexpr int64_t die_slot(int x, int bb, int die) {
+  return (((int64_t)x * SP_MAX_PROMPTS + bb) * kDies + die) * kRows;
+}
 
 template <int D>
 struct Smem {
@@ -107,10 +128,8 @@ struct Smem {
   int q_seq;         // Q of problems < q_seq has been staged (one at a time)
   int q_used;        // compute waves that have read the staged Q
   int stats_cnt;     // compute waves that have written their statistics
-  int posted;        // problems this block has posted
   int lse_ready[2];  // lse[s] holds problem lse_ready[s] - 1 (0: nothing yet)
   int lse_used;      // compute waves that have folded with a staged lse
-  int ctl_done;      // control waves that have finished
 };
 
 __device__ __forceinline__ int lds_get(const int *p) {
@@ -126,6 +145,10 @@ __device__ __forceinline__ int lds_inc(int *p) {
 }
 __device__ __forceinline__ void timeout(const StreamWs &ws) {
   __hip_atomic_store(ws.hdr, ws.call_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Device-coherent store (reaches every die).
+__device__ __forceinline__ void post(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wait (bounded) until *p >= v.
@@ -183,70 +206,44 @@ __device__ __forceinline__ float lse_of(float m, float z) {
   return (m == -INFINITY || !(z > 0.f)) ? -INFINITY : m + log2f(z);
 }
 
-// Merge every block's partial lse of one problem: lane l takes rows
-// 4 (l % 8) .. 4 (l % 8) + 3 of blocks l / 8, l / 8 + 8, ... (in block order),
-// then the eight lanes of a row quad merge by an xor tree (each merge is
-// symmetric, so every lane ends with identical bits). Lanes 0..7 return the
-// row lse of rows 4 l .. 4 l + 3. Empty slots are read again bypassing the L2.
-//
-// Buffer loads: the resource covers exactly this prompt's slots of the
-// problem, so the loads of blocks past its last one return zeros without
-// touching memory, and each load's block offset is a scalar operand (no
-// per-load address registers).
-__device__ f32x4 gather_lse(const StreamWs &ws, int prob, int n_cta, int c_lo, int n_c, int lane) {
-  constexpr int kPer = kMaxCtas / 8;
-  constexpr int kStride = 8 * kRows * (int)sizeof(float);   // bytes between a lane's blocks
-  const uint32_t *base = ws.slot + ((int64_t)prob * n_cta + c_lo) * kRows;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t *>(base), 0, n_c * kRows * (int)sizeof(float), 0x00020000);
-  const int c0 = lane >> 3;
-  const int voff = c0 * kRows * (int)sizeof(float) + (lane & 7) * 16;
-  u32x4 v[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, u * kStride, 0);
-  const uint64_t t0 = wall_clock64();
-  for (;;) {
-    bool ok = true;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u)
-      ok &= (c0 + 8 * u >= n_c) | ((v[u][0] != 0u) & (v[u][1] != 0u) & (v[u][2] != 0u) & (v[u][3] != 0u));
-    if (__all(ok)) break;
-    if (wall_clock64() - t0 > kWaitTicks) { timeout(ws); break; }
-    __builtin_amdgcn_s_sleep(1);
-    asm volatile("" ::: "memory");   // the slots change behind the compiler's back: reload
-    // Only the quads with an empty slot; cache policy 16: device-coherent
-    // (bypasses this die's L2).
-#pragma unroll
-    for (int u = 0; u < kPer; ++u)
-      if ((v[u][0] == 0u) | (v[u][1] == 0u) | (v[u][2] == 0u) | (v[u][3] == 0u))
-        v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, u * kStride, 16);
-  }
-  // Row max first (exact, so the order does not matter), across the lanes
-  // of the row quad too; then one exp per partial and a sum tree. Every
-  // combination is of two values, so all lanes of a quad end with the same
-  // bits (a + b == b + a).
+// The streaming blocks of prompt bb on die d: c_lo <= c < c_lo + n_c with
+// c % 8 == d, i.e. first, first + 8, ... (size of them, possibly none).
+struct Group {
+  int first;
+  int size;
+};
+
+__device__ __forceinline__ Group group_of(int d, int c_lo, int n_c) {
+  Group g;
+  g.first = c_lo + ((d - c_lo) & (kDies - 1));
+  g.size = g.first < c_lo + n_c ? (c_lo + n_c - 1 - g.first) / kDies + 1 : 0;
+  return g;
+}
+
+// Merge (lse) of up to 4 partials per lane and row, across the lanes of a
+// row quad (lane bits 3..5): the max first (exact, order-free), then one exp
+// per partial and a sum tree. Every combination is of two values, so all
+// lanes of a quad end with the same bits (a + b == b + a).
+template <int N>
+__device__ __forceinline__ f32x4 merge_quads(const u32x4 (&v)[N], const bool (&in)[N]) {
   f32x4 M = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const bool in = c0 + 8 * u < n_c;
+  for (int u = 0; u < N; ++u)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) M[e] = fmaxf(M[e], in ? __uint_as_float(v[u][e]) : -INFINITY);
-  }
+    for (int e = 0; e < 4; ++e) M[e] = fmaxf(M[e], in[u] ? __uint_as_float(v[u][e]) : -INFINITY);
 #pragma unroll
   for (int off = 8; off < 64; off <<= 1)
 #pragma unroll
     for (int e = 0; e < 4; ++e) M[e] = fmaxf(M[e], __shfl_xor(M[e], off, 64));
-  f32x4 Z = {0.f, 0.f, 0.f, 0.f};
-  f32x4 Ms;   // M, or 0 where the row has no keys (keeps the exps finite)
+  f32x4 Ms;   // M, or 0 where a row has no keys (keeps the exps finite)
 #pragma unroll
   for (int e = 0; e < 4; ++e) Ms[e] = M[e] == -INFINITY ? 0.f : M[e];
+  f32x4 Z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const bool in = c0 + 8 * u < n_c;
+  for (int u = 0; u < N; ++u)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      Z[e] += in ? __builtin_amdgcn_exp2f(__uint_as_float(v[u][e]) - Ms[e]) : 0.f;
-  }
+      Z[e] += in[u] ? __builtin_amdgcn_exp2f(__uint_as_float(v[u][e]) - Ms[e]) : 0.f;
 #pragma unroll
   for (int off = 8; off < 64; off <<= 1)
 #pragma unroll
@@ -257,9 +254,119 @@ __device__ f32x4 gather_lse(const StreamWs &ws, int prob, int n_cta, int c_lo, i
   return out;
 }
 
+__device__ __forceinline__ bool quad_full(const u32x4 &v) {
+  return (v[0] != 0u) & (v[1] != 0u) & (v[2] != 0u) & (v[3] != 0u);
+}
+
+// A slot value is never all-zero bits (the empty mark): +0.0 goes as -0.0.
+__device__ __forceinline__ uint32_t slot_bits(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return u ? u : 0x80000000u;
+}
+
+// Loads that see other CUs' stores: cache policy 16 (device scope). Plain
+// and policy-1 loads can keep returning a stale line that another CU wrote.
+constexpr int kCoherent = 16;
+
+// A merge block's merge of its group's partials of problem x: lane l takes
+// rows 4 (l % 8) .. + 3 of members l / 8, l / 8 + 8, ... (member k is block
+// first + 8 k, in member order). Polls read the ordinary-store copies, which
+// a member on the same die makes visible within about 0.2 us; every eighth
+// poll reads the device-coherent copies instead, in case a member runs on
+// another die. Buffer loads: the resources cover the group's slots only,
+// loads past them return zeros.
+__device__ f32x4 gather_group(const StreamWs &ws, int x, const Group &g, int lane) {
+  constexpr int kPer = (kMaxMembers + 7) / 8;             // members per lane
+  constexpr int kMember = kDies * kRows * (int)sizeof(float);   // bytes between members
+  const int64_t at = cta_slot(x, g.first);
+  const int bytes = (g.size - 1) * kMember + kRows * (int)sizeof(float);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t *>(ws.lslot + at), 0, bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t *>(ws.slot + at), 0, bytes, 0x00020000);
+  const int m0 = lane >> 3;
+  const int voff = m0 * kMember + (lane & 7) * 16;
+  bool in[kPer];
+  u32x4 v[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    in[u] = m0 + 8 * u < g.size;
+    v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, u * 8 * kMember, kCoherent);
+  }
+  const uint64_t t0 = wall_clock64();
+  for (int round = 1;; ++round) {
+    bool ok = true;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) ok &= !in[u] | quad_full(v[u]);
+    if (__all(ok)) break;
+    if (wall_clock64() - t0 > kWaitTicks) { timeout(ws); break; }
+    asm volatile("" ::: "memory");   // the slots change behind the compiler's back: reload
+    const bool far = (round & 7) == 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (in[u] && !quad_full(v[u]))
+        v[u] = far ? __builtin_amdgcn_raw_buffer_load_b128(rg, voff, u * 8 * kMember, kCoherent)
+                   : __builtin_amdgcn_raw_buffer_load_b128(rs, voff, u * 8 * kMember, kCoherent);
+  }
+  return merge_quads(v, in);
+}
+
+// A merge block's merge of the die partials of (x, prompt bb): lane l takes
+// rows 4 (l % 8) .. + 3 of die l / 8, for the dies set in `dies`.
+__device__ f32x4 gather_dies(const StreamWs &ws, int x, int bb, unsigned dies, int lane) {
+  const uint32_t *base = ws.dslot + die_slot(x, bb, 0);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t *>(base), 0, kDies * kRows * (int)sizeof(float), 0x00020000);
+  const int voff = (lane >> 3) * kRows * (int)sizeof(float) + (lane & 7) * 16;
+  const bool in[1] = {((dies >> (lane >> 3)) & 1u) != 0u};
+  u32x4 v[1];
+  v[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, kCoherent);
+  const uint64_t t0 = wall_clock64();
+  for (;;) {
+    if (__all(!in[0] | quad_full(v[0]))) break;
+    if (wall_clock64() - t0 > kWaitTicks) { timeout(ws); break; }
+    asm volatile("" ::: "memory");
+    if (in[0] && !quad_full(v[0]))
+      v[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, kCoherent);
+  }
+  return merge_quads(v, in);
+}
+
+// Dies holding streaming blocks of a prompt: (c_lo + i) % 8 for i < min(n_c, 8).
+__device__ __forceinline__ unsigned prompt_dies(int c_lo, int n_c) {
+  if (n_c >= kDies) return 0xffu;
+  const unsigned d = ((1u << n_c) - 1u) << (c_lo & (kDies - 1));
+  return (d | (d >> kDies)) & 0xffu;
+}
+
+// Lanes 0..7 post rows 4 lane .. + 3 of a merged quad (device-coherent).
+__device__ __forceinline__ void post_rows(uint32_t *dst, const f32x4 &v, int lane) {
+  if (lane < 8) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) post(dst + 4 * lane + e, slot_bits(v[e]));
+  }
+}
+
+// Merge block of die d. Its waves take the (problem, prompt) items x * B + bb
+// round robin, in increasing order; an item waits only on smaller ones, so
+// every item completes.
+__device__ void merge_block(const AttnShape &s, const StreamTable &tb, int d, int wave, int lane,
+                            const StreamWs &ws) {
+  const int P = s.n_layers * s.Hkv;
+  const int items = P * tb.B;
+  for (int it = wave; it < items; it += kWaves) {
+    const int x = it / tb.B, bb = it - x * tb.B;
+    const int c_lo = tb.cta_off[bb], n_c = tb.cta_off[bb + 1] - c_lo;
+    const Group g = group_of(d, c_lo, n_c);
+    if (g.size == 0) continue;   // the prompt has no blocks on this die
+    const f32x4 gl = gather_group(ws, x, g, lane);
+    post_rows(ws.dslot + die_slot(x, bb, d), gl, lane);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable tb,
-                                                        int64_t total_keys, int n_cta,
+                                                        int64_t total_keys,
                                                         const __bf16 *__restrict__ q,
                                                         const __bf16 *__restrict__ k,
                                                         float *__restrict__ imp, StreamWs ws) {
@@ -269,6 +376,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
   // derived from it in scalar registers and every branch on it scalar.
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, r = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int P = s.n_layers * s.Hkv;
+  if (cta >= tb.n_stream) {
+    // Merge blocks, and idle blocks that only pad the merge blocks onto a
+    // multiple of 8.
+    if (cta >= tb.merge0) merge_block(s, tb, cta - tb.merge0, wave, lane, ws);
+    return;
+  }
   const bool control = wave >= kCompute;
   const int bb = cta_prompt(tb, cta), b = tb.p0 + bb;
   const int c_lo = tb.cta_off[bb], n_c = tb.cta_off[bb + 1] - c_lo, ci = cta - c_lo;
@@ -278,15 +392,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
   const int ta = (int)((int64_t)tiles * ci / n_c);
   const int nt = (int)((int64_t)tiles * (ci + 1) / n_c) - ta;
   const int64_t key0 = (int64_t)tb.tok_off[bb] + (int64_t)b * s.L;
-  const int P = s.n_layers * s.Hkv;
 
   if (control) {
-    // ---------------- control waves: merges, Q staging ----------------
+    // ---------------- control waves: Q staging, row lse ----------------
     // Control wave c takes the problems x = c, c + 2, ...: once the compute
     // waves' statistics of x are in, it stages Q(x + 1) (prefetched into its
-    // registers), then reads every block's partials of x, merges them and
-    // stages the row lse of x. Each control wave thus has two problems'
-    // time for one such round.
+    // registers), then merges the die partials of x into the row lse and
+    // stages it. Each control wave thus has two problems' time for one such
+    // round.
     const int cw = wave - kCompute;
     QRegs<D> qn;
     if (cw == 0) {
@@ -295,16 +408,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
       if (lane == 0) {
         sm.q_used = 0;
         sm.stats_cnt = 0;
-        sm.posted = 0;
         sm.lse_ready[0] = 0;
         sm.lse_ready[1] = 0;
         sm.lse_used = 0;
-        sm.ctl_done = 0;
         lds_set(&sm.q_seq, 1);
         __hip_atomic_store(ws.hdr + 1, ws.call_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     if (cw + 1 < P) load_q(qn, s, q, b, cw + 1, lane);
+    const unsigned dies = prompt_dies(c_lo, n_c);
+    // The last of the prompt's blocks to read the die partials of x empties
+    // them (64 lanes x 16 bytes: all eight dies) and the count.
+    uint32_t pend = 0u;
+    int px = -1;
+    auto last_reader = [&](int x, uint32_t v) {
+      if (x < 0 || __builtin_amdgcn_readfirstlane(v) != (uint32_t)n_c - 1u) return;
+      uint32_t *dp = ws.dslot + die_slot(x, bb, 0) + 4 * lane;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) post(dp + e, 0u);
+      if (lane == 0) post(ws.readers + (int64_t)x * SP_MAX_PROMPTS + bb, 0u);
+    };
     __syncthreads();
     for (int x = cw; x < P; x += kControl) {
       lds_wait_ge(&sm.stats_cnt, kCompute * (x + 1), ws);
@@ -313,34 +436,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
         store_q(sm, qn, lane);
         if (lane == 0) lds_set(&sm.q_seq, x + 2);
       }
-      lds_wait_ge(&sm.posted, x + 1, ws);                   // our own partial is out
-      const f32x4 lq = gather_lse(ws, x, n_cta, c_lo, n_c, lane);
-      // The Q prefetch goes out after the gather's loads, so their wait
-      // does not include it.
+      last_reader(px, pend);
+      px = -1;
+      const f32x4 lq = gather_dies(ws, x, bb, dies, lane);
+      // The Q prefetch goes out after the gather's loads, so its waits do
+      // not include it.
       if (x + 1 + kControl < P) load_q(qn, s, q, b, x + 1 + kControl, lane);
       if (x >= 2) lds_wait_ge(&sm.lse_used, kCompute * (x - 1), ws);   // slot is free
       if (lane < 8) *reinterpret_cast<f32x4 *>(&sm.lse[x & 1][4 * lane]) = lq;
       if (lane == 0) lds_set(&sm.lse_ready[x & 1], x + 1);
-      // Every block has read our partials of x - 3: leave them empty.
-      if (x >= kClearLag && lane < kRows)
-        ws.slot[((int64_t)(x - kClearLag) * n_cta + cta) * kRows + lane] = 0u;
-    }
-    // The last control wave of the last block out empties the slots of the
-    // final problems, which no block can clear earlier.
-    const int order = __builtin_amdgcn_readfirstlane(lane == 0 ? lds_inc(&sm.ctl_done) : 0);
-    if (order == kControl - 1) {
-      const uint32_t done = __builtin_amdgcn_readfirstlane(
-          lane == 0 ? __hip_atomic_fetch_add(ws.hdr + 2, 1u, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT)
-                    : 0u);
-      if (done == gridDim.x - 1) {
-        const int x0 = P > kClearLag ? P - kClearLag : 0;
-        const int n16 = (P - x0) * n_cta * kRows / 4;
-        u32x4 *tail = reinterpret_cast<u32x4 *>(ws.slot + (int64_t)x0 * n_cta * kRows);
-        for (int i = lane; i < n16; i += 64) tail[i] = u32x4{0u, 0u, 0u, 0u};
-        if (lane == 0) __hip_atomic_store(ws.hdr + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // The merge block of our group has read our partial of x.
+      if (lane < kRows) {
+        ws.slot[cta_slot(x, cta) + lane] = 0u;
+        ws.lslot[cta_slot(x, cta) + lane] = 0u;
       }
+      // Count ourselves as a reader of the die partials of x; the result is
+      // looked at a round later (it comes back behind the block's K loads).
+      pend = lane == 0 ? __hip_atomic_fetch_add(ws.readers + (int64_t)x * SP_MAX_PROMPTS + bb,
+                                                1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : 0u;
+      px = x;
     }
+    last_reader(px, pend);
     return;
   }
 
@@ -407,9 +524,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
       // register copy would not fit), so the staging buffer is released
       // after the last tile's MFMAs.
       lds_wait_ge(&sm.q_seq, it + 1, ws);
-      // Base of the next problem's K (the last problem reloads its own).
+      // Base of the next problem's K. After the last problem the loads
+      // (unconditional, see above) go to the prompt's first 96 keys, which
+      // every wave of the prompt shares, instead of a whole problem again.
       if (it + 1 < P && ++gn == s.Hkv) { gn = 0; ++ln; }
-      const __bf16 *kb_next = kprompt + ln * kstride_l + gn * D;
+      const __bf16 *kb_next = it + 1 < P ? kprompt + ln * kstride_l + gn * D
+                                         : kprompt - (int64_t)w_t0 * kTile * s.Hkv * D;
       float m = -INFINITY, z = 0.f;    // base-2 running max and sum of this lane's keys
 #pragma unroll
       for (int t = 0; t < kTPW; ++t) {
@@ -421,6 +541,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
                                                      __builtin_bit_cast(bf16x8, qs[2 * st]), x, 0,
                                                      0, 0);
         if (t == kTPW - 1 && lane == 0) lds_inc(&sm.q_used);
+        // The tile's registers take the next problem's K at once: the K
+        // stream runs ahead by one problem.
+        __builtin_amdgcn_sched_barrier(0);
         load_k(kb_next, t);
         if (t < full_tiles) {
           // All keys are prompt keys, seen by every row: no masks. (Padding
@@ -463,24 +586,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
         mref[0][t] = m;
       }
       // Merge the two wave halves (same row, different keys) and hand the
-      // wave's statistics to the control wave.
+      // wave's statistics over.
       const float mo = __shfl_xor(m, 32, 64), zo = __shfl_xor(z, 32, 64);
       stats_merge(m, z, mo, zo);
       if (lane < 32) sm.red[it & 1][wave][r] = make_float2(m, z);
       // The last wave to finish the problem posts the block's partials.
       const int arrived = __builtin_amdgcn_readfirstlane(lane == 0 ? lds_inc(&sm.stats_cnt) : 0);
-      if (arrived == kCompute * (it + 1) - 1) {
-        if (lane < kRows) {
-          float M = -INFINITY, Z = 0.f;
+      if (arrived == kCompute * (it + 1) - 1 && lane < kRows) {
+        float M = -INFINITY, Z = 0.f;
 #pragma unroll
-          for (int w = 0; w < kCompute; ++w)
-            stats_merge(M, Z, sm.red[it & 1][w][lane].x, sm.red[it & 1][w][lane].y);
-          const uint32_t bits = __float_as_uint(lse_of(M, Z));
-          __hip_atomic_store(ws.slot + ((int64_t)it * n_cta + cta) * kRows + lane,
-                             bits ? bits : 0x80000000u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (lane == 0) lds_set(&sm.posted, it + 1);
+        for (int w = 0; w < kCompute; ++w)
+          stats_merge(M, Z, sm.red[it & 1][w][lane].x, sm.red[it & 1][w][lane].y);
+        // Twice: an ordinary store that the merge block of this die reads
+        // from the die's L2, and a device-coherent one for a merge block
+        // elsewhere.
+        const int64_t at = cta_slot(it, cta) + lane;
+        const uint32_t bits = slot_bits(lse_of(M, Z));
+        ws.lslot[at] = bits;
+        post(ws.slot + at, bits);
       }
     }
     if (it >= kLag) {
@@ -566,15 +689,16 @@ const DeviceInfo &device_info() {
   return info[dev];
 }
 
-// Split the batch into launches and give each prompt blocks in proportion to
-// its tiles (each block <= 18 tiles). Returns false if a prompt is too long.
+// Split the batch into launches and give each prompt streaming blocks in
+// proportion to its tiles (each block <= 18 tiles); the merge blocks follow
+// at the next multiple of 8. Returns false if a prompt is too long.
 struct Plan {
   int n_launch = 0;
   StreamTable t[SP_MAX_PROMPTS];
   int grid[SP_MAX_PROMPTS];
 };
 
-bool make_plan(const SegTable &tok, int L, int n_cta, Plan &plan) {
+bool make_plan(const SegTable &tok, int L, int n_stream, Plan &plan) {
   plan.n_launch = 0;
   int b = 0;
   while (b < tok.B) {
@@ -586,8 +710,8 @@ bool make_plan(const SegTable &tok, int L, int n_cta, Plan &plan) {
       const int n = tok.tok_off[b + 1] - tok.tok_off[b];
       const int tl = (n + L + kTile - 1) / kTile;
       const int nd = (tl + kTilesPerCta - 1) / kTilesPerCta;
-      if (nd > n_cta) return false;
-      if (used + nd > n_cta) break;
+      if (nd > n_stream) return false;
+      if (used + nd > n_stream) break;
       tiles[b - p0] = tl;
       need[b - p0] = nd;
       used += nd;
@@ -596,7 +720,7 @@ bool make_plan(const SegTable &tok, int L, int n_cta, Plan &plan) {
     const int B = b - p0;
     // Hand out the spare blocks one at a time to the prompt whose blocks
     // carry the most tiles (never more blocks than tiles).
-    int spare = n_cta - used;
+    int spare = n_stream - used;
     while (spare > 0) {
       int best = -1, best_load = 1;
       for (int i = 0; i < B; ++i) {
@@ -618,17 +742,31 @@ bool make_plan(const SegTable &tok, int L, int n_cta, Plan &plan) {
       t.cta_off[i + 1] = t.cta_off[i] + need[i];
     }
     t.tok_off[B] = tok.tok_off[p0 + B];
-    plan.grid[plan.n_launch] = t.cta_off[B];
+    t.n_stream = t.cta_off[B];
+    t.merge0 = (t.n_stream + kDies - 1) / kDies * kDies;
+    plan.grid[plan.n_launch] = t.merge0 + kDies;
     ++plan.n_launch;
   }
   return true;
 }
 
+// Streaming blocks per launch: the CUs (whole dies' worth) minus the merge
+// blocks, so that every block of a launch is resident at once.
 int stream_ctas(const AttnShape &s) {
   const DeviceInfo &d = device_info();
   const int occ = s.d == 128 ? d.occ128 : d.occ64;
-  if (occ < 1 || d.cus < 1) return 0;
-  return std::min(d.cus, kMaxCtas);
+  if (occ < 1 || d.cus < 2 * kDies) return 0;
+  return std::min(d.cus / kDies * kDies, kMaxCtas) - kDies;
+}
+
+size_t cta_region(const AttnShape &s) {
+  return align_up((size_t)s.n_layers * s.Hkv * kMaxCtas * kRows * sizeof(uint32_t));
+}
+size_t readers_region(const AttnShape &s) {
+  return align_up((size_t)s.n_layers * s.Hkv * SP_MAX_PROMPTS * sizeof(uint32_t));
+}
+size_t die_region(const AttnShape &s) {
+  return align_up((size_t)s.n_layers * s.Hkv * SP_MAX_PROMPTS * kDies * kRows * sizeof(uint32_t));
 }
 
 }  // namespace
@@ -641,7 +779,7 @@ bool score_stream_supported(const AttnShape &s) {
 
 size_t score_stream_slot_bytes(const AttnShape &s) {
   if (!score_stream_supported(s)) return 0;
-  return align_up((size_t)s.n_layers * s.Hkv * kMaxCtas * kRows * sizeof(uint32_t));
+  return 2 * cta_region(s) + die_region(s) + readers_region(s);
 }
 
 hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const void *q,
@@ -649,14 +787,19 @@ hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const 
                                bool *supported) {
   *supported = false;
   if (!score_stream_supported(s)) return hipSuccess;
-  const int n_cta = stream_ctas(s);
-  if (n_cta < 1) return hipSuccess;
+  const int n_stream = stream_ctas(s);
+  if (n_stream < 1) return hipSuccess;
   static thread_local Plan plan;
-  if (!make_plan(tiles, s.L, n_cta, plan)) return hipSuccess;
+  if (!make_plan(tiles, s.L, n_stream, plan)) return hipSuccess;
   *supported = true;
   StreamWs w;
-  w.hdr = reinterpret_cast<uint32_t *>(ws);
-  w.slot = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(ws) + kStatusBytes);
+  char *base = reinterpret_cast<char *>(ws);
+  w.hdr = reinterpret_cast<uint32_t *>(base);
+  base += kStatusBytes;
+  w.slot = reinterpret_cast<uint32_t *>(base);
+  w.lslot = reinterpret_cast<uint32_t *>(base + cta_region(s));
+  w.dslot = reinterpret_cast<uint32_t *>(base + 2 * cta_region(s));
+  w.readers = reinterpret_cast<uint32_t *>(base + 2 * cta_region(s) + die_region(s));
   w.call_tag = reserve_tags(1);
   const int64_t total_keys = (int64_t)tiles.tok_off[tiles.B] + (int64_t)tiles.B * tiles.L;
   const __bf16 *qp = reinterpret_cast<const __bf16 *>(q);
@@ -664,10 +807,10 @@ hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const 
   for (int li = 0; li < plan.n_launch; ++li) {
     if (s.d == 128)
       hipLaunchKernelGGL(k_stream<128>, dim3(plan.grid[li]), dim3(kThreads), 0, st, s, plan.t[li],
-                         total_keys, n_cta, qp, kp, imp, w);
+                         total_keys, qp, kp, imp, w);
     else
       hipLaunchKernelGGL(k_stream<64>, dim3(plan.grid[li]), dim3(kThreads), 0, st, s, plan.t[li],
-                         total_keys, n_cta, qp, kp, imp, w);
+                         total_keys, qp, kp, imp, w);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
