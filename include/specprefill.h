@@ -141,7 +141,8 @@ sp_status sp_gather_workspace_bytes(const sp_batch *batch, int32_t chunk_size, s
  *       workspace must not overlap in time.
  *   The single-pass kernel runs one block per compute unit and needs all of
  *   them resident together. Blocks exchange partial results through the
- *   workspace, tagged with the call, so nothing needs clearing between calls.
+ *   workspace; every launch empties again each slot it used, so nothing
+ *   needs clearing between calls.
  *   A block waits at most about 2 s for another one, then finishes without
  *   hanging the device and marks the call as failed (importance is then not
  *   valid); sp_score_status() reports it. Only other work that keeps compute
