@@ -364,6 +364,23 @@ __device__ void merge_block(const AttnShape &s, const StreamTable &tb, int d, in
   }
 }
 
+// One level of the final butterfly on every value of the wave's tiles:
+// Ctrl >= 0 is a DPP control (within rows of 16 lanes), -1 the swizzle that
+// exchanges lane bit 4 (within groups of 32 lanes). Max or sum.
+template <int Ctrl>
+__device__ __forceinline__ void butterfly_level(f32x16 (&run)[kTPW], bool use_max) {
+#pragma unroll
+  for (int t = 0; t < kTPW; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int v = __float_as_int(run[t][i]);
+      const float o = __int_as_float(Ctrl >= 0 ? __builtin_amdgcn_update_dpp(0, v, Ctrl & 0x1ff, 0xf,
+                                                                             0xf, false)
+                                               : __builtin_amdgcn_ds_swizzle(v, 0x401f));
+      run[t][i] = use_max ? fmaxf(run[t][i], o) : run[t][i] + o;
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable tb,
                                                         int64_t total_keys,
@@ -544,7 +561,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
         // The tile's registers take the next problem's K at once: the K
         // stream runs ahead by one problem.
         __builtin_amdgcn_sched_barrier(0);
-        load_k(kb_next, t);
+        if (t > 0) load_k(kb_next, t - 1);
         if (t < full_tiles) {
           // All keys are prompt keys, seen by every row: no masks. (Padding
           // rows compute harmless values that are never folded.)
@@ -605,6 +622,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
         ws.lslot[at] = bits;
         post(ws.slot + at, bits);
       }
+      load_k(kb_next, kTPW - 1);
     }
     if (it >= kLag) {
       // Fold problem it - kLag once its lse is staged: p = e * 2^(m_tile -
@@ -637,29 +655,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
 
   // Max over the G heads of each step (lanes j*G .. j*G+G-1), then the sum
   // over the steps (the other lane bits; padding rows hold 0): one butterfly
-  // over the five lane bits of the row, each level a max or a sum.
+  // over the five lane bits of the row, each level a max or a sum. After
+  // level k every aligned group of 2^k lanes holds one value, so a mirror
+  // inside the next group pairs the same partial results as an exchange
+  // across lane bit k: levels 1, 2 are quad permutations, 4 and 8 the
+  // half-row and row mirrors (all DPP), 16 a swizzle within 32 lanes.
+  butterfly_level<0xB1>(run, 1 < s.G);
+  butterfly_level<0x4E>(run, 2 < s.G);
+  butterfly_level<0x141>(run, 4 < s.G);
+  butterfly_level<0x140>(run, 8 < s.G);
+  butterfly_level<-1>(run, 16 < s.G);
+  // Every lane of a half now holds the 16 results of its half's keys; lane
+  // r < 16 stores result r, so each tile is one store instruction.
+  const float inv_l = 1.f / (float)s.L;
+  float *out = imp + tb.tok_off[bb];
 #pragma unroll
-  for (int lvl = 0; lvl < 5; ++lvl) {
-    const int off = 1 << lvl;
-    const bool head = off < s.G;
+  for (int t = 0; t < kTPW; ++t) {
+    float v = run[t][0];
 #pragma unroll
-    for (int t = 0; t < kTPW; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float o = __shfl_xor(run[t][i], off, 64);
-        run[t][i] = head ? fmaxf(run[t][i], o) : run[t][i] + o;
-      }
-  }
-  if (r == 0) {
-    float *out = imp + tb.tok_off[bb];
-#pragma unroll
-    for (int t = 0; t < kTPW; ++t) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = (w_t0 + t) * kTile + acc_row(i, half);
-        if (t < w_nt && key < N) out[key] = run[t][i] / (float)s.L;
-      }
-    }
+    for (int i = 1; i < 16; ++i) v = r == i ? run[t][i] : v;
+    const int key = (w_t0 + t) * kTile + acc_row(r & 15, half);
+    if (r < 16 && t < w_nt && key < N) out[key] = v * inv_l;
   }
 }
 
