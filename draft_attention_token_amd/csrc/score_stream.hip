@@ -400,6 +400,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
     if (cta >= tb.merge0) merge_block(s, tb, cta - tb.merge0, wave, lane, ws);
     return;
   }
+  // The hand-off counters start at zero; the block's only barrier comes
+  // before any load, so Q(0) and the first K tiles are fetched together.
+  if (tid == 0) {
+    sm.q_seq = 0;
+    sm.q_used = 0;
+    sm.stats_cnt = 0;
+    sm.lse_ready[0] = 0;
+    sm.lse_ready[1] = 0;
+    sm.lse_used = 0;
+    __hip_atomic_store(ws.hdr + 1, ws.call_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
   const bool control = wave >= kCompute;
   const int bb = cta_prompt(tb, cta), b = tb.p0 + bb;
   const int c_lo = tb.cta_off[bb], n_c = tb.cta_off[bb + 1] - c_lo, ci = cta - c_lo;
@@ -422,15 +434,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
     if (cw == 0) {
       load_q(qn, s, q, b, 0, lane);
       store_q(sm, qn, lane);
-      if (lane == 0) {
-        sm.q_used = 0;
-        sm.stats_cnt = 0;
-        sm.lse_ready[0] = 0;
-        sm.lse_ready[1] = 0;
-        sm.lse_used = 0;
-        lds_set(&sm.q_seq, 1);
-        __hip_atomic_store(ws.hdr + 1, ws.call_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      if (lane == 0) lds_set(&sm.q_seq, 1);
     }
     if (cw + 1 < P) load_q(qn, s, q, b, cw + 1, lane);
     const unsigned dies = prompt_dies(c_lo, n_c);
@@ -445,7 +449,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
       for (int e = 0; e < 4; ++e) post(dp + e, 0u);
       if (lane == 0) post(ws.readers + (int64_t)x * SP_MAX_PROMPTS + bb, 0u);
     };
-    __syncthreads();
     for (int x = cw; x < P; x += kControl) {
       lds_wait_ge(&sm.stats_cnt, kCompute * (x + 1), ws);
       if (x + 1 < P) {
@@ -525,7 +528,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
 
 #pragma unroll
   for (int t = 0; t < kTPW; ++t) load_k(kprompt, t);
-  __syncthreads();
 
   const u32x4 *qs = reinterpret_cast<const u32x4 *>(&sm.q[r][0]) + half;
   int ln = 0, gn = 0;     // (layer, group) of the next problem to load
