@@ -423,25 +423,44 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
   const int64_t key0 = (int64_t)tb.tok_off[bb] + (int64_t)b * s.L;
 
   if (control) {
-    // ---------------- control waves: Q staging, row lse ----------------
-    // Control wave c takes the problems x = c, c + 2, ...: once the compute
-    // waves' statistics of x are in, it stages Q(x + 1) (prefetched into its
-    // registers), then merges the die partials of x into the row lse and
-    // stages it. Each control wave thus has two problems' time for one such
-    // round.
-    const int cw = wave - kCompute;
-    QRegs<D> qn;
-    if (cw == 0) {
-      load_q(qn, s, q, b, 0, lane);
-      store_q(sm, qn, lane);
+    // ---------------- control waves ----------------
+    // Wave kCompute stages Q, wave kCompute + 1 the row lse. Neither waits
+    // for the other: a late lse (the cross-block exchange) must not hold up
+    // the next problem's Q.
+    if (wave == kCompute) {
+      // Q(x + 1) goes into the staging buffer once every compute wave has
+      // read Q(x) and written its statistics of x (so that no wave starts
+      // x + 1 before the last one has counted itself in for x: the last to
+      // arrive merges and posts). Two register sets hold the next two
+      // problems' Q, loaded two problems ahead (the loads queue behind the
+      // block's K stream).
+      QRegs<D> qa, qb;
+      load_q(qa, s, q, b, 0, lane);
+      store_q(sm, qa, lane);
       if (lane == 0) lds_set(&sm.q_seq, 1);
+      if (P > 1) load_q(qa, s, q, b, 1, lane);
+      if (P > 2) load_q(qb, s, q, b, 2, lane);
+      auto stage = [&](int x, QRegs<D> &qr) {   // Q(x + 1), then prefetch Q(x + 3)
+        lds_wait_ge(&sm.stats_cnt, kCompute * (x + 1), ws);
+        lds_wait_ge(&sm.q_used, kCompute * (x + 1), ws);
+        store_q(sm, qr, lane);
+        if (lane == 0) lds_set(&sm.q_seq, x + 2);
+        if (x + 3 < P) load_q(qr, s, q, b, x + 3, lane);
+      };
+      for (int x = 0; x + 1 < P; x += 2) {
+        stage(x, qa);
+        if (x + 2 < P) stage(x + 1, qb);
+      }
+      return;
     }
-    if (cw + 1 < P) load_q(qn, s, q, b, cw + 1, lane);
+    // The lse wave takes the problems in order: merges the die partials of
+    // x into the row lse and stages it.
     const unsigned dies = prompt_dies(c_lo, n_c);
     // The last of the prompt's blocks to read the die partials of x empties
-    // them (64 lanes x 16 bytes: all eight dies) and the count.
-    uint32_t pend = 0u;
-    int px = -1;
+    // them (64 lanes x 16 bytes: all eight dies) and the count. A reader
+    // learns that it was the last from an atomic whose result it looks at
+    // two problems later (it comes back behind the block's K loads).
+    uint32_t pend1 = 0u, pend2 = 0u;
     auto last_reader = [&](int x, uint32_t v) {
       if (x < 0 || __builtin_amdgcn_readfirstlane(v) != (uint32_t)n_c - 1u) return;
       uint32_t *dp = ws.dslot + die_slot(x, bb, 0) + 4 * lane;
@@ -449,35 +468,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
       for (int e = 0; e < 4; ++e) post(dp + e, 0u);
       if (lane == 0) post(ws.readers + (int64_t)x * SP_MAX_PROMPTS + bb, 0u);
     };
-    for (int x = cw; x < P; x += kControl) {
-      lds_wait_ge(&sm.stats_cnt, kCompute * (x + 1), ws);
-      if (x + 1 < P) {
-        lds_wait_ge(&sm.q_used, kCompute * (x + 1), ws);   // Q(x) read by all
-        store_q(sm, qn, lane);
-        if (lane == 0) lds_set(&sm.q_seq, x + 2);
-      }
-      last_reader(px, pend);
-      px = -1;
+    for (int x = 0; x < P; ++x) {
+      lds_wait_ge(&sm.stats_cnt, kCompute * (x + 1), ws);   // our own partial of x is out
+      last_reader(x - 2, pend2);
+      pend2 = pend1;
       const f32x4 lq = gather_dies(ws, x, bb, dies, lane);
-      // The Q prefetch goes out after the gather's loads, so its waits do
-      // not include it.
-      if (x + 1 + kControl < P) load_q(qn, s, q, b, x + 1 + kControl, lane);
-      if (x >= 2) lds_wait_ge(&sm.lse_used, kCompute * (x - 1), ws);   // slot is free
-      if (lane < 8) *reinterpret_cast<f32x4 *>(&sm.lse[x & 1][4 * lane]) = lq;
-      if (lane == 0) lds_set(&sm.lse_ready[x & 1], x + 1);
+      // The slot held lse(x - kLag): free once every compute wave folded it.
+      if (x >= kLag) lds_wait_ge(&sm.lse_used, kCompute * (x - kLag + 1), ws);
+      if (lane < 8) *reinterpret_cast<f32x4 *>(&sm.lse[x % kLag][4 * lane]) = lq;
+      if (lane == 0) lds_set(&sm.lse_ready[x % kLag], x + 1);
       // The merge block of our group has read our partial of x.
       if (lane < kRows) {
         ws.slot[cta_slot(x, cta) + lane] = 0u;
         ws.lslot[cta_slot(x, cta) + lane] = 0u;
       }
-      // Count ourselves as a reader of the die partials of x; the result is
-      // looked at a round later (it comes back behind the block's K loads).
-      pend = lane == 0 ? __hip_atomic_fetch_add(ws.readers + (int64_t)x * SP_MAX_PROMPTS + bb,
-                                                1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                       : 0u;
-      px = x;
+      pend1 = lane == 0 ? __hip_atomic_fetch_add(ws.readers + (int64_t)x * SP_MAX_PROMPTS + bb,
+                                                 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                        : 0u;
     }
-    last_reader(px, pend);
+    last_reader(P - 2, pend2);
+    last_reader(P - 1, pend1);
     return;
   }
 
