@@ -417,9 +417,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
   const int c_lo = tb.cta_off[bb], n_c = tb.cta_off[bb + 1] - c_lo, ci = cta - c_lo;
   const int N = tb.tok_off[bb + 1] - tb.tok_off[bb];
   const int NK = N + s.L;                                   // keys of the prompt
-  const int tiles = (NK + kTile - 1) / kTile;
-  const int ta = (int)((int64_t)tiles * ci / n_c);
-  const int nt = (int)((int64_t)tiles * (ci + 1) / n_c) - ta;
+  // The block's keys: an even share of the prompt's (K bytes are what the
+  // kernel is bound by), in tiles of 32 from its first key; the last tile
+  // may be partial.
+  const int k_lo = (int)((int64_t)NK * ci / n_c), k_hi = (int)((int64_t)NK * (ci + 1) / n_c);
+  const int nt = (k_hi - k_lo + kTile - 1) / kTile;
   const int64_t key0 = (int64_t)tb.tok_off[bb] + (int64_t)b * s.L;
 
   if (control) {
@@ -492,26 +494,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
   }
 
   // ---------------- compute waves ----------------
-  const int w_t0 = ta + (nt * wave) / kCompute;
-  const int w_nt = ta + (nt * (wave + 1)) / kCompute - w_t0;
+  const int w_t0 = (nt * wave) / kCompute;   // the wave's first tile within the block
+  const int w_nt = (nt * (wave + 1)) / kCompute - w_t0;
+  const int w_k0 = k_lo + w_t0 * kTile;                  // the wave's keys: [w_k0, w_k1)
+  const int w_k1 = min(w_k0 + w_nt * kTile, k_hi);
   const int rows = s.L * s.G;
   const bool row_ok = r < rows;
   const int jr = row_ok ? r / s.G : 0;
   const float sl2 = s.scale_log2;
   // K addressing: a per-problem base pointer plus a 32-bit per-lane element
-  // offset of each tile's key row (clamped into the prompt; keys outside the
-  // wave's tiles are masked later). Loads are unconditional, which keeps
-  // the compiler's wait counts exact: a tile's MFMAs wait for its loads only.
+  // offset of each tile's key row (rows past the wave's keys read its last
+  // key again, so they cost no traffic, and are masked later). Loads are
+  // unconditional, which keeps the compiler's wait counts exact: a tile's
+  // MFMAs wait for its loads only.
   const int64_t kstride_l = total_keys * s.Hkv * D;   // elements per layer
   uint32_t koff[kTPW];
 #pragma unroll
   for (int t = 0; t < kTPW; ++t) {
-    const int key = min((w_t0 + t) * kTile + r, NK - 1);
+    const int key = min(w_k0 + t * kTile + r, max(w_k1, k_lo + 1) - 1);
     koff[t] = (uint32_t)((int64_t)key * s.Hkv * D) + 8u * half;
   }
   const __bf16 *kprompt = k + key0 * s.Hkv * D;
-  // A tile is "full" when all its keys are prompt keys: no masking needed.
-  const int full_tiles = max(0, min((N - w_t0 * kTile) / kTile, w_nt));
+  // A tile is "full" when all its keys are the wave's and prompt keys: no
+  // masking needed.
+  const int full_tiles = max(0, min((min(w_k1, N) - w_k0) / kTile, w_nt));
 
   Frag<__bf16, D> kf[kTPW];
   f32x16 E[kTPW], run[kTPW];
@@ -554,11 +560,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
       // after the last tile's MFMAs.
       lds_wait_ge(&sm.q_seq, it + 1, ws);
       // Base of the next problem's K. After the last problem the loads
-      // (unconditional, see above) go to the prompt's first 96 keys, which
-      // every wave of the prompt shares, instead of a whole problem again.
+      // (unconditional, see above) go to the prompt's first keys (every row
+      // offset is at least k_lo), which all blocks of the prompt share,
+      // instead of a whole problem again.
       if (it + 1 < P && ++gn == s.Hkv) { gn = 0; ++ln; }
       const __bf16 *kb_next = it + 1 < P ? kprompt + ln * kstride_l + gn * D
-                                         : kprompt - (int64_t)w_t0 * kTile * s.Hkv * D;
+                                         : kprompt - (int64_t)k_lo * s.Hkv * D;
       float m = -INFINITY, z = 0.f;    // base-2 running max and sum of this lane's keys
 #pragma unroll
       for (int t = 0; t < kTPW; ++t) {
@@ -594,8 +601,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
           float mt = -INFINITY;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = (w_t0 + t) * kTile + acc_row(i, half);
-            const bool ok = row_ok && t < w_nt && key <= N + jr;   // causal; implies key < NK
+            const int key = w_k0 + t * kTile + acc_row(i, half);
+            const bool ok = row_ok && key < w_k1 && key <= N + jr;   // causal: key < NK
             x[i] = ok ? x[i] * sl2 : -INFINITY;
             mt = fmaxf(mt, x[i]);
           }
@@ -608,7 +615,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
           for (int i = 0; i < 16; ++i) {
             const float e = x[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[i] - m);
             z += e;
-            const int key = (w_t0 + t) * kTile + acc_row(i, half);
+            const int key = w_k0 + t * kTile + acc_row(i, half);
             E[t][i] = key < N ? e : 0.f;    // lookahead keys get no importance
           }
         }
@@ -686,8 +693,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
     float v = run[t][0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) v = r == i ? run[t][i] : v;
-    const int key = (w_t0 + t) * kTile + acc_row(r & 15, half);
-    if (r < 16 && t < w_nt && key < N) out[key] = v * inv_l;
+    const int key = w_k0 + t * kTile + acc_row(r & 15, half);
+    if (r < 16 && key < w_k1 && key < N) out[key] = v * inv_l;
   }
 }
 
