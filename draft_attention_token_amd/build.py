@@ -1,4 +1,6 @@
-"""Build libspecprefill.so for gfx950 with hipcc (in-tree).
+"""Build libspecprefill.so for gfx950 with hipcc (in-tree), and the small
+measurement library libspbench.so (a plain streaming read) that bench.py
+uses next to it.
 
 Usage: python -m draft_attention_token_amd.build
 """
@@ -15,6 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libspecprefill.so")
+BENCH_SRC = os.path.join(PKG, "bench", "read_peak.hip")
+BENCH_OUT = os.path.join(PKG, "libspbench.so")
 OBJDIR = os.path.join(PKG, "_build")
 
 ARCH = os.environ.get("SP_OFFLOAD_ARCH", "gfx950")
@@ -46,20 +50,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link the shared library. Always rebuilds."""
-    os.makedirs(OBJDIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = OUT + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link the shared libraries. Always rebuilds."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+        bench_obj = ex.submit(_compile, BENCH_SRC)
+        objs = list(ex.map(_compile, srcs))
+        bench_obj = bench_obj.result()
+    _link(objs, OUT)
+    _link([bench_obj], BENCH_OUT)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {BENCH_OUT}")
     return OUT
 
 
