@@ -12,6 +12,7 @@ the 8 TB/s peak, and the CPU oracle timed on the host as a baseline.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -28,7 +29,7 @@ HBM_PEAK_GBS = 8000.0
 # HBM traffic of the scoring kernel from hardware counters (two rocprofv3 --pmc
 # passes, FETCH_SIZE and WRITE_SIZE, scaled by a copy of known size). Valid
 # only for the kernel sources it was measured on.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_stream_n128k_traffic.md")
+TRAFFIC_FILES = os.path.join(ROOT, "profiles", "k_stream_*_traffic.md")
 KERNEL_SOURCES = ("draft_attention_token_amd/csrc/score_stream.hip",
                   "draft_attention_token_amd/csrc/score_common.h")
 COPY_BYTES = 1 << 30
@@ -49,17 +50,16 @@ def kernel_source_hash() -> str:
 def measured_traffic(workload: str):
     """Bytes per scoring launch from the committed counter summary, or None if
     it is missing, covers another workload or older kernel sources."""
-    try:
-        text = open(TRAFFIC_FILE).read()
-    except OSError:
-        return None
-    fields = dict(re.findall(r"^- (\w+): (\S+)$", text, re.M))
-    if fields.get("workload") != workload or fields.get("source_hash") != kernel_source_hash():
-        return None
-    try:
-        return float(fields["bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+    for path in sorted(glob.glob(TRAFFIC_FILES)):
+        with open(path) as fh:
+            fields = dict(re.findall(r"^- (\w+): (\S+)$", fh.read(), re.M))
+        if fields.get("workload") != workload or fields.get("source_hash") != kernel_source_hash():
+            continue
+        try:
+            return float(fields["bytes_per_launch"])
+        except (KeyError, ValueError):
+            return None
+    return None
 
 
 def copy_calibration():
@@ -177,7 +177,8 @@ def main():
     pipe = sp.Pipeline(inp.offsets, w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim,
                        w.n_lookahead, w.dtype, dev, W=w.pool_window, C=w.chunk_size,
                        normalize=w.normalize, boost=w.boost, mode=mode, param=param,
-                       algo=args.algo)
+                       algo=args.algo, k_dtype=inp.k.dtype, k_scales=inp.k_scales)
+    fp8k = inp.k.dtype == torch.float8_e4m3fn
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         pipe.run(q, k, ids)
@@ -242,10 +243,13 @@ def main():
                    "lookahead": w.n_lookahead, "layers": w.n_layers, "q_heads": w.n_q_heads,
                    "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "pool_window": w.pool_window,
                    "chunk": w.chunk_size, "normalize": w.normalize, "boost": w.boost,
-                   "select": f"{mode} {param}", "score_algo": args.algo, "kept_tokens": kept},
+                   "select": f"{mode} {param}", "score_algo": args.algo, "kept_tokens": kept,
+                   "k_cache": "fp8 e4m3 codes, fp32 scale per (layer, KV head)" if fp8k
+                   else "same type as Q"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "k_stream<128> (sp_score_attention)", "launch_us": ms_score * 1e3,
+                     "kernel": f"k_stream<{w.head_dim}, fp8 K={fp8k}> (sp_score_attention)",
+                     "launch_us": ms_score * 1e3,
                      "algorithmic_bytes": alg_bytes,
                      "achievable": {"read": read_gbs, "frac": achieved / read_gbs,
                                     "kernel": f"k_read, plain streaming read of 1 GiB, "

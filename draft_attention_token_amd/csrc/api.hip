@@ -76,12 +76,17 @@ sp_status check_attn(const sp_attn_desc *d, AttnShape *s) {
   if (d->n_layers < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->n_lookahead < 1)
     return SP_ERR_INVALID_ARGUMENT;
   if (d->n_q_heads % d->n_kv_heads != 0) return SP_ERR_INVALID_ARGUMENT;
-  if (d->dtype != SP_DTYPE_F32 && d->dtype != SP_DTYPE_BF16) return SP_ERR_INVALID_ARGUMENT;
+  if (d->dtype != SP_DTYPE_F32 && d->dtype != SP_DTYPE_BF16 && d->dtype != SP_DTYPE_BF16_FP8K)
+    return SP_ERR_INVALID_ARGUMENT;
   if (!(isfinite(d->scale))) return SP_ERR_INVALID_ARGUMENT;
   if (d->algo < SP_SCORE_AUTO || d->algo > SP_SCORE_STREAM) return SP_ERR_INVALID_ARGUMENT;
   if (d->head_dim != 64 && d->head_dim != 128) return SP_ERR_UNSUPPORTED;
   const int G = d->n_q_heads / d->n_kv_heads;
   if ((int64_t)d->n_lookahead * G > kRows) return SP_ERR_UNSUPPORTED;
+  if (d->dtype == SP_DTYPE_BF16_FP8K) {
+    if (d->algo == SP_SCORE_TWO_PASS) return SP_ERR_UNSUPPORTED;   // single-pass only
+    if ((int64_t)d->n_layers * d->n_kv_heads > kMaxScaledProblems) return SP_ERR_UNSUPPORTED;
+  }
   s->n_layers = d->n_layers;
   s->Hq = d->n_q_heads;
   s->Hkv = d->n_kv_heads;
@@ -179,16 +184,28 @@ sp_status sp_score_attention(const sp_attn_desc *desc, const sp_batch *batch, co
   if ((st = check_batch(batch, &total)) != SP_OK) return st;
   if (!q || !k || !importance) return SP_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(ws)) return SP_ERR_INVALID_ARGUMENT;
+  KScales ks;
+  const bool f8 = s.dtype == SP_DTYPE_BF16_FP8K;
+  if (f8) {
+    if (!desc->k_scales) return SP_ERR_INVALID_ARGUMENT;
+    const int P = s.n_layers * s.Hkv;
+    for (int x = 0; x < P; ++x) {
+      const float v = desc->k_scales[x];
+      if (!(v > 0.f) || !isfinite(v)) return SP_ERR_INVALID_ARGUMENT;
+      ks.v[x] = v;
+    }
+  }
   const SegTable tiles = make_table(batch, s.L, kTile, s.L);
   const int total_tiles = tiles.unit_off[tiles.B];
   if (!ws || ws_bytes < score_ws_bytes(s, tiles)) return SP_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  if (desc->algo == SP_SCORE_STREAM && !score_stream_supported(s)) return SP_ERR_UNSUPPORTED;
+  if ((desc->algo == SP_SCORE_STREAM || f8) && !score_stream_supported(s))
+    return SP_ERR_UNSUPPORTED;
   if (desc->algo != SP_SCORE_TWO_PASS) {
     bool supported = false;
-    const hipError_t e = launch_score_stream(s, tiles, q, k, importance, ws, hs, &supported);
+    const hipError_t e = launch_score_stream(s, tiles, q, k, ks, importance, ws, hs, &supported);
     if (supported) return launched(e);
-    if (desc->algo == SP_SCORE_STREAM) return SP_ERR_UNSUPPORTED;
+    if (desc->algo == SP_SCORE_STREAM || f8) return SP_ERR_UNSUPPORTED;
   }
   char *region = reinterpret_cast<char *>(ws) + kStatusBytes + score_stream_slot_bytes(s);
   return launched(launch_score_two_pass(s, tiles, total_tiles, q, k, importance,

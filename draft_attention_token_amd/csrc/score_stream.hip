@@ -381,12 +381,16 @@ __device__ __forceinline__ void butterfly_level(f32x16 (&run)[kTPW], bool use_ma
     }
 }
 
-template <int D>
+// kF8: K holds fp8 e4m3 codes, key value = kscale[problem] * code; each code
+// becomes a bf16 exactly (v_cvt_scalef32_pk_bf16_fp8 with scale 1) and the
+// scale joins the logit scale of its problem.
+template <int D, bool kF8>
 __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable tb,
                                                         int64_t total_keys,
                                                         const __bf16 *__restrict__ q,
-                                                        const __bf16 *__restrict__ k,
-                                                        float *__restrict__ imp, StreamWs ws) {
+                                                        const uint8_t *__restrict__ k,
+                                                        float *__restrict__ imp, StreamWs ws,
+                                                        KScales ks) {
   __shared__ Smem<D> sm;
   const int cta = blockIdx.x;
   // The wave index is uniform across a wave; saying so keeps every value
@@ -501,25 +505,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
   const int rows = s.L * s.G;
   const bool row_ok = r < rows;
   const int jr = row_ok ? r / s.G : 0;
-  const float sl2 = s.scale_log2;
-  // K addressing: a per-problem base pointer plus a 32-bit per-lane element
+  // K addressing: a per-problem base pointer plus a 32-bit per-lane byte
   // offset of each tile's key row (rows past the wave's keys read its last
   // key again, so they cost no traffic, and are masked later). Loads are
   // unconditional, which keeps the compiler's wait counts exact: a tile's
   // MFMAs wait for its loads only.
-  const int64_t kstride_l = total_keys * s.Hkv * D;   // elements per layer
+  // Element layout of the MFMA k-steps (Q in LDS follows the same one):
+  //  bf16: step st, half h takes d in [16 st + 8 h, + 8): the lane's loads
+  //        are 16 bytes at 32-byte strides;
+  //  fp8:  step st, half h takes d in [h D / 2 + 8 st, + 8): the lane reads
+  //        its half of the row as D / 32 contiguous 16-byte loads, two steps
+  //        per load.
+  constexpr int kES = kF8 ? 1 : 2;                  // bytes per K element
+  constexpr int kSteps = D / 16;
+  constexpr int kLoads = kF8 ? D / 32 : D / 16;     // 16-byte loads per lane and tile
+  const int64_t rowb = (int64_t)s.Hkv * D * kES;    // bytes per key row
+  const int64_t kstride_l = total_keys * rowb;      // bytes per layer
   uint32_t koff[kTPW];
 #pragma unroll
   for (int t = 0; t < kTPW; ++t) {
     const int key = min(w_k0 + t * kTile + r, max(w_k1, k_lo + 1) - 1);
-    koff[t] = (uint32_t)((int64_t)key * s.Hkv * D) + 8u * half;
+    koff[t] = (uint32_t)((int64_t)key * rowb) + (uint32_t)(kF8 ? half * (D / 2) : 16 * half);
   }
-  const __bf16 *kprompt = k + key0 * s.Hkv * D;
+  const uint8_t *kprompt = k + key0 * rowb;
   // A tile is "full" when all its keys are the wave's and prompt keys: no
   // masking needed.
   const int full_tiles = max(0, min((min(w_k1, N) - w_k0) / kTile, w_nt));
 
-  Frag<__bf16, D> kf[kTPW];
+  u32x4 kf[kTPW][kLoads];
   f32x16 E[kTPW], run[kTPW];
 #pragma unroll
   for (int t = 0; t < kTPW; ++t) run[t] = f32x16{};
@@ -535,17 +548,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
   // the tile's 32 key rows, so four consecutive instructions share every
   // 128-byte line; a streaming (non-temporal) hint lets the line go between
   // them and costs a refetch each time.
-  auto load_k = [&](const __bf16 *kb, int t) {
+  auto load_k = [&](const uint8_t *kb, int t) {
     const u32x4 *p = reinterpret_cast<const u32x4 *>(kb + koff[t]);
 #pragma unroll
-    for (int st = 0; st < Frag<__bf16, D>::kSteps; ++st)
-      kf[t].v[st] = p[2 * st];
+    for (int i = 0; i < kLoads; ++i) kf[t][i] = p[kF8 ? i : 2 * i];
+  };
+  // The A operand (8 bf16 of the lane's key row) of k-step st of tile t.
+  auto k_operand = [&](int t, int st) -> bf16x8 {
+    if constexpr (!kF8) {
+      return __builtin_bit_cast(bf16x8, kf[t][st]);
+    } else {
+      const u32x4 w = kf[t][st / 2];
+      const uint32_t lo = w[2 * (st % 2)], hi = w[2 * (st % 2) + 1];
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false);
+      const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true);
+      const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false);
+      const bf16x2 d2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true);
+      return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d2[0], d2[1]};
+    }
   };
 
 #pragma unroll
   for (int t = 0; t < kTPW; ++t) load_k(kprompt, t);
 
-  const u32x4 *qs = reinterpret_cast<const u32x4 *>(&sm.q[r][0]) + half;
+  const u32x4 *qs = reinterpret_cast<const u32x4 *>(&sm.q[r][0]) + (kF8 ? half * (D / 16) : half);
   int ln = 0, gn = 0;     // (layer, group) of the next problem to load
 
   for (int it = 0; it < P + kLag; ++it) {
@@ -564,21 +591,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
       // offset is at least k_lo), which all blocks of the prompt share,
       // instead of a whole problem again.
       if (it + 1 < P && ++gn == s.Hkv) { gn = 0; ++ln; }
-      const __bf16 *kb_next = it + 1 < P ? kprompt + ln * kstride_l + gn * D
-                                         : kprompt - (int64_t)k_lo * s.Hkv * D;
+      const uint8_t *kb_next = it + 1 < P ? kprompt + ln * kstride_l + gn * D * kES
+                                          : kprompt - (int64_t)k_lo * rowb;
+      const float sl2 = kF8 ? s.scale_log2 * ks.v[it] : s.scale_log2;
       float m = -INFINITY, z = 0.f;    // base-2 running max and sum of this lane's keys
 #pragma unroll
       for (int t = 0; t < kTPW; ++t) {
         asm volatile("" ::: "memory");   // keep the Q reads inside the tile
         f32x16 x = {};
 #pragma unroll
-        for (int st = 0; st < Frag<__bf16, D>::kSteps; ++st)
-          x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[t].v[st]),
-                                                     __builtin_bit_cast(bf16x8, qs[2 * st]), x, 0,
-                                                     0, 0);
+        for (int st = 0; st < kSteps; ++st)
+          x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              k_operand(t, st), __builtin_bit_cast(bf16x8, qs[kF8 ? st : 2 * st]), x, 0, 0, 0);
         if (t == kTPW - 1 && lane == 0) lds_inc(&sm.q_used);
-        // The tile's registers take the next problem's K at once: the K
-        // stream runs ahead by one problem.
+        // The previous tile's registers take the next problem's K (the
+        // wave's last tile after the post): about two thirds of a problem
+        // of K in flight per block.
         __builtin_amdgcn_sched_barrier(0);
         if (t > 0) load_k(kb_next, t - 1);
         if (t < full_tiles) {
@@ -713,10 +741,10 @@ const DeviceInfo &device_info() {
   if (!done[dev]) {
     DeviceInfo d;
     if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.occ64, k_stream<64>, kThreads, 0) !=
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.occ64, k_stream<64, false>, kThreads, 0) !=
             hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.occ128, k_stream<128>, kThreads, 0) !=
-            hipSuccess)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.occ128, k_stream<128, false>, kThreads,
+                                                     0) != hipSuccess)
       d = DeviceInfo();
     info[dev] = d;
     done[dev] = true;
@@ -807,7 +835,7 @@ size_t die_region(const AttnShape &s) {
 }  // namespace
 
 bool score_stream_supported(const AttnShape &s) {
-  if (s.dtype != SP_DTYPE_BF16) return false;
+  if (s.dtype != SP_DTYPE_BF16 && s.dtype != SP_DTYPE_BF16_FP8K) return false;
   if (s.G & (s.G - 1)) return false;                 // head groups of 2^k lanes
   return true;
 }
@@ -818,8 +846,8 @@ size_t score_stream_slot_bytes(const AttnShape &s) {
 }
 
 hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const void *q,
-                               const void *k, float *imp, void *ws, hipStream_t st,
-                               bool *supported) {
+                               const void *k, const KScales &ks, float *imp, void *ws,
+                               hipStream_t st, bool *supported) {
   *supported = false;
   if (!score_stream_supported(s)) return hipSuccess;
   const int n_stream = stream_ctas(s);
@@ -838,14 +866,13 @@ hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const 
   w.call_tag = reserve_tags(1);
   const int64_t total_keys = (int64_t)tiles.tok_off[tiles.B] + (int64_t)tiles.B * tiles.L;
   const __bf16 *qp = reinterpret_cast<const __bf16 *>(q);
-  const __bf16 *kp = reinterpret_cast<const __bf16 *>(k);
+  const uint8_t *kp = reinterpret_cast<const uint8_t *>(k);
+  const bool f8 = s.dtype == SP_DTYPE_BF16_FP8K;
   for (int li = 0; li < plan.n_launch; ++li) {
-    if (s.d == 128)
-      hipLaunchKernelGGL(k_stream<128>, dim3(plan.grid[li]), dim3(kThreads), 0, st, s, plan.t[li],
-                         total_keys, qp, kp, imp, w);
-    else
-      hipLaunchKernelGGL(k_stream<64>, dim3(plan.grid[li]), dim3(kThreads), 0, st, s, plan.t[li],
-                         total_keys, qp, kp, imp, w);
+    auto kern = s.d == 128 ? (f8 ? k_stream<128, true> : k_stream<128, false>)
+                           : (f8 ? k_stream<64, true> : k_stream<64, false>);
+    hipLaunchKernelGGL(kern, dim3(plan.grid[li]), dim3(kThreads), 0, st, s, plan.t[li], total_keys,
+                       qp, kp, imp, w, ks);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

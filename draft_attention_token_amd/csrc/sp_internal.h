@@ -59,11 +59,17 @@ size_t score_two_pass_region_bytes(const AttnShape &s, int B, int total_tiles);
 
 bool score_stream_supported(const AttnShape &s);
 size_t score_stream_slot_bytes(const AttnShape &s);
+// Per-problem multipliers of the logit scale for fp8 K (problem x = layer *
+// Hkv + group); unused for other K types.
+constexpr int kMaxScaledProblems = 128;
+struct KScales {
+  float v[kMaxScaledProblems];
+};
 // Sets *supported = false (and launches nothing) when the device or the
 // batch does not fit the kernel.
 hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const void *q,
-                               const void *k, float *imp, void *ws, hipStream_t st,
-                               bool *supported);
+                               const void *k, const KScales &ks, float *imp, void *ws,
+                               hipStream_t st, bool *supported);
 
 struct PoolParams {
   int W, C, normalize, first_n, last_n;

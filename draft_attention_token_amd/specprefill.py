@@ -28,7 +28,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspecprefill.so")
 
 SP_OK, SP_ERR_INVALID_ARGUMENT, SP_ERR_UNSUPPORTED, SP_ERR_WORKSPACE_TOO_SMALL, SP_ERR_DEVICE = range(5)
-SP_DTYPE_F32, SP_DTYPE_BF16 = 0, 1
+SP_DTYPE_F32, SP_DTYPE_BF16, SP_DTYPE_BF16_FP8K = 0, 1, 2
 SP_SELECT_TOP_P, SP_SELECT_MASS = 0, 1
 SP_SCORE_AUTO, SP_SCORE_TWO_PASS, SP_SCORE_STREAM = 0, 1, 2
 SP_MAX_PROMPTS = 128
@@ -57,7 +57,8 @@ class sp_attn_desc(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("n_lookahead", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("algo", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("algo", ctypes.c_int32),
+                ("k_scales", ctypes.POINTER(ctypes.c_float))]
 
 
 class sp_pool_desc(ctypes.Structure):
@@ -148,12 +149,27 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 
 
 def attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype, scale=None,
-              algo="auto") -> sp_attn_desc:
-    dt = {torch.float32: SP_DTYPE_F32, torch.bfloat16: SP_DTYPE_BF16}.get(dtype, -1)
+              algo="auto", k_dtype=None, k_scales=None) -> sp_attn_desc:
+    """dtype: Q's torch dtype (and K's unless k_dtype says otherwise).
+    k_dtype=torch.float8_e4m3fn with bf16 Q selects fp8 K codes; k_scales
+    is then the [n_layers * n_kv_heads] fp32 host array of key scales."""
+    if k_dtype is None or k_dtype == dtype:
+        dt = {torch.float32: SP_DTYPE_F32, torch.bfloat16: SP_DTYPE_BF16}.get(dtype, -1)
+    elif dtype == torch.bfloat16 and k_dtype == torch.float8_e4m3fn:
+        dt = SP_DTYPE_BF16_FP8K
+    else:
+        dt = -1
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
-    return sp_attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dt, float(scale),
-                        _ALGOS[algo] if isinstance(algo, str) else int(algo))
+    desc = sp_attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dt, float(scale),
+                        _ALGOS[algo] if isinstance(algo, str) else int(algo), None)
+    if k_scales is not None:
+        ks = np.ascontiguousarray(np.asarray(
+            k_scales.cpu() if isinstance(k_scales, torch.Tensor) else k_scales,
+            dtype=np.float32).reshape(-1))
+        desc._k_scales = ks   # the descriptor points into it: keep it alive with the descriptor
+        desc.k_scales = ks.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    return desc
 
 
 def pool_desc(W=13, C=32, normalize=True, first_n=64, first_mult=1.5, last_n=128,
@@ -192,14 +208,17 @@ def gather_workspace_bytes(batch: Batch, C: int) -> int:
 def sp_score_attention(q: torch.Tensor, k: torch.Tensor, offsets, n_layers: int, n_q_heads: int,
                        n_kv_heads: int, head_dim: int, n_lookahead: int, scale=None,
                        algo="auto", out: Optional[torch.Tensor] = None,
-                       ws: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Token importance [sum N_b] fp32 (see the C header for layouts)."""
+                       ws: Optional[torch.Tensor] = None, k_scales=None) -> torch.Tensor:
+    """Token importance [sum N_b] fp32 (see the C header for layouts). K may
+    be fp8 e4m3 codes with bf16 Q; k_scales ([n_layers * n_kv_heads]) then
+    gives each (layer, KV head)'s key scale."""
     batch = offsets if isinstance(offsets, Batch) else Batch(offsets)
-    desc = attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, q.dtype, scale, algo)
+    desc = attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, q.dtype, scale, algo,
+                     k_dtype=k.dtype, k_scales=k_scales)
     if not (q.is_contiguous() and k.is_contiguous()):
         raise ValueError("q and k must be contiguous")
-    if q.dtype != k.dtype:
-        raise ValueError("q and k must share a dtype")
+    if q.dtype != k.dtype and not (q.dtype == torch.bfloat16 and k.dtype == torch.float8_e4m3fn):
+        raise ValueError("q and k must share a dtype (or be bf16 Q with fp8 e4m3 K)")
     if q.numel() != batch.B * n_layers * n_lookahead * n_q_heads * head_dim:
         raise ValueError("q has the wrong number of elements")
     if k.numel() != n_layers * (batch.total + batch.B * n_lookahead) * n_kv_heads * head_dim:
@@ -298,11 +317,11 @@ class Pipeline:
 
     def __init__(self, offsets, n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype,
                  device, W=13, C=32, normalize=True, boost=True, mode="mass", param=0.85,
-                 algo="auto", scale=None, token_scores=True):
+                 algo="auto", scale=None, token_scores=True, k_dtype=None, k_scales=None):
         self.batch = offsets if isinstance(offsets, Batch) else Batch(offsets)
         fm, lm = (1.5, 1.3) if boost else (1.0, 1.0)
         self.adesc = attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype,
-                               scale, algo)
+                               scale, algo, k_dtype=k_dtype, k_scales=k_scales)
         self.pdesc = pool_desc(W, C, normalize, 64, fm, 128, lm)
         self.C, self.mode, self.param = C, _MODES[mode], float(param)
         self.shape = (n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead)

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SP_ABI_VERSION 1
+#define SP_ABI_VERSION 2
 #define SP_MAX_PROMPTS 128          /* prompts per batch */
 #define SP_MAX_CHUNKS_PER_PROMPT 16384
 
@@ -64,7 +64,13 @@ typedef enum {
   SP_ERR_DEVICE = 4
 } sp_status;
 
-typedef enum { SP_DTYPE_F32 = 0, SP_DTYPE_BF16 = 1 } sp_dtype;
+/* Element types of Q and K. SP_DTYPE_BF16_FP8K: Q bf16, K fp8 e4m3 codes
+ * (OCP E4M3FN: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, max 448) with one fp32 scale per (layer, KV head): the key
+ * value is k_scales[layer * n_kv_heads + kv_head] * code (a quantised draft
+ * K cache: the [PR] discussion runs the draft model's K cache in an 8-bit
+ * type through the draft KV-type options). */
+typedef enum { SP_DTYPE_F32 = 0, SP_DTYPE_BF16 = 1, SP_DTYPE_BF16_FP8K = 2 } sp_dtype;
 
 typedef enum { SP_SELECT_TOP_P = 0, SP_SELECT_MASS = 1 } sp_select_mode;
 
@@ -93,6 +99,9 @@ typedef struct {
   int32_t dtype;        /* sp_dtype of Q and K */
   float scale;          /* logit scale, usually 1 / sqrt(d) */
   int32_t algo;         /* sp_score_algo */
+  const float *k_scales; /* host, [n_layers * n_kv_heads], finite and > 0:
+                            SP_DTYPE_BF16_FP8K only (n_layers * n_kv_heads
+                            <= 128); NULL otherwise */
 } sp_attn_desc;
 
 /* Smoothing, normalisation, boosts and chunking ([PR] Approach step 3;
@@ -128,8 +137,11 @@ sp_status sp_gather_workspace_bytes(const sp_batch *batch, int32_t chunk_size, s
  * head h / G. Only the prompt columns go forward ([G] capture callback).
  *   importance[b][k] = (1/L) * sum_j max_{l, h} p[b][l][j][h][k],  k < N_b
  *
- *   q:  [B][n_layers][L][Hq][d] of dtype, contiguous.
- *   k:  [n_layers][sum_b (N_b + L)][Hkv][d] of dtype, contiguous; prompt b's
+ *   q:  [B][n_layers][L][Hq][d] of dtype (bf16 for SP_DTYPE_BF16_FP8K),
+ *       contiguous.
+ *   k:  [n_layers][sum_b (N_b + L)][Hkv][d] of dtype (one byte per code for
+ *       SP_DTYPE_BF16_FP8K, whose logits are scale * k_scales[l * Hkv + g] *
+ *       <q, code>; single-pass kernel only), contiguous; prompt b's
  *       key rows start at token_offsets[b] + b * L: its N_b prompt keys, then
  *       its L lookahead keys.
  *   importance: [sum_b N_b] fp32 out.

@@ -57,10 +57,11 @@ def lib():
         L = ctypes.CDLL(_LIB_PATH)
         L.oracle_softmax_row.argtypes = [ctypes.c_int, _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_double, _fp, _fp,
-                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp]
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp,
+                                         _dp]
         L.oracle_importance.argtypes = [ctypes.c_int, _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_int, ctypes.c_double, _fp, _fp, _dp,
-                                        ctypes.c_int]
+                                        ctypes.c_int, _dp]
         L.oracle_pool_chunk.argtypes = [ctypes.c_int64, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double,
                                         _dp, _dp]
@@ -86,7 +87,7 @@ def max_threads() -> int:
 
 
 def _as_f32(x) -> np.ndarray:
-    """Widen Q/K to a contiguous fp32 numpy array (exact for bf16 input)."""
+    """Widen Q/K to a contiguous fp32 numpy array (exact for bf16 and fp8 input)."""
     try:
         import torch
         if isinstance(x, torch.Tensor):
@@ -96,29 +97,52 @@ def _as_f32(x) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
 
 
-def softmax_row(offsets, q, k, n_layers, Hq, Hkv, d, L, scale, b, l, j, h) -> np.ndarray:
-    """Softmax probabilities of query (b, l, j, h) over its N_b + j + 1 visible keys."""
+def _scales(k_scales, n):
+    """Key scales as an fp64 array of n values, or None (keys are values)."""
+    if k_scales is None:
+        return None
+    try:
+        import torch
+        if isinstance(k_scales, torch.Tensor):
+            k_scales = k_scales.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    ks = np.ascontiguousarray(np.asarray(k_scales, dtype=np.float64).reshape(-1))
+    assert ks.size == n, "k_scales needs one value per (layer, KV head)"
+    return ks
+
+
+def softmax_row(offsets, q, k, n_layers, Hq, Hkv, d, L, scale, b, l, j, h,
+                k_scales=None) -> np.ndarray:
+    """Softmax probabilities of query (b, l, j, h) over its N_b + j + 1 visible
+    keys; with k_scales, K holds codes and key = k_scales[l][g] * code."""
     off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
     qf, kf = _as_f32(q), _as_f32(k)
+    ks = _scales(k_scales, n_layers * Hkv)
     n = int(off[b + 1] - off[b])
     p = np.empty(n + j + 1, dtype=np.float64)
     rc = lib().oracle_softmax_row(len(off) - 1, _ptr(off, _i64p), n_layers, Hq, Hkv, d, L, scale,
-                                  _ptr(qf, _fp), _ptr(kf, _fp), b, l, j, h, _ptr(p, _dp))
+                                  _ptr(qf, _fp), _ptr(kf, _fp), b, l, j, h, _ptr(p, _dp),
+                                  None if ks is None else _ptr(ks, _dp))
     if rc != 0:
         raise ValueError("oracle_softmax_row: bad arguments")
     return p
 
 
-def importance(offsets, q, k, n_layers, Hq, Hkv, d, L, scale, nthreads: int = 0) -> np.ndarray:
-    """Importance of every prompt token, [sum N_b] fp64."""
+def importance(offsets, q, k, n_layers, Hq, Hkv, d, L, scale, nthreads: int = 0,
+               k_scales=None) -> np.ndarray:
+    """Importance of every prompt token, [sum N_b] fp64 (k_scales: see
+    softmax_row)."""
     off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
     qf, kf = _as_f32(q), _as_f32(k)
+    ks = _scales(k_scales, n_layers * Hkv)
     B = len(off) - 1
     assert qf.size == B * n_layers * L * Hq * d, "q has the wrong size"
     assert kf.size == n_layers * (int(off[-1]) + B * L) * Hkv * d, "k has the wrong size"
     imp = np.empty(int(off[-1]), dtype=np.float64)
     rc = lib().oracle_importance(B, _ptr(off, _i64p), n_layers, Hq, Hkv, d, L, scale,
-                                 _ptr(qf, _fp), _ptr(kf, _fp), _ptr(imp, _dp), nthreads)
+                                 _ptr(qf, _fp), _ptr(kf, _fp), _ptr(imp, _dp), nthreads,
+                                 None if ks is None else _ptr(ks, _dp))
     if rc != 0:
         raise ValueError("oracle_importance: bad arguments")
     return imp
@@ -175,7 +199,8 @@ def pipeline(inputs, mode: str = None, param: float = None, nthreads: int = 0, i
         mode, param = w.select
     if imp is None:
         imp = importance(inputs.offsets.numpy(), inputs.q, inputs.k, w.n_layers, w.n_q_heads,
-                         w.n_kv_heads, w.head_dim, w.n_lookahead, inputs.scale, nthreads)
+                         w.n_kv_heads, w.head_dim, w.n_lookahead, inputs.scale, nthreads,
+                         k_scales=inputs.k_scales)
     off = inputs.offsets.numpy()
     ids = inputs.token_ids.numpy()
     fm, lm = (1.5, 1.3) if w.boost else (1.0, 1.0)

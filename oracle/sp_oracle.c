@@ -57,10 +57,15 @@ int oracle_max_threads(void) {
  *
  *   q: [B][layers][L][Hq][d]   k: [layers][sum_b (N_b + L)][Hkv][d]
  *   tok_off: [B + 1]; prompt b's key rows start at tok_off[b] + b * L.
+ *   k_scales: NULL, or [layers][Hkv]: a quantised K cache (the [PR]
+ *   discussion runs the draft's K cache in an 8-bit type) holds codes, and
+ *   the key is k_scales[l][g] * code, so
+ *     s_k = scale * <Q, k_scales[l][h / G] * K_code> = scale * k_scales[l][h / G] * <Q, K_code>.
  */
 int oracle_softmax_row(int B, const int64_t *tok_off, int n_layers, int Hq,
                        int Hkv, int d, int L, double scale, const float *q,
-                       const float *k, int b, int l, int j, int h, double *p) {
+                       const float *k, int b, int l, int j, int h, double *p,
+                       const double *k_scales) {
   if (b < 0 || b >= B || l < 0 || l >= n_layers || j < 0 || j >= L || h < 0 ||
       h >= Hq || Hkv <= 0 || Hq % Hkv != 0)
     return -1;
@@ -70,12 +75,13 @@ int oracle_softmax_row(int B, const int64_t *tok_off, int n_layers, int Hq,
   const int64_t key0 = tok_off[b] + (int64_t)b * L;
   const float *qrow = q + ((((int64_t)b * n_layers + l) * L + j) * Hq + h) * d;
   const int64_t nvis = N + j + 1;
+  const double ks = k_scales ? k_scales[(int64_t)l * Hkv + h / G] : 1.0;
   double m = -INFINITY;
   for (int64_t kk = 0; kk < nvis; kk++) {
     const float *krow = k + (((int64_t)l * total_keys + key0 + kk) * Hkv + h / G) * d;
     double s = 0.0;
     for (int e = 0; e < d; e++) s += (double)qrow[e] * (double)krow[e];
-    s *= scale;
+    s *= scale * ks;
     p[kk] = s;
     if (s > m) m = s;
   }
@@ -103,7 +109,8 @@ int oracle_softmax_row(int B, const int64_t *tok_off, int n_layers, int Hq,
  */
 int oracle_importance(int B, const int64_t *tok_off, int n_layers, int Hq,
                       int Hkv, int d, int L, double scale, const float *q,
-                      const float *k, double *imp, int nthreads) {
+                      const float *k, double *imp, int nthreads,
+                      const double *k_scales) {
   if (B <= 0 || n_layers <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
       d <= 0 || L <= 0)
     return -1;
@@ -132,7 +139,7 @@ int oracle_importance(int B, const int64_t *tok_off, int n_layers, int Hq,
       for (int l = 0; l < n_layers; l++) {
         for (int h = 0; h < Hq; h++) {
           oracle_softmax_row(B, tok_off, n_layers, Hq, Hkv, d, L, scale, q, k,
-                             b, l, j, h, p);
+                             b, l, j, h, p, k_scales);
           for (int64_t kk = 0; kk < N; kk++)  /* prompt columns only */
             if (p[kk] > sm[kk]) sm[kk] = p[kk];
         }

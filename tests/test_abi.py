@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     L = sp.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert L.sp_abi_version() == 1
+    assert L.sp_abi_version() == 2
 
 
 def test_status_strings():
@@ -66,6 +66,35 @@ def _desc(**kw):
 ])
 def test_score_rejects_bad_descriptors(kw, want):
     assert _score(_desc(**kw), sp.Batch([0, 100])) == want
+
+
+def _fp8(**kw):
+    base = dict(dtype=torch.bfloat16, k_dtype=torch.float8_e4m3fn, algo="auto",
+                k_scales=[0.01] * 24)
+    base.update(kw)
+    return _desc(**base)
+
+
+@pytest.mark.parametrize("kw, want", [
+    (dict(k_scales=None), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(k_scales=[0.01] * 23 + [0.0]), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(k_scales=[0.01] * 23 + [-1.0]), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(k_scales=[float("inf")] + [0.01] * 23), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(k_scales=[float("nan")] * 24), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(algo="two_pass"), sp.SP_ERR_UNSUPPORTED),           # fp8 K: single-pass kernel only
+    (dict(n_layers=40, n_kv_heads=4, k_scales=[0.01] * 160), sp.SP_ERR_UNSUPPORTED),  # > 128
+])
+def test_score_rejects_bad_fp8_key_scales(kw, want):
+    assert _score(_fp8(**kw), sp.Batch([0, 100])) == want
+
+
+def test_fp8_descriptor_fields():
+    d = _fp8()
+    assert d.dtype == sp.SP_DTYPE_BF16_FP8K
+    assert [d.k_scales[i] for i in range(24)] == pytest.approx([0.01] * 24)
+    # fp8 Q, or fp8 K under fp32 Q, has no code
+    assert _desc(dtype=torch.float32, k_dtype=torch.float8_e4m3fn).dtype == -1
+    assert _desc(dtype=torch.float8_e4m3fn).dtype == -1
 
 
 @pytest.mark.parametrize("offsets, want", [

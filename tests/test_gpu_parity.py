@@ -32,7 +32,8 @@ def run_gpu(inp, mode, param, algo="auto"):
           f"mode={mode} p={param} algo={algo}", flush=True)
     pipe = sp.Pipeline(inp.offsets, w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim,
                        w.n_lookahead, w.dtype, DEV, W=w.pool_window, C=w.chunk_size,
-                       normalize=w.normalize, boost=w.boost, mode=mode, param=param, algo=algo)
+                       normalize=w.normalize, boost=w.boost, mode=mode, param=param, algo=algo,
+                       k_dtype=inp.k.dtype, k_scales=inp.k_scales)
     q, k, ids = inp.q.to(DEV), inp.k.to(DEV), inp.token_ids.to(DEV)
     pipe.run(q, k, ids)
     torch.cuda.synchronize()
@@ -254,12 +255,34 @@ def test_pool_select_gather_stages_on_oracle_importance():
         c0 += nc
 
 
-@pytest.mark.parametrize("name", ["n32k_bf16", "n128k_bf16", "n128k_diffuse_bf16"])
+FP8K_SMALL = [
+    ("fp8k_d128_g4", "n3212_fp8k", dict(lengths=(1000,))),
+    ("fp8k_d128_ragged", "n3212_fp8k", dict(lengths=(65, 1, 640, 129))),
+    ("fp8k_d64_g8_l4", "n3212_fp8k", dict(lengths=(500,), head_dim=64, n_q_heads=16,
+                                          n_kv_heads=2, n_lookahead=4)),
+    ("fp8k_d128_g1_l1", "n3212_fp8k", dict(lengths=(300, 45), n_q_heads=4, n_kv_heads=4,
+                                           n_lookahead=1)),
+]
+
+
+@pytest.mark.parametrize("name, base, kw", FP8K_SMALL, ids=[s[0] for s in FP8K_SMALL])
+def test_fp8k_small_shapes(name, base, kw):
+    """fp8 e4m3 K codes with per-(layer, KV head) scales, bf16 Q."""
+    w = workloads.small_workload(base, seed=700 + len(name), n_spans=2, **kw)
+    inp = workloads.make_inputs(w)
+    assert inp.k.dtype == torch.float8_e4m3fn and inp.k_scales is not None
+    for mode, param in (("top_p", 0.3), ("mass", 0.85)):
+        pipe = run_gpu(inp, mode, param)
+        compare(inp, pipe, mode, param)
+
+
+@pytest.mark.parametrize("name", ["n32k_bf16", "n128k_bf16", "n128k_diffuse_bf16", "n128k_fp8k"])
 def test_full_size_single_prompt(name):
     w = workloads.WORKLOADS[name]
     inp = workloads.make_inputs(w)
     imp = oracle.importance(inp.offsets.numpy(), inp.q, inp.k, w.n_layers, w.n_q_heads,
-                            w.n_kv_heads, w.head_dim, w.n_lookahead, inp.scale)
+                            w.n_kv_heads, w.head_dim, w.n_lookahead, inp.scale,
+                            k_scales=inp.k_scales)
     for mode, param in (w.select,) + tuple(w.also_select):
         pipe = run_gpu(inp, mode, param)
         ora = oracle.pipeline(inp, mode, param, imp=imp)

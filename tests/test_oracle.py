@@ -170,6 +170,96 @@ def test_importance_prompts_are_independent():
 
 
 # ----------------------------------------------------------------------------
+# Quantised draft keys: fp8 e4m3 codes with a per-(layer, KV head) scale
+# ----------------------------------------------------------------------------
+
+def _e4m3fn_value(code):
+    """OCP 8-bit e4m3 ("fn" variant): sign, 4 exponent bits with bias 7,
+    3 mantissa bits, subnormals at exponent 0, no infinities, S.1111.111 NaN."""
+    sgn = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 7
+    if e == 0xF and m == 7:
+        return float("nan")
+    if e == 0:
+        return sgn * m * 2.0 ** -9
+    return sgn * (1 + m / 8) * 2.0 ** (e - 7)
+
+
+def test_fp8_codes_widen_per_the_format_definition():
+    """The oracle widens K through torch's float8_e4m3fn; every one of the
+    256 codes must give the value the format defines (448 the largest)."""
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn)
+    got = oracle._as_f32(codes).astype(np.float64)
+    want = np.array([_e4m3fn_value(c) for c in range(256)])
+    nan = np.isnan(want)
+    assert nan.sum() == 2 and np.isnan(got[nan]).all()
+    np.testing.assert_array_equal(got[~nan], want[~nan])
+    assert want[0x7E] == 448.0 and want[0x01] == 2.0 ** -9 and want[0x38] == 1.0
+
+
+def _rand_fp8_problem(rng, lengths, n_layers, Hq, Hkv, d, L):
+    off, q, k = _rand_problem(rng, lengths, n_layers, Hq, Hkv, d, L, scale_q=2.0)
+    codes, scales = workloads.quantize_fp8(torch.from_numpy(k))
+    return off, q, codes, scales
+
+
+def test_fp8_importance_matches_bruteforce_on_widened_keys():
+    """Codes with scales equal the brute-force route on keys written out as
+    scale * value(code) (values from the format definition, not torch)."""
+    rng = np.random.default_rng(11)
+    n_layers, Hq, Hkv, d, L = 2, 8, 2, 16, 4
+    off, q, codes, scales = _rand_fp8_problem(rng, [19, 7, 30], n_layers, Hq, Hkv, d, L)
+    table = np.array([_e4m3fn_value(c) for c in range(256)])
+    vals = table[codes.view(torch.uint8).numpy().astype(np.int64)]
+    assert not np.isnan(vals).any()
+    keys = vals * scales.numpy().astype(np.float64)[:, None, :, None]
+    scale = 1 / math.sqrt(d)
+    got = oracle.importance(off, q, codes, n_layers, Hq, Hkv, d, L, scale, k_scales=scales)
+    ref = _importance_bruteforce(off, q, keys, n_layers, Hq, Hkv, d, L, scale)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_fp8_key_scale_is_a_logit_temperature():
+    """Scaling problem (l, g)'s key scale by c scales that problem's logits by c:
+    with one layer and one KV group, that is the plain scale times c."""
+    rng = np.random.default_rng(12)
+    off, q, codes, scales = _rand_fp8_problem(rng, [25, 9], 1, 4, 1, 8, 3)
+    c = 2.0 ** 0.5
+    ks = scales.double().numpy() * c                  # fp64: no rounding of the product
+    a = oracle.importance(off, q, codes, 1, 4, 1, 8, 3, 0.3, k_scales=ks)
+    b = oracle.importance(off, q, codes, 1, 4, 1, 8, 3, 0.3 * c * float(scales[0, 0]))
+    np.testing.assert_allclose(a, b, rtol=1e-12)
+
+
+def test_fp8_unit_scales_equal_plain_keys():
+    """k_scales of one make the codes the keys."""
+    rng = np.random.default_rng(13)
+    off, q, codes, scales = _rand_fp8_problem(rng, [14], 2, 4, 2, 8, 2)
+    ones = np.ones(scales.numel())
+    a = oracle.importance(off, q, codes, 2, 4, 2, 8, 2, 0.25, k_scales=ones)
+    b = oracle.importance(off, q, codes.to(torch.float32), 2, 4, 2, 8, 2, 0.25)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_fp8_scale_index_is_layer_major():
+    """Scale s[l][g] applies to layer l, KV group g only: raising one scale
+    moves that problem's rows and leaves a problem it does not touch alone."""
+    rng = np.random.default_rng(14)
+    n_layers, Hq, Hkv, d, L = 2, 4, 2, 8, 2
+    off, q, codes, scales = _rand_fp8_problem(rng, [12], n_layers, Hq, Hkv, d, L)
+    base = scales.clone()
+    hot = scales.clone()
+    hot[1, 0] *= 3.0                                  # layer 1, group 0
+    for (l, j, h) in itertools.product(range(n_layers), range(L), range(Hq)):
+        p0 = oracle.softmax_row(off, q, codes, n_layers, Hq, Hkv, d, L, 0.3, 0, l, j, h,
+                                k_scales=base)
+        p1 = oracle.softmax_row(off, q, codes, n_layers, Hq, Hkv, d, L, 0.3, 0, l, j, h,
+                                k_scales=hot)
+        touched = l == 1 and h // (Hq // Hkv) == 0
+        assert (np.abs(p0 - p1).max() > 1e-6) == touched, (l, j, h)
+
+
+# ----------------------------------------------------------------------------
 # Pooling, normalisation, boosts, chunk means
 # ----------------------------------------------------------------------------
 

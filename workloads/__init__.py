@@ -14,6 +14,10 @@ so each workload is a seeded draw with the shapes of those runs:
   towards the mean query direction of their KV group, so the draft attends to
   them; they play the role of the needle / evidence chunks.
 * Token ids are uniform in [0, 2**17).
+* Quantised-K workloads (``k_fp8``) store K as fp8 e4m3 codes with one fp32
+  scale per (layer, KV head): scale = max |K| / 448 over that slice (the
+  largest finite e4m3 value), code = K / scale rounded to e4m3. This stands
+  in for a draft model whose K cache is kept in an 8-bit type.
 
 Layouts (all C-contiguous):
 
@@ -32,7 +36,7 @@ from typing import List, Optional
 
 import torch
 
-__all__ = ["Workload", "Inputs", "WORKLOADS", "make_inputs", "small_workload"]
+__all__ = ["Workload", "Inputs", "WORKLOADS", "make_inputs", "small_workload", "quantize_fp8"]
 
 VOCAB = 1 << 17
 
@@ -60,6 +64,7 @@ class Workload:
     also_select: tuple = ()           # further (mode, param) pairs on the same scores
     ragged_count: int = 0             # >0: draw this many lengths log-uniform
     ragged_range: tuple = (2048, 65536)
+    k_fp8: bool = False               # K as fp8 e4m3 codes + per-(layer, KV head) scales
 
     @property
     def group(self) -> int:
@@ -91,6 +96,12 @@ WORKLOADS = {
                               torch.bfloat16, 1500, None, None,
                               select=("top_p", 0.15),
                               also_select=(("mass", 0.85),), ragged_count=16),
+    # The same shapes with K quantised to fp8 e4m3 (Q stays bf16).
+    "n3212_fp8k": Workload("n3212_fp8k", (3212,), 6, 16, 4, 128, 8,
+                           torch.bfloat16, 1002, 5, 2.0, select=("top_p", 0.30),
+                           also_select=(("mass", 0.85),), k_fp8=True),
+    "n128k_fp8k": Workload("n128k_fp8k", (131072,), 6, 16, 4, 128, 8,
+                           torch.bfloat16, 1004, 64, None, k_fp8=True),
 }
 
 
@@ -104,6 +115,7 @@ class Inputs:
     token_ids: torch.Tensor    # [sum N_b] int32
     spans: List[List[int]]     # planted chunk indices per prompt
     strengths: List[List[float]]
+    k_scales: Optional[torch.Tensor] = None   # [layers][Hkv] fp32 when K holds fp8 codes
 
     @property
     def scale(self) -> float:
@@ -149,8 +161,8 @@ def _draw_prompt(w: Workload, n: int, seed: int, k_out: torch.Tensor, q_out: tor
             u = v / v.norm()
             for c, s in zip(spans, strengths):
                 kk[32 * c:32 * c + 32, grp, :] += float(s) * u
-        q_out[layer].copy_(q.to(w.dtype))
-        k_out[layer].copy_(kk.to(w.dtype))
+        q_out[layer].copy_(q.to(q_out.dtype))
+        k_out[layer].copy_(kk.to(k_out.dtype))
     ids = torch.randint(0, VOCAB, (n,), generator=g, dtype=torch.int64).to(torch.int32)
     return ids, spans, strengths
 
@@ -171,7 +183,8 @@ def make_inputs(w: Workload, lengths: Optional[List[int]] = None) -> Inputs:
         offsets[b + 1] = offsets[b] + n
     total_keys = int(offsets[-1]) + B * L
     q = torch.empty(B, w.n_layers, L, w.n_q_heads, w.head_dim, dtype=w.dtype)
-    k = torch.empty(w.n_layers, total_keys, w.n_kv_heads, w.head_dim, dtype=w.dtype)
+    k = torch.empty(w.n_layers, total_keys, w.n_kv_heads, w.head_dim,
+                    dtype=torch.float32 if w.k_fp8 else w.dtype)
     ids, spans, strengths = [], [], []
     for b, n in enumerate(lengths):
         kb = int(offsets[b]) + b * L
@@ -182,7 +195,22 @@ def make_inputs(w: Workload, lengths: Optional[List[int]] = None) -> Inputs:
         spans.append(s)
         strengths.append(st)
     token_ids = torch.cat(ids) if ids else torch.empty(0, dtype=torch.int32)
-    return Inputs(w, list(lengths), offsets, q, k, token_ids, spans, strengths)
+    k_scales = None
+    if w.k_fp8:
+        k, k_scales = quantize_fp8(k)
+    return Inputs(w, list(lengths), offsets, q, k, token_ids, spans, strengths, k_scales)
+
+
+FP8_MAX = 448.0   # largest finite float8 e4m3 (OCP E4M3FN) value
+
+
+def quantize_fp8(k: torch.Tensor):
+    """fp32 K [layers][keys][Hkv][d] -> (fp8 e4m3 codes, [layers][Hkv] fp32
+    scales) with scale = max |K| / 448 per (layer, KV head)."""
+    amax = k.abs().amax(dim=(1, 3))                       # [layers][Hkv]
+    scales = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax)).to(torch.float32)
+    codes = (k / scales[:, None, :, None]).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
+    return codes.contiguous(), scales.contiguous()
 
 
 def small_workload(base: str, **overrides) -> Workload:
