@@ -56,11 +56,13 @@ def lib():
             build(force=True)
         L = ctypes.CDLL(_LIB_PATH)
         L.oracle_softmax_row.argtypes = [ctypes.c_int, _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                         ctypes.c_int, ctypes.c_int, ctypes.c_double, _fp, _fp,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                         _fp, _fp,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp,
                                          _dp]
         L.oracle_importance.argtypes = [ctypes.c_int, _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                        ctypes.c_int, ctypes.c_int, ctypes.c_double, _fp, _fp, _dp,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, _fp,
+                                        _fp, _dp,
                                         ctypes.c_int, _dp]
         L.oracle_pool_chunk.argtypes = [ctypes.c_int64, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double,
@@ -113,15 +115,19 @@ def _scales(k_scales, n):
 
 
 def softmax_row(offsets, q, k, n_layers, Hq, Hkv, d, L, scale, b, l, j, h,
-                k_scales=None) -> np.ndarray:
-    """Softmax probabilities of query (b, l, j, h) over its N_b + j + 1 visible
-    keys; with k_scales, K holds codes and key = k_scales[l][g] * code."""
+                k_scales=None, prefill_row=False) -> np.ndarray:
+    """Softmax probabilities of query (b, l, j, h) over its N_b - pre + j + 1
+    visible keys (L lookahead keys; with prefill_row, q has L + 1 steps and
+    step 0 is the prompt's last row); with k_scales, K holds codes and
+    key = k_scales[l][g] * code."""
     off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
     qf, kf = _as_f32(q), _as_f32(k)
     ks = _scales(k_scales, n_layers * Hkv)
     n = int(off[b + 1] - off[b])
-    p = np.empty(n + j + 1, dtype=np.float64)
-    rc = lib().oracle_softmax_row(len(off) - 1, _ptr(off, _i64p), n_layers, Hq, Hkv, d, L, scale,
+    pre = int(bool(prefill_row))
+    p = np.empty(max(n - pre + j + 1, 1), dtype=np.float64)
+    rc = lib().oracle_softmax_row(len(off) - 1, _ptr(off, _i64p), n_layers, Hq, Hkv, d, L, pre,
+                                  scale,
                                   _ptr(qf, _fp), _ptr(kf, _fp), b, l, j, h, _ptr(p, _dp),
                                   None if ks is None else _ptr(ks, _dp))
     if rc != 0:
@@ -130,17 +136,18 @@ def softmax_row(offsets, q, k, n_layers, Hq, Hkv, d, L, scale, b, l, j, h,
 
 
 def importance(offsets, q, k, n_layers, Hq, Hkv, d, L, scale, nthreads: int = 0,
-               k_scales=None) -> np.ndarray:
-    """Importance of every prompt token, [sum N_b] fp64 (k_scales: see
-    softmax_row)."""
+               k_scales=None, prefill_row=False) -> np.ndarray:
+    """Importance of every prompt token, [sum N_b] fp64 (k_scales and
+    prefill_row: see softmax_row)."""
     off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
     qf, kf = _as_f32(q), _as_f32(k)
     ks = _scales(k_scales, n_layers * Hkv)
     B = len(off) - 1
-    assert qf.size == B * n_layers * L * Hq * d, "q has the wrong size"
+    pre = int(bool(prefill_row))
+    assert qf.size == B * n_layers * (L + pre) * Hq * d, "q has the wrong size"
     assert kf.size == n_layers * (int(off[-1]) + B * L) * Hkv * d, "k has the wrong size"
     imp = np.empty(int(off[-1]), dtype=np.float64)
-    rc = lib().oracle_importance(B, _ptr(off, _i64p), n_layers, Hq, Hkv, d, L, scale,
+    rc = lib().oracle_importance(B, _ptr(off, _i64p), n_layers, Hq, Hkv, d, L, pre, scale,
                                  _ptr(qf, _fp), _ptr(kf, _fp), _ptr(imp, _dp), nthreads,
                                  None if ks is None else _ptr(ks, _dp))
     if rc != 0:
@@ -200,7 +207,7 @@ def pipeline(inputs, mode: str = None, param: float = None, nthreads: int = 0, i
     if imp is None:
         imp = importance(inputs.offsets.numpy(), inputs.q, inputs.k, w.n_layers, w.n_q_heads,
                          w.n_kv_heads, w.head_dim, w.n_lookahead, inputs.scale, nthreads,
-                         k_scales=inputs.k_scales)
+                         k_scales=inputs.k_scales, prefill_row=w.prefill_row)
     off = inputs.offsets.numpy()
     ids = inputs.token_ids.numpy()
     fm, lm = (1.5, 1.3) if w.boost else (1.0, 1.0)

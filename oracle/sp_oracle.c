@@ -53,9 +53,15 @@ int oracle_max_threads(void) {
  * 0 .. N_b + j (N_b prompt keys and its own and earlier lookahead keys):
  *     s_k = scale * <Q[b][l][j][h], K[l][key0 + k][h / G]>
  *     p_k = exp(s_k - max s) / sum_k' exp(s_k' - max s)
- * Writes p[0 .. N_b + j] (N_b + j + 1 values). Returns 0, or -1 on bad args.
+ * Prefill row (pre = 1; [G] Full Source Code, the capture callback and the
+ * window loop): the last row of the prompt's own prefill is captured too and
+ * counts as one more step, in front of the lookahead ones. Then S = L + 1
+ * steps, step j sits at position N_b - 1 + j, and step 0 sees exactly the
+ * prompt's keys. In general step j (0 <= j < L + pre) sees keys
+ * 0 .. N_b - pre + j.
+ * Writes p[0 .. N_b - pre + j]. Returns 0, or -1 on bad args.
  *
- *   q: [B][layers][L][Hq][d]   k: [layers][sum_b (N_b + L)][Hkv][d]
+ *   q: [B][layers][L + pre][Hq][d]   k: [layers][sum_b (N_b + L)][Hkv][d]
  *   tok_off: [B + 1]; prompt b's key rows start at tok_off[b] + b * L.
  *   k_scales: NULL, or [layers][Hkv]: a quantised K cache (the [PR]
  *   discussion runs the draft's K cache in an 8-bit type) holds codes, and
@@ -63,18 +69,19 @@ int oracle_max_threads(void) {
  *     s_k = scale * <Q, k_scales[l][h / G] * K_code> = scale * k_scales[l][h / G] * <Q, K_code>.
  */
 int oracle_softmax_row(int B, const int64_t *tok_off, int n_layers, int Hq,
-                       int Hkv, int d, int L, double scale, const float *q,
+                       int Hkv, int d, int L, int pre, double scale, const float *q,
                        const float *k, int b, int l, int j, int h, double *p,
                        const double *k_scales) {
-  if (b < 0 || b >= B || l < 0 || l >= n_layers || j < 0 || j >= L || h < 0 ||
-      h >= Hq || Hkv <= 0 || Hq % Hkv != 0)
+  const int S = L + pre;
+  if (b < 0 || b >= B || l < 0 || l >= n_layers || j < 0 || j >= S || h < 0 ||
+      h >= Hq || Hkv <= 0 || Hq % Hkv != 0 || L < 0 || pre < 0 || pre > 1)
     return -1;
   const int G = Hq / Hkv;
   const int64_t total_keys = tok_off[B] + (int64_t)B * L;
   const int64_t N = tok_off[b + 1] - tok_off[b];
   const int64_t key0 = tok_off[b] + (int64_t)b * L;
-  const float *qrow = q + ((((int64_t)b * n_layers + l) * L + j) * Hq + h) * d;
-  const int64_t nvis = N + j + 1;
+  const float *qrow = q + ((((int64_t)b * n_layers + l) * S + j) * Hq + h) * d;
+  const int64_t nvis = N - pre + j + 1;
   const double ks = k_scales ? k_scales[(int64_t)l * Hkv + h / G] : 1.0;
   double m = -INFINITY;
   for (int64_t kk = 0; kk < nvis; kk++) {
@@ -93,7 +100,8 @@ int oracle_softmax_row(int B, const int64_t *tok_off, int n_layers, int Hq,
 
 /*
  * Token importance of every prompt token (steps: softmax rows, max over
- * heads, max over layers, mean over lookahead steps).
+ * heads, max over layers, mean over the S = L + pre steps; pre: see
+ * oracle_softmax_row).
  *
  * [G] Token Importance and compute_imp: for each lookahead step, take the
  * maximum attention probability over all heads, then over all attention
@@ -101,19 +109,20 @@ int oracle_softmax_row(int B, const int64_t *tok_off, int n_layers, int Hq,
  * [G] capture callback: only the first N columns (the prompt keys) of each
  * row are read, although each row is normalised over every key it sees.
  *
- *   imp[tok_off[b] + k] = (1/L) * sum_j max_{l, h} p[b][l][j][h][k],  k < N_b
+ *   imp[tok_off[b] + k] = (1/S) * sum_j max_{l, h} p[b][l][j][h][k],  k < N_b
  *
  * Parallel over (prompt, step) pairs when built with OpenMP; each pair owns
  * its own step-max row, so the result does not depend on the thread count.
  * nthreads <= 0 uses the OpenMP default. Returns 0, or -1 on bad args.
  */
 int oracle_importance(int B, const int64_t *tok_off, int n_layers, int Hq,
-                      int Hkv, int d, int L, double scale, const float *q,
+                      int Hkv, int d, int L, int pre, double scale, const float *q,
                       const float *k, double *imp, int nthreads,
                       const double *k_scales) {
   if (B <= 0 || n_layers <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
-      d <= 0 || L <= 0)
+      d <= 0 || L < 0 || pre < 0 || pre > 1 || L + pre <= 0)
     return -1;
+  const int S = L + pre;
   const int64_t total_tok = tok_off[B];
   int64_t max_n = 0;
   for (int b = 0; b < B; b++) {
@@ -121,8 +130,8 @@ int oracle_importance(int B, const int64_t *tok_off, int n_layers, int Hq,
     if (n <= 0) return -1;
     if (n > max_n) max_n = n;
   }
-  /* stepmax[b][j][k] lives at stepmax[(tok_off[b] * L) + j * N_b + k]. */
-  double *stepmax = (double *)malloc(sizeof(double) * (size_t)(total_tok * L));
+  /* stepmax[b][j][k] lives at stepmax[(tok_off[b] * S) + j * N_b + k]. */
+  double *stepmax = (double *)malloc(sizeof(double) * (size_t)(total_tok * S));
   if (!stepmax) return -1;
   int err = 0;
 #ifdef _OPENMP
@@ -130,15 +139,15 @@ int oracle_importance(int B, const int64_t *tok_off, int n_layers, int Hq,
 #pragma omp parallel for collapse(2) schedule(dynamic) num_threads(nthreads) reduction(| : err)
 #endif
   for (int b = 0; b < B; b++) {
-    for (int j = 0; j < L; j++) {
+    for (int j = 0; j < S; j++) {
       const int64_t N = tok_off[b + 1] - tok_off[b];
-      double *sm = stepmax + tok_off[b] * L + (int64_t)j * N;
+      double *sm = stepmax + tok_off[b] * S + (int64_t)j * N;
       double *p = (double *)malloc(sizeof(double) * (size_t)(N + L));
       if (!p) { err |= 1; continue; }
       for (int64_t kk = 0; kk < N; kk++) sm[kk] = 0.0; /* probabilities are >= 0 */
       for (int l = 0; l < n_layers; l++) {
         for (int h = 0; h < Hq; h++) {
-          oracle_softmax_row(B, tok_off, n_layers, Hq, Hkv, d, L, scale, q, k,
+          oracle_softmax_row(B, tok_off, n_layers, Hq, Hkv, d, L, pre, scale, q, k,
                              b, l, j, h, p, k_scales);
           for (int64_t kk = 0; kk < N; kk++)  /* prompt columns only */
             if (p[kk] > sm[kk]) sm[kk] = p[kk];
@@ -152,8 +161,8 @@ int oracle_importance(int B, const int64_t *tok_off, int n_layers, int Hq,
       const int64_t N = tok_off[b + 1] - tok_off[b];
       for (int64_t kk = 0; kk < N; kk++) {
         double acc = 0.0;
-        for (int j = 0; j < L; j++) acc += stepmax[tok_off[b] * L + (int64_t)j * N + kk];
-        imp[tok_off[b] + kk] = acc / L;
+        for (int j = 0; j < S; j++) acc += stepmax[tok_off[b] * S + (int64_t)j * N + kk];
+        imp[tok_off[b] + kk] = acc / S;
       }
     }
   }

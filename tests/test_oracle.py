@@ -170,6 +170,82 @@ def test_importance_prompts_are_independent():
 
 
 # ----------------------------------------------------------------------------
+# Prefill row: the prompt's own last row as one more step in front
+# ----------------------------------------------------------------------------
+
+def _prerow_problem(rng, lengths, n_layers, Hq, Hkv, d, L, scale_q=2.0):
+    """Q with L + 1 steps, K with L lookahead keys per prompt."""
+    B = len(lengths)
+    off = np.zeros(B + 1, dtype=np.int64)
+    off[1:] = np.cumsum(lengths)
+    q = (rng.standard_normal((B, n_layers, L + 1, Hq, d)) * scale_q).astype(np.float32)
+    k = rng.standard_normal((n_layers, int(off[-1]) + B * L, Hkv, d)).astype(np.float32)
+    return off, q, k
+
+
+def test_prefill_row_all_zero_q_closed_form():
+    """Zero queries: step j sees N + j keys (step 0 the N prompt keys), so
+    imp = (1/(L+1)) * sum_{j=0..L} 1/(N + j)."""
+    rng = np.random.default_rng(21)
+    lengths, L = [40, 17], 5
+    off, q, k = _prerow_problem(rng, lengths, 2, 4, 2, 8, L)
+    q[:] = 0
+    imp = oracle.importance(off, q, k, 2, 4, 2, 8, L, 0.3, prefill_row=True)
+    for b, n in enumerate(lengths):
+        want = sum(1.0 / (n + j) for j in range(L + 1)) / (L + 1)
+        np.testing.assert_allclose(imp[off[b]:off[b + 1]], want, rtol=1e-14)
+
+
+def test_prefill_row_is_a_shifted_lookahead_prompt():
+    """The same Q and K read as a prompt one token shorter with one more
+    lookahead key give the same rows: the first N - 1 scores agree, and only
+    the last prompt token (a lookahead key there) is new."""
+    rng = np.random.default_rng(22)
+    n_layers, Hq, Hkv, d, L = 2, 8, 2, 8, 3
+    lengths = [23, 9, 31]
+    off, q, k = _prerow_problem(rng, lengths, n_layers, Hq, Hkv, d, L)
+    pre = oracle.importance(off, q, k, n_layers, Hq, Hkv, d, L, 0.35, prefill_row=True)
+    short = np.concatenate([[0], np.cumsum([n - 1 for n in lengths])]).astype(np.int64)
+    plain = oracle.importance(short, q, k, n_layers, Hq, Hkv, d, L + 1, 0.35)
+    for b, n in enumerate(lengths):
+        np.testing.assert_allclose(pre[off[b]:off[b] + n - 1], plain[short[b]:short[b + 1]],
+                                   rtol=1e-13, atol=1e-16)
+
+
+def test_prefill_row_matches_bruteforce():
+    """Dense route: step j of prompt b sits at position N - 1 + j."""
+    rng = np.random.default_rng(23)
+    n_layers, Hq, Hkv, d, L = 2, 4, 2, 8, 2
+    lengths = [11, 6]
+    off, q, k = _prerow_problem(rng, lengths, n_layers, Hq, Hkv, d, L)
+    scale = 0.4
+    got = oracle.importance(off, q, k, n_layers, Hq, Hkv, d, L, scale, prefill_row=True)
+    G = Hq // Hkv
+    for b, n in enumerate(lengths):
+        k0 = int(off[b]) + b * L
+        kb = np.repeat(k[:, k0:k0 + n + L].astype(np.float64), G, axis=2)   # [l][key][h][d]
+        s = np.einsum("ljhd,lkhd->ljhk", q[b].astype(np.float64), kb) * scale
+        vis = np.arange(n + L)[None, :] <= (n - 1 + np.arange(L + 1))[:, None]
+        s = np.where(vis[None, :, None, :], s, -np.inf)
+        p = scipy.special.softmax(s, axis=-1)[..., :n]
+        want = p.max(axis=2).max(axis=0).mean(axis=0)
+        np.testing.assert_allclose(got[off[b]:off[b + 1]], want, rtol=1e-12, atol=1e-15)
+
+
+def test_prefill_row_alone():
+    """With no lookahead keys the prefill row is the only step: its
+    importance is the row's own softmax over the prompt, maxed over heads and
+    layers."""
+    rng = np.random.default_rng(24)
+    off, q, k = _prerow_problem(rng, [15], 2, 4, 1, 8, 0)
+    got = oracle.importance(off, q, k, 2, 4, 1, 8, 0, 0.5, prefill_row=True)
+    rows = [oracle.softmax_row(off, q, k, 2, 4, 1, 8, 0, 0.5, 0, l, 0, h, prefill_row=True)
+            for l in range(2) for h in range(4)]
+    assert all(r.size == 15 for r in rows)
+    np.testing.assert_allclose(got, np.max(rows, axis=0), rtol=1e-15)
+
+
+# ----------------------------------------------------------------------------
 # Quantised draft keys: fp8 e4m3 codes with a per-(layer, KV head) scale
 # ----------------------------------------------------------------------------
 

@@ -65,10 +65,16 @@ class Workload:
     ragged_count: int = 0             # >0: draw this many lengths log-uniform
     ragged_range: tuple = (2048, 65536)
     k_fp8: bool = False               # K as fp8 e4m3 codes + per-(layer, KV head) scales
+    prefill_row: bool = False         # one more query step: the prompt's last row
 
     @property
     def group(self) -> int:
         return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def steps(self) -> int:
+        """Query steps per (layer, head): the lookahead ones, plus the prefill row."""
+        return self.n_lookahead + int(self.prefill_row)
 
 
 WORKLOADS = {
@@ -102,6 +108,14 @@ WORKLOADS = {
                            also_select=(("mass", 0.85),), k_fp8=True),
     "n128k_fp8k": Workload("n128k_fp8k", (131072,), 6, 16, 4, 128, 8,
                            torch.bfloat16, 1004, 64, None, k_fp8=True),
+    # The prefill's last row as one more step: 7 lookahead steps + 1 = 8 rows
+    # per head, so the 32 query rows of a KV group stay filled.
+    "n3212_prerow_bf16": Workload("n3212_prerow_bf16", (3212,), 6, 16, 4, 128, 7,
+                                  torch.bfloat16, 1002, 5, 2.0, select=("top_p", 0.30),
+                                  also_select=(("mass", 0.85),), prefill_row=True),
+    "n32k_prerow_bf16": Workload("n32k_prerow_bf16", (32768,), 6, 16, 4, 128, 7,
+                                 torch.bfloat16, 1003, 20, None,
+                                 also_select=(("top_p", 0.15),), prefill_row=True),
 }
 
 
@@ -110,7 +124,7 @@ class Inputs:
     workload: Workload
     lengths: List[int]
     offsets: torch.Tensor      # [B+1] int64
-    q: torch.Tensor            # [B][layers][L][Hq][d]
+    q: torch.Tensor            # [B][layers][S][Hq][d], S = L (+ 1 with the prefill row)
     k: torch.Tensor            # [layers][sum(N_b+L)][Hkv][d]
     token_ids: torch.Tensor    # [sum N_b] int32
     spans: List[List[int]]     # planted chunk indices per prompt
@@ -139,7 +153,7 @@ def ragged_lengths(w: Workload) -> List[int]:
 def _draw_prompt(w: Workload, n: int, seed: int, k_out: torch.Tensor, q_out: torch.Tensor,
                  n_spans: int):
     """Draw one prompt's Q, K (written into the given slices) and token ids."""
-    L, Hq, Hkv, d, G = w.n_lookahead, w.n_q_heads, w.n_kv_heads, w.head_dim, w.group
+    L, S, Hq, Hkv, d, G = w.n_lookahead, w.steps, w.n_q_heads, w.n_kv_heads, w.head_dim, w.group
     g = torch.Generator("cpu").manual_seed(seed)
     # Chunks wholly inside [64, n - 128): clear of the boosted edges and of
     # the always-kept final chunk.
@@ -154,7 +168,7 @@ def _draw_prompt(w: Workload, n: int, seed: int, k_out: torch.Tensor, q_out: tor
     else:
         strengths = [float(w.span_strength)] * n_spans
     for layer in range(w.n_layers):
-        q = torch.randn(L, Hq, d, generator=g, dtype=torch.float32)
+        q = torch.randn(S, Hq, d, generator=g, dtype=torch.float32)
         kk = torch.randn(n + L, Hkv, d, generator=g, dtype=torch.float32)
         for grp in range(Hkv):
             v = q[:, grp * G:(grp + 1) * G, :].reshape(-1, d).mean(dim=0)
@@ -182,7 +196,7 @@ def make_inputs(w: Workload, lengths: Optional[List[int]] = None) -> Inputs:
     for b, n in enumerate(lengths):
         offsets[b + 1] = offsets[b] + n
     total_keys = int(offsets[-1]) + B * L
-    q = torch.empty(B, w.n_layers, L, w.n_q_heads, w.head_dim, dtype=w.dtype)
+    q = torch.empty(B, w.n_layers, w.steps, w.n_q_heads, w.head_dim, dtype=w.dtype)
     k = torch.empty(w.n_layers, total_keys, w.n_kv_heads, w.head_dim,
                     dtype=torch.float32 if w.k_fp8 else w.dtype)
     ids, spans, strengths = [], [], []
