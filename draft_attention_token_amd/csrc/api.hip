@@ -73,8 +73,10 @@ PoolTable make_pool_table(const sp_batch *batch, int C) {
 
 sp_status check_attn(const sp_attn_desc *d, AttnShape *s) {
   if (!d) return SP_ERR_INVALID_ARGUMENT;
-  if (d->n_layers < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->n_lookahead < 1)
+  if (d->n_layers < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->n_lookahead < 0)
     return SP_ERR_INVALID_ARGUMENT;
+  if (d->prefill_row != 0 && d->prefill_row != 1) return SP_ERR_INVALID_ARGUMENT;
+  if (d->n_lookahead + d->prefill_row < 1) return SP_ERR_INVALID_ARGUMENT;
   if (d->n_q_heads % d->n_kv_heads != 0) return SP_ERR_INVALID_ARGUMENT;
   if (d->dtype != SP_DTYPE_F32 && d->dtype != SP_DTYPE_BF16 && d->dtype != SP_DTYPE_BF16_FP8K)
     return SP_ERR_INVALID_ARGUMENT;
@@ -82,7 +84,7 @@ sp_status check_attn(const sp_attn_desc *d, AttnShape *s) {
   if (d->algo < SP_SCORE_AUTO || d->algo > SP_SCORE_STREAM) return SP_ERR_INVALID_ARGUMENT;
   if (d->head_dim != 64 && d->head_dim != 128) return SP_ERR_UNSUPPORTED;
   const int G = d->n_q_heads / d->n_kv_heads;
-  if ((int64_t)d->n_lookahead * G > kRows) return SP_ERR_UNSUPPORTED;
+  if ((int64_t)(d->n_lookahead + d->prefill_row) * G > kRows) return SP_ERR_UNSUPPORTED;
   if (d->dtype == SP_DTYPE_BF16_FP8K) {
     if (d->algo == SP_SCORE_TWO_PASS) return SP_ERR_UNSUPPORTED;   // single-pass only
     if ((int64_t)d->n_layers * d->n_kv_heads > kMaxScaledProblems) return SP_ERR_UNSUPPORTED;
@@ -91,8 +93,10 @@ sp_status check_attn(const sp_attn_desc *d, AttnShape *s) {
   s->Hq = d->n_q_heads;
   s->Hkv = d->n_kv_heads;
   s->d = d->head_dim;
-  s->L = d->n_lookahead;
+  s->L = d->n_lookahead + d->prefill_row;
   s->G = G;
+  s->La = d->n_lookahead;
+  s->pre = d->prefill_row;
   s->scale_log2 = d->scale * kLog2e;
   s->dtype = d->dtype;
   return SP_OK;
@@ -169,7 +173,7 @@ sp_status sp_score_workspace_bytes(const sp_attn_desc *desc, const sp_batch *bat
   sp_status st = check_attn(desc, &s);
   if (st != SP_OK) return st;
   if ((st = check_batch(batch, &total)) != SP_OK) return st;
-  const SegTable tiles = make_table(batch, s.L, kTile, s.L);
+  const SegTable tiles = make_table(batch, s.La, kTile, s.La);
   *bytes = score_ws_bytes(s, tiles);
   return SP_OK;
 }
@@ -195,7 +199,7 @@ sp_status sp_score_attention(const sp_attn_desc *desc, const sp_batch *batch, co
       ks.v[x] = v;
     }
   }
-  const SegTable tiles = make_table(batch, s.L, kTile, s.L);
+  const SegTable tiles = make_table(batch, s.La, kTile, s.La);
   const int total_tiles = tiles.unit_off[tiles.B];
   if (!ws || ws_bytes < score_ws_bytes(s, tiles)) return SP_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);

@@ -84,7 +84,8 @@ __device__ __forceinline__ constexpr int acc_row(int i, int half) {
 }
 
 // Pointer to the d-vector of query row r = j * G + hh of (prompt b, layer l,
-// KV group g) in q[B][layers][L][Hq][d]; rows >= L * G are padding.
+// KV group g) in q[B][layers][L][Hq][d] (L query steps, the prefill row
+// included); rows >= L * G are padding.
 template <typename T>
 __device__ __forceinline__ const T *q_row_ptr(const T *q, const AttnShape &s, int b, int l, int g,
                                               int r) {

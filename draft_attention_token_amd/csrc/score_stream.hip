@@ -4,7 +4,10 @@
 // Importance (max over heads, then layers, then mean over lookahead steps);
 // "Speculative prefill" (llama.cpp pull request 27692), Approach steps 2-3.
 // Query j of a prompt sits at position N + j and sees keys 0 .. N + j; only
-// the N prompt columns receive importance.
+// the N prompt columns receive importance. With the prefill row (the same
+// guide's Full Source Code captures the prefill's last row as one more step)
+// every step sits one position earlier: step 0 is the prompt's last token and
+// sees only the prompt.
 //
 // Design. A probability needs its row's log-sum-exp (lse) over every key the
 // row sees, so no probability is final before all of K has been read. Rather
@@ -420,13 +423,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
   const int bb = cta_prompt(tb, cta), b = tb.p0 + bb;
   const int c_lo = tb.cta_off[bb], n_c = tb.cta_off[bb + 1] - c_lo, ci = cta - c_lo;
   const int N = tb.tok_off[bb + 1] - tb.tok_off[bb];
-  const int NK = N + s.L;                                   // keys of the prompt
+  const int NK = N + s.La;                                  // keys of the prompt
   // The block's keys: an even share of the prompt's (K bytes are what the
   // kernel is bound by), in tiles of 32 from its first key; the last tile
   // may be partial.
   const int k_lo = (int)((int64_t)NK * ci / n_c), k_hi = (int)((int64_t)NK * (ci + 1) / n_c);
   const int nt = (k_hi - k_lo + kTile - 1) / kTile;
-  const int64_t key0 = (int64_t)tb.tok_off[bb] + (int64_t)b * s.L;
+  const int64_t key0 = (int64_t)tb.tok_off[bb] + (int64_t)b * s.La;
 
   if (control) {
     // ---------------- control waves ----------------
@@ -630,7 +633,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = w_k0 + t * kTile + acc_row(i, half);
-            const bool ok = row_ok && key < w_k1 && key <= N + jr;   // causal: key < NK
+            const bool ok = row_ok && key < w_k1 && key <= N - s.pre + jr;   // causal
             x[i] = ok ? x[i] * sl2 : -INFINITY;
             mt = fmaxf(mt, x[i]);
           }
@@ -853,7 +856,7 @@ hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const 
   const int n_stream = stream_ctas(s);
   if (n_stream < 1) return hipSuccess;
   static thread_local Plan plan;
-  if (!make_plan(tiles, s.L, n_stream, plan)) return hipSuccess;
+  if (!make_plan(tiles, s.La, n_stream, plan)) return hipSuccess;
   *supported = true;
   StreamWs w;
   char *base = reinterpret_cast<char *>(ws);

@@ -6,8 +6,9 @@
 // Method: "SpecPrefill — Implementation Guide", How It Works / Token
 // Importance (max over heads, then layers, then mean over lookahead steps),
 // and "Speculative prefill" (llama.cpp pull request 27692), Approach
-// steps 2-3. Causality: query j of a prompt sits at position N + j and sees
-// keys 0 .. N + j; only the N prompt columns receive importance.
+// steps 2-3. Causality: query j of a prompt sits at position N - pre + j
+// and sees keys 0 .. N - pre + j (pre = 1 with the prefill row, the prompt's
+// last row as step 0); only the N prompt columns receive importance.
 #include "score_common.h"
 
 namespace sp {
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(64) void k_stats(AttnShape s, SegTable tiles, int64
   for (int i = 0; i < 16; ++i) {
     const int row = acc_row(i, half);
     const int j = row / s.G;
-    const bool vis = row < rows && c.kl < c.nkeys && c.kl <= c.N + j;
+    const bool vis = row < rows && c.kl < c.nkeys && c.kl <= c.N - s.pre + j;
     const float x = vis ? acc[i] * s.scale_log2 : -INFINITY;
     const float m = wave_max32(x);
     const float e = vis ? exp2f(x - m) : 0.f;

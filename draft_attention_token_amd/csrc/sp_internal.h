@@ -41,7 +41,11 @@ __device__ __forceinline__ int seg_of(const SegTable &t, int32_t u) {
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct AttnShape {
-  int n_layers, Hq, Hkv, d, L, G;
+  int n_layers, Hq, Hkv, d;
+  int L;                            // query steps per (layer, head): La + pre
+  int G;
+  int La;                           // lookahead keys per prompt (K rows past the prompt)
+  int pre;                          // 1: step 0 is the prompt's last row (position N - 1)
   float scale_log2;                 // scale * log2(e): logits kept in base-2 units
   int dtype;
 };

@@ -58,7 +58,7 @@ class sp_attn_desc(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("n_lookahead", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("algo", ctypes.c_int32),
-                ("k_scales", ctypes.POINTER(ctypes.c_float))]
+                ("k_scales", ctypes.POINTER(ctypes.c_float)), ("prefill_row", ctypes.c_int32)]
 
 
 class sp_pool_desc(ctypes.Structure):
@@ -149,10 +149,11 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 
 
 def attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype, scale=None,
-              algo="auto", k_dtype=None, k_scales=None) -> sp_attn_desc:
+              algo="auto", k_dtype=None, k_scales=None, prefill_row=False) -> sp_attn_desc:
     """dtype: Q's torch dtype (and K's unless k_dtype says otherwise).
     k_dtype=torch.float8_e4m3fn with bf16 Q selects fp8 K codes; k_scales
-    is then the [n_layers * n_kv_heads] fp32 host array of key scales."""
+    is then the [n_layers * n_kv_heads] fp32 host array of key scales.
+    prefill_row: Q carries one more step in front, the prompt's last row."""
     if k_dtype is None or k_dtype == dtype:
         dt = {torch.float32: SP_DTYPE_F32, torch.bfloat16: SP_DTYPE_BF16}.get(dtype, -1)
     elif dtype == torch.bfloat16 and k_dtype == torch.float8_e4m3fn:
@@ -162,7 +163,8 @@ def attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype, sca
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
     desc = sp_attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dt, float(scale),
-                        _ALGOS[algo] if isinstance(algo, str) else int(algo), None)
+                        _ALGOS[algo] if isinstance(algo, str) else int(algo), None,
+                        int(prefill_row) if isinstance(prefill_row, (bool, int)) else -1)
     if k_scales is not None:
         ks = np.ascontiguousarray(np.asarray(
             k_scales.cpu() if isinstance(k_scales, torch.Tensor) else k_scales,
@@ -208,18 +210,21 @@ def gather_workspace_bytes(batch: Batch, C: int) -> int:
 def sp_score_attention(q: torch.Tensor, k: torch.Tensor, offsets, n_layers: int, n_q_heads: int,
                        n_kv_heads: int, head_dim: int, n_lookahead: int, scale=None,
                        algo="auto", out: Optional[torch.Tensor] = None,
-                       ws: Optional[torch.Tensor] = None, k_scales=None) -> torch.Tensor:
+                       ws: Optional[torch.Tensor] = None, k_scales=None,
+                       prefill_row=False) -> torch.Tensor:
     """Token importance [sum N_b] fp32 (see the C header for layouts). K may
     be fp8 e4m3 codes with bf16 Q; k_scales ([n_layers * n_kv_heads]) then
-    gives each (layer, KV head)'s key scale."""
+    gives each (layer, KV head)'s key scale. prefill_row: q holds
+    n_lookahead + 1 steps, the first the prompt's last row."""
     batch = offsets if isinstance(offsets, Batch) else Batch(offsets)
     desc = attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, q.dtype, scale, algo,
-                     k_dtype=k.dtype, k_scales=k_scales)
+                     k_dtype=k.dtype, k_scales=k_scales, prefill_row=prefill_row)
+    steps = n_lookahead + int(bool(prefill_row))
     if not (q.is_contiguous() and k.is_contiguous()):
         raise ValueError("q and k must be contiguous")
     if q.dtype != k.dtype and not (q.dtype == torch.bfloat16 and k.dtype == torch.float8_e4m3fn):
         raise ValueError("q and k must share a dtype (or be bf16 Q with fp8 e4m3 K)")
-    if q.numel() != batch.B * n_layers * n_lookahead * n_q_heads * head_dim:
+    if q.numel() != batch.B * n_layers * steps * n_q_heads * head_dim:
         raise ValueError("q has the wrong number of elements")
     if k.numel() != n_layers * (batch.total + batch.B * n_lookahead) * n_kv_heads * head_dim:
         raise ValueError("k has the wrong number of elements")
@@ -317,11 +322,13 @@ class Pipeline:
 
     def __init__(self, offsets, n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype,
                  device, W=13, C=32, normalize=True, boost=True, mode="mass", param=0.85,
-                 algo="auto", scale=None, token_scores=True, k_dtype=None, k_scales=None):
+                 algo="auto", scale=None, token_scores=True, k_dtype=None, k_scales=None,
+                 prefill_row=False):
         self.batch = offsets if isinstance(offsets, Batch) else Batch(offsets)
         fm, lm = (1.5, 1.3) if boost else (1.0, 1.0)
         self.adesc = attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype,
-                               scale, algo, k_dtype=k_dtype, k_scales=k_scales)
+                               scale, algo, k_dtype=k_dtype, k_scales=k_scales,
+                               prefill_row=prefill_row)
         self.pdesc = pool_desc(W, C, normalize, 64, fm, 128, lm)
         self.C, self.mode, self.param = C, _MODES[mode], float(param)
         self.shape = (n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead)

@@ -89,19 +89,25 @@ typedef struct {
 } sp_batch;
 
 /* Draft attention shape ([G] Attention Capture; [PR] Approach steps 1-2).
- * n_lookahead (L) queries per prompt sit at positions N_b .. N_b + L - 1. */
+ * n_lookahead (L) queries per prompt sit at positions N_b .. N_b + L - 1.
+ * With prefill_row = 1 ([G] Full Source Code: the capture during the
+ * prefill keeps the prompt's last row, and the importance averages it with
+ * the lookahead rows) there are S = L + 1 query steps at positions
+ * N_b - 1 .. N_b + L - 1; step 0 is the prompt's last token and sees only
+ * the prompt. Without it S = L. */
 typedef struct {
   int32_t n_layers;     /* attention layers that give scores, >= 1 */
   int32_t n_q_heads;    /* Hq >= 1 */
   int32_t n_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0; G = Hq / Hkv */
   int32_t head_dim;     /* d: 64 or 128 */
-  int32_t n_lookahead;  /* L >= 1; L * G <= 32 */
+  int32_t n_lookahead;  /* L >= 0 lookahead keys and steps; S >= 1; S * G <= 32 */
   int32_t dtype;        /* sp_dtype of Q and K */
   float scale;          /* logit scale, usually 1 / sqrt(d) */
   int32_t algo;         /* sp_score_algo */
   const float *k_scales; /* host, [n_layers * n_kv_heads], finite and > 0:
                             SP_DTYPE_BF16_FP8K only (n_layers * n_kv_heads
                             <= 128); NULL otherwise */
+  int32_t prefill_row;  /* 0 or 1: step 0 is the prompt's last row */
 } sp_attn_desc;
 
 /* Smoothing, normalisation, boosts and chunking ([PR] Approach step 3;
@@ -131,14 +137,15 @@ sp_status sp_gather_workspace_bytes(const sp_batch *batch, int32_t chunk_size, s
 
 /*
  * Token importance ([G] Token Importance; [PR] Approach steps 1-3).
- * For every prompt b, layer l, lookahead step j and query head h, the softmax
- * row of query (b, l, j, h) over the keys it sees (its N_b prompt keys and
- * lookahead keys 0..j, causal), with logits scale * <q, k> against the key
- * head h / G. Only the prompt columns go forward ([G] capture callback).
- *   importance[b][k] = (1/L) * sum_j max_{l, h} p[b][l][j][h][k],  k < N_b
+ * For every prompt b, layer l, step j and query head h, the softmax row of
+ * query (b, l, j, h) over the keys it sees (keys 0 .. N_b - pre + j, causal,
+ * pre = prefill_row: the prompt keys and the lookahead keys up to its own),
+ * with logits scale * <q, k> against the key head h / G. Only the prompt
+ * columns go forward ([G] capture callback).
+ *   importance[b][k] = (1/S) * sum_j max_{l, h} p[b][l][j][h][k],  k < N_b
  *
- *   q:  [B][n_layers][L][Hq][d] of dtype (bf16 for SP_DTYPE_BF16_FP8K),
- *       contiguous.
+ *   q:  [B][n_layers][S][Hq][d] of dtype (bf16 for SP_DTYPE_BF16_FP8K),
+ *       contiguous; S = L + prefill_row, step 0 the prefill row if any.
  *   k:  [n_layers][sum_b (N_b + L)][Hkv][d] of dtype (one byte per code for
  *       SP_DTYPE_BF16_FP8K, whose logits are scale * k_scales[l * Hkv + g] *
  *       <q, code>; single-pass kernel only), contiguous; prompt b's

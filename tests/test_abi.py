@@ -63,6 +63,9 @@ def _desc(**kw):
     (dict(head_dim=96), sp.SP_ERR_UNSUPPORTED),
     (dict(n_lookahead=9), sp.SP_ERR_UNSUPPORTED),           # L * G = 36 > 32
     (dict(n_q_heads=64, n_kv_heads=4), sp.SP_ERR_UNSUPPORTED),
+    (dict(n_lookahead=-1), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(prefill_row=2), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(n_lookahead=8, prefill_row=True), sp.SP_ERR_UNSUPPORTED),   # (8 + 1) * 4 > 32
 ])
 def test_score_rejects_bad_descriptors(kw, want):
     assert _score(_desc(**kw), sp.Batch([0, 100])) == want

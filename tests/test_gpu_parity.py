@@ -33,7 +33,7 @@ def run_gpu(inp, mode, param, algo="auto"):
     pipe = sp.Pipeline(inp.offsets, w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim,
                        w.n_lookahead, w.dtype, DEV, W=w.pool_window, C=w.chunk_size,
                        normalize=w.normalize, boost=w.boost, mode=mode, param=param, algo=algo,
-                       k_dtype=inp.k.dtype, k_scales=inp.k_scales)
+                       k_dtype=inp.k.dtype, k_scales=inp.k_scales, prefill_row=w.prefill_row)
     q, k, ids = inp.q.to(DEV), inp.k.to(DEV), inp.token_ids.to(DEV)
     pipe.run(q, k, ids)
     torch.cuda.synchronize()
@@ -95,6 +95,13 @@ SMALL = [
     ("bf16_d128_g32_l1", "n3212_bf16", dict(lengths=(200,), n_q_heads=32, n_kv_heads=1,
                                             n_lookahead=1, n_layers=2)),
     ("bf16_no_norm", "n3212_bf16", dict(lengths=(800,), normalize=False, boost=False)),
+    # The prefill's last row as step 0.
+    ("prerow_bf16_d128_g4_l7", "n3212_prerow_bf16", dict(lengths=(1000,))),
+    ("prerow_bf16_ragged", "n3212_prerow_bf16", dict(lengths=(65, 1, 640, 129, 2))),
+    ("prerow_fp32_d64_alone", "n800_fp32", dict(lengths=(333, 2, 1), n_lookahead=0,
+                                                 prefill_row=True)),
+    ("prerow_bf16_d64_g8_l3", "n3212_bf16", dict(lengths=(500,), head_dim=64, n_q_heads=16,
+                                                 n_kv_heads=2, n_lookahead=3, prefill_row=True)),
 ]
 
 
@@ -108,7 +115,7 @@ def test_small_shapes(name, base, kw, algo):
         compare(inp, pipe, mode, param)
 
 
-@pytest.mark.parametrize("name", ["n800_fp32", "n3212_bf16"])
+@pytest.mark.parametrize("name", ["n800_fp32", "n3212_bf16", "n3212_prerow_bf16"])
 def test_named_small_workloads(name):
     w = workloads.WORKLOADS[name]
     inp = workloads.make_inputs(w)
@@ -262,6 +269,7 @@ FP8K_SMALL = [
                                           n_kv_heads=2, n_lookahead=4)),
     ("fp8k_d128_g1_l1", "n3212_fp8k", dict(lengths=(300, 45), n_q_heads=4, n_kv_heads=4,
                                            n_lookahead=1)),
+    ("fp8k_prerow_l7", "n3212_fp8k", dict(lengths=(700, 33), n_lookahead=7, prefill_row=True)),
 ]
 
 
@@ -276,13 +284,14 @@ def test_fp8k_small_shapes(name, base, kw):
         compare(inp, pipe, mode, param)
 
 
-@pytest.mark.parametrize("name", ["n32k_bf16", "n128k_bf16", "n128k_diffuse_bf16", "n128k_fp8k"])
+@pytest.mark.parametrize("name", ["n32k_bf16", "n128k_bf16", "n128k_diffuse_bf16", "n128k_fp8k",
+                                  "n32k_prerow_bf16"])
 def test_full_size_single_prompt(name):
     w = workloads.WORKLOADS[name]
     inp = workloads.make_inputs(w)
     imp = oracle.importance(inp.offsets.numpy(), inp.q, inp.k, w.n_layers, w.n_q_heads,
                             w.n_kv_heads, w.head_dim, w.n_lookahead, inp.scale,
-                            k_scales=inp.k_scales)
+                            k_scales=inp.k_scales, prefill_row=w.prefill_row)
     for mode, param in (w.select,) + tuple(w.also_select):
         pipe = run_gpu(inp, mode, param)
         ora = oracle.pipeline(inp, mode, param, imp=imp)
