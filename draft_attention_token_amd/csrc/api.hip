@@ -331,4 +331,18 @@ sp_status sp_gather_kept(const sp_batch *batch, int32_t chunk_size, const uint8_
                                 reinterpret_cast<hipStream_t>(stream)));
 }
 
+sp_status sp_break_even(int64_t n_tokens, int64_t n_kept, double spec_tps, double target_tps,
+                        double safety, int32_t *run) {
+  if (!run || n_tokens < 1 || n_kept < 0 || n_kept > n_tokens) return SP_ERR_INVALID_ARGUMENT;
+  if (!isfinite(spec_tps) || !isfinite(target_tps) || !isfinite(safety))
+    return SP_ERR_INVALID_ARGUMENT;
+  const double spec = spec_tps > 0.0 ? spec_tps : 600.0;      // speculator tokens/s
+  const double target = target_tps > 0.0 ? target_tps : 270.0;  // target-model tokens/s
+  const double margin = safety > 0.0 ? safety : 1.2;
+  const double scoring_time = (double)n_tokens / spec;
+  const double saved_time = (double)(n_tokens - n_kept) / target;
+  *run = saved_time < scoring_time * margin ? 0 : 1;
+  return SP_OK;
+}
+
 }  // extern "C"

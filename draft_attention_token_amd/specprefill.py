@@ -36,7 +36,7 @@ SP_MAX_PROMPTS = 128
 EXPORTED = [
     "sp_abi_version", "sp_status_string", "sp_score_workspace_bytes", "sp_pool_workspace_bytes",
     "sp_select_workspace_bytes", "sp_gather_workspace_bytes", "sp_score_attention",
-    "sp_pool_chunk", "sp_select_chunks", "sp_gather_kept", "sp_score_status",
+    "sp_pool_chunk", "sp_select_chunks", "sp_gather_kept", "sp_score_status", "sp_break_even",
 ]
 
 _ALGOS = {"auto": SP_SCORE_AUTO, "two_pass": SP_SCORE_TWO_PASS, "stream": SP_SCORE_STREAM}
@@ -94,6 +94,8 @@ def lib():
                                        vp, vp, sz, vp]
         L.sp_gather_kept.argtypes = [bp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sp_score_status.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
+        L.sp_break_even.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                                    ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_int32)]
         for name in EXPORTED[2:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -236,6 +238,16 @@ def sp_score_attention(q: torch.Tensor, k: torch.Tensor, offsets, n_layers: int,
     _check(lib().sp_score_attention(ctypes.byref(desc), batch.ref(), _ptr(q), _ptr(k), _ptr(out),
                                     _ptr(ws), ws.numel(), _stream(dev)), "sp_score_attention")
     return out
+
+
+def break_even(n_tokens: int, n_kept: int, spec_tps: float = 0.0, target_tps: float = 0.0,
+               safety: float = 0.0) -> bool:
+    """Whether sparse prefill is estimated to save more than scoring costs
+    (sp_break_even; values <= 0 take the defaults 600 t/s, 270 t/s, 1.2)."""
+    run = ctypes.c_int32()
+    _check(lib().sp_break_even(int(n_tokens), int(n_kept), float(spec_tps), float(target_tps),
+                               float(safety), ctypes.byref(run)), "sp_break_even")
+    return bool(run.value)
 
 
 def score_status(ws: torch.Tensor) -> int:

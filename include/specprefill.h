@@ -11,6 +11,7 @@
  *   sp_pool_chunk       importance      -> token_scores[token], chunk_scores[chunk]
  *   sp_select_chunks    chunk_scores    -> keep[chunk], n_kept_chunks[prompt]
  *   sp_gather_kept      keep, token ids -> kept ids + original positions
+ *   sp_break_even       host-side estimate: is sparse prefill worth running?
  *
  * Sources (web pages on SpecPrefill):
  *   [G]  "SpecPrefill — Implementation Guide": How It Works (Core Algorithm,
@@ -232,6 +233,22 @@ sp_status sp_select_chunks(int32_t mode, double param, const sp_batch *batch, in
 sp_status sp_gather_kept(const sp_batch *batch, int32_t chunk_size, const uint8_t *keep,
                          const int32_t *token_ids, int32_t *kept_ids, int32_t *kept_pos,
                          int64_t *kept_offsets, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Break-even gate ([G] v3 Improvements item 4 and Configuration Reference:
+ * SP_BREAK_EVEN, SP_SPEC_THROUGHPUT, SP_BREAK_EVEN_SAFETY). Host arithmetic,
+ * no device work; a caller runs it before scoring, with the number of tokens
+ * it expects to keep. In double precision:
+ *   scoring_time = n_tokens / spec_tps
+ *   saved_time   = (n_tokens - n_kept) / target_tps
+ *   *run = 0 (skip sparse prefill) if saved_time < scoring_time * safety,
+ *          else 1.
+ * A value <= 0 selects the guide's default: spec_tps 600, target_tps 270,
+ * safety 1.2.
+ *   n_tokens >= 1, 0 <= n_kept <= n_tokens; arguments finite; run non-NULL.
+ */
+sp_status sp_break_even(int64_t n_tokens, int64_t n_kept, double spec_tps, double target_tps,
+                        double safety, int32_t *run);
 
 #ifdef __cplusplus
 }

@@ -224,3 +224,15 @@ def pipeline(inputs, mode: str = None, param: float = None, nthreads: int = 0, i
         out["kept_ids"].append(ki)
         out["kept_pos"].append(kp)
     return out
+
+
+def break_even(n_tokens: int, n_kept: int, spec_tps: float = 600.0, target_tps: float = 270.0,
+               safety: float = 1.2) -> bool:
+    """Break-even gate, "SpecPrefill — Implementation Guide", v3 Improvements
+    item 4 and Configuration Reference: scoring is estimated at n_tokens at the
+    speculator's rate, the saving at the dropped tokens at the target's rate;
+    sparse prefill runs unless the saving is below the scoring time times the
+    safety factor."""
+    scoring_time = n_tokens / spec_tps
+    saved_time = (n_tokens - n_kept) / target_tps
+    return not (saved_time < scoring_time * safety)

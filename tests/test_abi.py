@@ -208,3 +208,22 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(sp, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not found"):
         sp.lib()
+
+
+def test_break_even_matches_oracle_and_defaults():
+    import oracle
+    for n in (1, 600, 5400, 100000):
+        for f in (0.0, 0.3, 0.45, 0.46, 0.47, 0.9, 1.0):
+            kept = int(round(f * n))
+            assert sp.break_even(n, kept) == oracle.break_even(n, kept), (n, kept)
+            assert sp.break_even(n, kept, 995.0, 270.0, 1.5) == \
+                oracle.break_even(n, kept, 995.0, 270.0, 1.5), (n, kept)
+
+
+@pytest.mark.parametrize("args", [
+    (0, 0, 0, 0, 0), (10, 11, 0, 0, 0), (10, -1, 0, 0, 0), (10, 5, float("nan"), 0, 0),
+    (10, 5, 0, float("inf"), 0),
+])
+def test_break_even_rejects_bad_arguments(args):
+    run = ctypes.c_int32()
+    assert sp.lib().sp_break_even(*args, ctypes.byref(run)) == sp.SP_ERR_INVALID_ARGUMENT

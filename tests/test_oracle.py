@@ -591,3 +591,27 @@ def test_all_zero_q_gives_equal_chunk_scores():
     out = oracle.pipeline(inp)
     cs = out["chunk_scores"][0]
     np.testing.assert_allclose(cs, cs[0], rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# Break-even gate (host arithmetic)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n, kept, want", [
+    (600, 330, False),     # saves 270/270 = 1 s; scoring 600/600 = 1 s, x 1.2 = 1.2 s
+    (600, 0, True),        # saves 600/270 = 2.2 s > 1.2 s
+    (5400, 2700, False),   # saves 10 s; scoring 9 s, x 1.2 = 10.8 s
+    (5400, 2000, True),    # saves 3400/270 = 12.6 s > 10.8 s
+    (1, 1, False),         # nothing dropped
+])
+def test_break_even_hand_values(n, kept, want):
+    assert oracle.break_even(n, kept) == want
+
+
+def test_break_even_threshold_is_a_kept_fraction():
+    """Both times grow with n, so with the default rates the gate only
+    depends on the kept fraction f: run iff (1 - f) / 270 >= 1.2 / 600,
+    i.e. f <= 0.46."""
+    for n in (1000, 50000, 10 ** 7):
+        assert oracle.break_even(n, int(0.45 * n))
+        assert not oracle.break_even(n, int(0.47 * n))
