@@ -61,8 +61,8 @@ def lib():
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp,
                                          _dp]
         L.oracle_importance.argtypes = [ctypes.c_int, _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, _fp,
-                                        _fp, _dp,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_double, _fp, _fp, _dp,
                                         ctypes.c_int, _dp]
         L.oracle_pool_chunk.argtypes = [ctypes.c_int64, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double,
@@ -136,9 +136,11 @@ def softmax_row(offsets, q, k, n_layers, Hq, Hkv, d, L, scale, b, l, j, h,
 
 
 def importance(offsets, q, k, n_layers, Hq, Hkv, d, L, scale, nthreads: int = 0,
-               k_scales=None, prefill_row=False) -> np.ndarray:
+               k_scales=None, prefill_row=False, row_pool: int = 1) -> np.ndarray:
     """Importance of every prompt token, [sum N_b] fp64 (k_scales and
-    prefill_row: see softmax_row)."""
+    prefill_row: see softmax_row). row_pool = W > 1 pools every probability
+    row's prompt columns (centred, width W) before the max over heads and
+    layers."""
     off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
     qf, kf = _as_f32(q), _as_f32(k)
     ks = _scales(k_scales, n_layers * Hkv)
@@ -147,7 +149,7 @@ def importance(offsets, q, k, n_layers, Hq, Hkv, d, L, scale, nthreads: int = 0,
     assert qf.size == B * n_layers * (L + pre) * Hq * d, "q has the wrong size"
     assert kf.size == n_layers * (int(off[-1]) + B * L) * Hkv * d, "k has the wrong size"
     imp = np.empty(int(off[-1]), dtype=np.float64)
-    rc = lib().oracle_importance(B, _ptr(off, _i64p), n_layers, Hq, Hkv, d, L, pre, scale,
+    rc = lib().oracle_importance(B, _ptr(off, _i64p), n_layers, Hq, Hkv, d, L, pre, row_pool, scale,
                                  _ptr(qf, _fp), _ptr(kf, _fp), _ptr(imp, _dp), nthreads,
                                  None if ks is None else _ptr(ks, _dp))
     if rc != 0:
@@ -204,10 +206,12 @@ def pipeline(inputs, mode: str = None, param: float = None, nthreads: int = 0, i
     w = inputs.workload
     if mode is None:
         mode, param = w.select
+    # Pool-before-max pools the probability rows, and then not again.
+    row_pool, W = (w.pool_window, 1) if w.pool_before_max else (1, w.pool_window)
     if imp is None:
         imp = importance(inputs.offsets.numpy(), inputs.q, inputs.k, w.n_layers, w.n_q_heads,
                          w.n_kv_heads, w.head_dim, w.n_lookahead, inputs.scale, nthreads,
-                         k_scales=inputs.k_scales, prefill_row=w.prefill_row)
+                         k_scales=inputs.k_scales, prefill_row=w.prefill_row, row_pool=row_pool)
     off = inputs.offsets.numpy()
     ids = inputs.token_ids.numpy()
     fm, lm = (1.5, 1.3) if w.boost else (1.0, 1.0)
@@ -215,7 +219,7 @@ def pipeline(inputs, mode: str = None, param: float = None, nthreads: int = 0, i
            "kept_pos": []}
     for b in range(len(off) - 1):
         x = imp[off[b]:off[b + 1]]
-        ts, cs = pool_chunk(x, w.pool_window, w.chunk_size, w.normalize, 64, fm, 128, lm)
+        ts, cs = pool_chunk(x, W, w.chunk_size, w.normalize, 64, fm, 128, lm)
         keep = select(cs, mode, param)
         ki, kp = gather(keep, ids[off[b]:off[b + 1]], w.chunk_size)
         out["token_scores"].append(ts)

@@ -99,9 +99,32 @@ int oracle_softmax_row(int B, const int64_t *tok_off, int n_layers, int Hq,
 }
 
 /*
+ * Centred average pool of width W (odd) over in[0 .. n): each output is the
+ * mean of the inputs within (W - 1) / 2 positions that lie inside [0, n)
+ * (divided by their count). [PR] Approach step 3; the edge rule is the one
+ * oracle_pool_chunk states.
+ */
+static void box_mean(int64_t n, const double *in, int W, double *out) {
+  const int64_t r = (W - 1) / 2;
+  for (int64_t t = 0; t < n; t++) {
+    const int64_t lo = t - r < 0 ? 0 : t - r;
+    const int64_t hi = t + r > n - 1 ? n - 1 : t + r;
+    double s = 0.0;
+    for (int64_t i = lo; i <= hi; i++) s += in[i];
+    out[t] = s / (double)(hi - lo + 1);
+  }
+}
+
+/*
  * Token importance of every prompt token (steps: softmax rows, max over
  * heads, max over layers, mean over the S = L + pre steps; pre: see
  * oracle_softmax_row).
+ *
+ * Pool-before-max (row_pool = W > 1): [PR] Approach step 3 lists the
+ * smoothing before the max over heads and layers. In that order each
+ * probability row's prompt columns are pooled (box_mean, width W) before
+ * they enter the max; row_pool = 1 leaves the rows as they are (the pooling
+ * then happens once, later, on the importance: oracle_pool_chunk).
  *
  * [G] Token Importance and compute_imp: for each lookahead step, take the
  * maximum attention probability over all heads, then over all attention
@@ -116,11 +139,12 @@ int oracle_softmax_row(int B, const int64_t *tok_off, int n_layers, int Hq,
  * nthreads <= 0 uses the OpenMP default. Returns 0, or -1 on bad args.
  */
 int oracle_importance(int B, const int64_t *tok_off, int n_layers, int Hq,
-                      int Hkv, int d, int L, int pre, double scale, const float *q,
-                      const float *k, double *imp, int nthreads,
+                      int Hkv, int d, int L, int pre, int row_pool, double scale,
+                      const float *q, const float *k, double *imp, int nthreads,
                       const double *k_scales) {
   if (B <= 0 || n_layers <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
-      d <= 0 || L < 0 || pre < 0 || pre > 1 || L + pre <= 0)
+      d <= 0 || L < 0 || pre < 0 || pre > 1 || L + pre <= 0 || row_pool < 1 ||
+      row_pool % 2 == 0)
     return -1;
   const int S = L + pre;
   const int64_t total_tok = tok_off[B];
@@ -143,17 +167,24 @@ int oracle_importance(int B, const int64_t *tok_off, int n_layers, int Hq,
       const int64_t N = tok_off[b + 1] - tok_off[b];
       double *sm = stepmax + tok_off[b] * S + (int64_t)j * N;
       double *p = (double *)malloc(sizeof(double) * (size_t)(N + L));
-      if (!p) { err |= 1; continue; }
+      double *pooled = (double *)malloc(sizeof(double) * (size_t)N);
+      if (!p || !pooled) { free(p); free(pooled); err |= 1; continue; }
       for (int64_t kk = 0; kk < N; kk++) sm[kk] = 0.0; /* probabilities are >= 0 */
       for (int l = 0; l < n_layers; l++) {
         for (int h = 0; h < Hq; h++) {
           oracle_softmax_row(B, tok_off, n_layers, Hq, Hkv, d, L, pre, scale, q, k,
                              b, l, j, h, p, k_scales);
+          const double *row = p;
+          if (row_pool > 1) {  /* the row's prompt columns only */
+            box_mean(N, p, row_pool, pooled);
+            row = pooled;
+          }
           for (int64_t kk = 0; kk < N; kk++)  /* prompt columns only */
-            if (p[kk] > sm[kk]) sm[kk] = p[kk];
+            if (row[kk] > sm[kk]) sm[kk] = row[kk];
         }
       }
       free(p);
+      free(pooled);
     }
   }
   if (!err) {
@@ -197,16 +228,9 @@ int oracle_pool_chunk(int64_t n, const double *imp, int W, int C, int normalize,
                       double last_mult, double *token_scores,
                       double *chunk_scores) {
   if (n <= 0 || W < 1 || W % 2 == 0 || C < 1) return -1;
-  const int64_t r = (W - 1) / 2;
   double *x = (double *)malloc(sizeof(double) * (size_t)n);
   if (!x) return -1;
-  for (int64_t t = 0; t < n; t++) {
-    const int64_t lo = t - r < 0 ? 0 : t - r;
-    const int64_t hi = t + r > n - 1 ? n - 1 : t + r;
-    double s = 0.0;
-    for (int64_t i = lo; i <= hi; i++) s += imp[i];
-    x[t] = s / (double)(hi - lo + 1);
-  }
+  box_mean(n, imp, W, x);
   if (normalize) {
     double mn = x[0], mx = x[0];
     for (int64_t t = 1; t < n; t++) {

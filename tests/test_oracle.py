@@ -170,6 +170,96 @@ def test_importance_prompts_are_independent():
 
 
 # ----------------------------------------------------------------------------
+# Pool-before-max: each probability row pooled before the head/layer max
+# ----------------------------------------------------------------------------
+
+def _box_counts(n, W):
+    """Centred window sums via numpy.convolve ("full", then the centred
+    slice, which also holds for n < W), divided by the in-range count."""
+    ones, r = np.ones(W), (W - 1) // 2
+    cnt = np.convolve(np.ones(n), ones)[r:r + n]
+    return lambda x: np.convolve(x, ones)[r:r + n] / cnt
+
+
+def test_row_pool_width_one_is_the_plain_importance():
+    rng = np.random.default_rng(31)
+    off, q, k = _rand_problem(rng, [30, 11], 2, 4, 2, 8, 3, scale_q=2.0)
+    a = oracle.importance(off, q, k, 2, 4, 2, 8, 3, 0.4)
+    b = oracle.importance(off, q, k, 2, 4, 2, 8, 3, 0.4, row_pool=1)
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("W", [3, 13])
+def test_row_pool_matches_bruteforce(W):
+    """Dense softmax, numpy.convolve on each row's prompt columns, then the
+    max over heads and layers and the mean over steps."""
+    rng = np.random.default_rng(32)
+    n_layers, Hq, Hkv, d, L = 2, 8, 2, 8, 3
+    lengths = [40, 5, 19]
+    off, q, k = _rand_problem(rng, lengths, n_layers, Hq, Hkv, d, L, scale_q=3.0)
+    scale = 1 / math.sqrt(d)
+    got = oracle.importance(off, q, k, n_layers, Hq, Hkv, d, L, scale, row_pool=W)
+    G = Hq // Hkv
+    for b, n in enumerate(lengths):
+        k0 = int(off[b]) + b * L
+        kb = np.repeat(k[:, k0:k0 + n + L].astype(np.float64), G, axis=2)
+        s = np.einsum("ljhd,lkhd->ljhk", q[b].astype(np.float64), kb) * scale
+        vis = np.arange(n + L)[None, :] <= (n + np.arange(L))[:, None]
+        s = np.where(vis[None, :, None, :], s, -np.inf)
+        p = scipy.special.softmax(s, axis=-1)[..., :n]
+        pool = _box_counts(n, W)
+        pooled = np.apply_along_axis(pool, -1, p)
+        want = pooled.max(axis=2).max(axis=0).mean(axis=0)
+        np.testing.assert_allclose(got[off[b]:off[b + 1]], want, rtol=1e-12, atol=1e-15)
+
+
+def test_row_pool_all_zero_q_keeps_the_uniform_closed_form():
+    """Uniform rows stay uniform under a count-normalised pool."""
+    rng = np.random.default_rng(33)
+    lengths, L = [50, 7], 4
+    off, q, k = _rand_problem(rng, lengths, 2, 4, 1, 8, L)
+    q[:] = 0
+    imp = oracle.importance(off, q, k, 2, 4, 1, 8, L, 0.25, row_pool=13)
+    for b, n in enumerate(lengths):
+        want = sum(1.0 / (n + j + 1) for j in range(L)) / L
+        np.testing.assert_allclose(imp[off[b]:off[b + 1]], want, rtol=1e-13)
+
+
+def test_row_pool_single_hot_key_closed_form():
+    """One hot key k0 (logit a) seen by the group-0 heads only. Group-0 rows:
+    p(k0) = e^a / D_j, every other key 1 / D_j, with D_j = e^a + N + j. Pooled
+    with W = 13, a key within 6 of k0 averages (e^a + 12) / (13 D_j) (interior
+    keys); farther keys stay at 1 / D_j, below group 1's uniform 1/(N + j + 1),
+    which the max then picks."""
+    n, L, d, a, k0, W = 60, 3, 8, 3.0, 30, 13
+    off = np.array([0, n], dtype=np.int64)
+    q = np.zeros((1, 1, L, 4, d), dtype=np.float32)   # 1 layer, Hq=4, Hkv=2
+    k = np.zeros((1, n + L, 2, d), dtype=np.float32)
+    k[0, k0, 0, 0] = 1.0
+    q[0, 0, :, 0:2, 0] = a
+    imp = oracle.importance(off, q, k, 1, 4, 2, d, L, 1.0, row_pool=W)
+    ea = math.exp(a)
+    near = sum(max((ea + 12) / (13 * (ea + n + j)), 1.0 / (n + j + 1)) for j in range(L)) / L
+    far = sum(1.0 / (n + j + 1) for j in range(L)) / L
+    assert (ea + 12) / 13 > 1.0                       # the pooled hot window wins the max
+    for kk in range(n):
+        want = near if abs(kk - k0) <= 6 else far
+        assert abs(imp[kk] - want) < 1e-14, kk
+
+
+def test_row_pool_differs_from_pool_after():
+    """The two orders are different functions (the max does not commute with
+    the pool): on random rows they disagree."""
+    rng = np.random.default_rng(34)
+    off, q, k = _rand_problem(rng, [80], 2, 8, 2, 8, 4, scale_q=3.0)
+    before = oracle.importance(off, q, k, 2, 8, 2, 8, 4, 0.35, row_pool=13)
+    after, _ = oracle.pool_chunk(oracle.importance(off, q, k, 2, 8, 2, 8, 4, 0.35), 13, 32,
+                                 False, 0, 1.0, 0, 1.0)
+    assert np.abs(before - after).max() > 1e-4
+    assert np.all(before <= after + 1e-15)   # max of means <= mean of maxes
+
+
+# ----------------------------------------------------------------------------
 # Prefill row: the prompt's own last row as one more step in front
 # ----------------------------------------------------------------------------
 

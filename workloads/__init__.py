@@ -66,6 +66,7 @@ class Workload:
     ragged_range: tuple = (2048, 65536)
     k_fp8: bool = False               # K as fp8 e4m3 codes + per-(layer, KV head) scales
     prefill_row: bool = False         # one more query step: the prompt's last row
+    pool_before_max: bool = False     # pool each probability row before the head/layer max
 
     @property
     def group(self) -> int:
@@ -116,6 +117,13 @@ WORKLOADS = {
     "n32k_prerow_bf16": Workload("n32k_prerow_bf16", (32768,), 6, 16, 4, 128, 7,
                                  torch.bfloat16, 1003, 20, None,
                                  also_select=(("top_p", 0.15),), prefill_row=True),
+    # Pool-before-max: the W = 13 pool moves onto every probability row.
+    "n3212_poolmax_bf16": Workload("n3212_poolmax_bf16", (3212,), 6, 16, 4, 128, 8,
+                                   torch.bfloat16, 1002, 5, 2.0, select=("top_p", 0.30),
+                                   also_select=(("mass", 0.85),), pool_before_max=True),
+    "n128k_poolmax_bf16": Workload("n128k_poolmax_bf16", (131072,), 6, 16, 4, 128, 8,
+                                   torch.bfloat16, 1004, 64, None,
+                                   also_select=(("top_p", 0.15),), pool_before_max=True),
 }
 
 
