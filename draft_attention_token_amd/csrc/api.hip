@@ -77,6 +77,8 @@ sp_status check_attn(const sp_attn_desc *d, AttnShape *s) {
     return SP_ERR_INVALID_ARGUMENT;
   if (d->prefill_row != 0 && d->prefill_row != 1) return SP_ERR_INVALID_ARGUMENT;
   if (d->n_lookahead + d->prefill_row < 1) return SP_ERR_INVALID_ARGUMENT;
+  if (d->row_pool < 0 || (d->row_pool > 1 && d->row_pool % 2 == 0)) return SP_ERR_INVALID_ARGUMENT;
+  if (d->row_pool > kMaxRowPool) return SP_ERR_UNSUPPORTED;
   if (d->n_q_heads % d->n_kv_heads != 0) return SP_ERR_INVALID_ARGUMENT;
   if (d->dtype != SP_DTYPE_F32 && d->dtype != SP_DTYPE_BF16 && d->dtype != SP_DTYPE_BF16_FP8K)
     return SP_ERR_INVALID_ARGUMENT;
@@ -85,6 +87,8 @@ sp_status check_attn(const sp_attn_desc *d, AttnShape *s) {
   if (d->head_dim != 64 && d->head_dim != 128) return SP_ERR_UNSUPPORTED;
   const int G = d->n_q_heads / d->n_kv_heads;
   if ((int64_t)(d->n_lookahead + d->prefill_row) * G > kRows) return SP_ERR_UNSUPPORTED;
+  if (d->row_pool > 1 && (d->algo == SP_SCORE_STREAM || d->dtype == SP_DTYPE_BF16_FP8K))
+    return SP_ERR_UNSUPPORTED;                                      // two-pass kernels only
   if (d->dtype == SP_DTYPE_BF16_FP8K) {
     if (d->algo == SP_SCORE_TWO_PASS) return SP_ERR_UNSUPPORTED;   // single-pass only
     if ((int64_t)d->n_layers * d->n_kv_heads > kMaxScaledProblems) return SP_ERR_UNSUPPORTED;
@@ -97,6 +101,7 @@ sp_status check_attn(const sp_attn_desc *d, AttnShape *s) {
   s->G = G;
   s->La = d->n_lookahead;
   s->pre = d->prefill_row;
+  s->row_pool = d->row_pool > 1 ? d->row_pool : 1;
   s->scale_log2 = d->scale * kLog2e;
   s->dtype = d->dtype;
   return SP_OK;

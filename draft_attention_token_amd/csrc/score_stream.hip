@@ -839,6 +839,7 @@ size_t die_region(const AttnShape &s) {
 
 bool score_stream_supported(const AttnShape &s) {
   if (s.dtype != SP_DTYPE_BF16 && s.dtype != SP_DTYPE_BF16_FP8K) return false;
+  if (s.row_pool > 1) return false;                   // pool-before-max: two-pass kernels
   if (s.G & (s.G - 1)) return false;                 // head groups of 2^k lanes
   return true;
 }

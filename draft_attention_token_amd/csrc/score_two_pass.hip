@@ -133,6 +133,85 @@ __global__ __launch_bounds__(64) void k_score(AttnShape s, SegTable tiles, int64
   }
 }
 
+// Pass 2, pool-before-max form ("Speculative prefill", Approach step 3, read
+// with the smoothing first): every (layer, head) probability row is pooled
+// over its prompt keys (centred window of W = 2 r + 1 keys, divided by the
+// number of prompt keys inside it) before the max over heads and layers.
+// A block owns one 32-key output tile at k0 and computes the probabilities
+// of keys [k0 - 16, k0 + 48) as two logit tiles (the window's reach is at
+// most 16 keys each side), parks them in LDS, and sums each output key's
+// window there: every window sum adds its terms afresh (no running sum that
+// subtracts, which would cancel near a large probability).
+// Blocks take tiles die by die (block i runs on die i % 8 and gets the i / 8-th
+// tile of that die's contiguous share), so neighbouring tiles, which read each
+// other's halo keys, meet in the same L2.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void k_score_pooled(AttnShape s, SegTable tiles,
+                                                     int64_t total_keys, int total_tiles,
+                                                     const T *__restrict__ q,
+                                                     const T *__restrict__ k,
+                                                     const float *__restrict__ lse,
+                                                     float *__restrict__ imp) {
+  __shared__ float pv[kPoolSpan][kRows + 1];   // [key - (k0 - kPoolHalo)][row], padded
+  __shared__ unsigned smax[kRows][kTile];
+  const int per = (total_tiles + 7) / 8;
+  const int t = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (t >= total_tiles) return;
+  const int b = seg_of(tiles, t);
+  const int N = tiles.tok_off[b + 1] - tiles.tok_off[b];
+  const int k0 = (t - tiles.unit_off[b]) * kTile;   // first output key (prompt-local)
+  if (k0 >= N) return;                               // a tile of lookahead keys only
+  const int64_t key0 = tiles.tok_off[b] + (int64_t)b * tiles.L;
+  const int lane = threadIdx.x, half = lane >> 5, col = lane & 31;
+  for (int i = lane; i < kRows * kTile; i += 64) (&smax[0][0])[i] = 0u;
+  const int n_prob = s.n_layers * s.Hkv, rows = s.L * s.G;
+  const int r = (s.row_pool - 1) / 2;
+  // The lane's 16 output keys for row `col` in the pooling step.
+  const int c0 = 16 * half;
+  for (int prob = 0; prob < n_prob; ++prob) {
+    const int l = prob / s.Hkv, g = prob - l * s.Hkv;
+    Frag<T, D> a;
+    if (col < rows) a.load_cached(q_row_ptr(q, s, b, l, g, col), half); else a.zero();
+    const float *lrow = lse + ((int64_t)b * n_prob + prob) * kRows;
+    float lr[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = acc_row(i, half);
+      lr[i] = row < rows ? lrow[row] : INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < kPoolSpan / kTile; ++u) {
+      const int kl = k0 - kPoolHalo + kTile * u + col;   // this lane's key column
+      const bool need = kl >= 0 && kl < N && kl >= k0 - r && kl < k0 + kTile + r;
+      Frag<T, D> bk;
+      if (need) bk.load(k_row_ptr(k, s, total_keys, l, key0 + kl, g), half); else bk.zero();
+      const f32x16 acc = mfma_tile<D>(a, bk);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = need ? exp2f(acc[i] * s.scale_log2 - lr[i]) : 0.f;   // 0 for padding rows
+        pv[kTile * u + col][acc_row(i, half)] = p;
+      }
+    }
+    __syncthreads();
+    if (col < rows) {
+      for (int c = c0; c < c0 + 16; ++c) {
+        const int kk = k0 + c;
+        if (kk >= N) break;
+        float w = 0.f;
+        for (int x = kk - r; x <= kk + r; ++x) w += pv[x - (k0 - kPoolHalo)][col];
+        const int lo = max(0, kk - r), hi = min(N - 1, kk + r);
+        atomicMax(&smax[col / s.G][c], __float_as_uint(w / (float)(hi - lo + 1)));
+      }
+    }
+    __syncthreads();
+  }
+  if (lane < kTile && k0 + lane < N) {
+    float acc = 0.f;
+    for (int j = 0; j < s.L; ++j) acc += __uint_as_float(smax[j][lane]);
+    imp[tiles.tok_off[b] + k0 + lane] = acc / (float)s.L;
+  }
+}
+
 template <typename T, int D>
 hipError_t run(const AttnShape &s, const SegTable &tiles, int total_tiles, const void *q,
                const void *k, float *imp, uint32_t *hdr, void *region, hipStream_t st) {
@@ -145,8 +224,12 @@ hipError_t run(const AttnShape &s, const SegTable &tiles, int total_tiles, const
                      total_keys, total_tiles, (const T *)q, (const T *)k, part);
   hipLaunchKernelGGL(k_lse, dim3(tiles.B, n_prob), dim3(256), 0, st, tiles, n_prob, total_tiles,
                      part, lse, hdr, reserve_tags(1));
-  hipLaunchKernelGGL((k_score<T, D>), dim3(total_tiles), dim3(64), 0, st, s, tiles, total_keys,
-                     (const T *)q, (const T *)k, lse, imp);
+  if (s.row_pool > 1)
+    hipLaunchKernelGGL((k_score_pooled<T, D>), dim3((total_tiles + 7) / 8 * 8), dim3(64), 0, st, s,
+                       tiles, total_keys, total_tiles, (const T *)q, (const T *)k, lse, imp);
+  else
+    hipLaunchKernelGGL((k_score<T, D>), dim3(total_tiles), dim3(64), 0, st, s, tiles, total_keys,
+                       (const T *)q, (const T *)k, lse, imp);
   return hipGetLastError();
 }
 

@@ -16,6 +16,11 @@ constexpr size_t kAlign = 256;
 // cross-block wait timed out. Every call gets fresh tags (reserve_tags).
 constexpr size_t kStatusBytes = 256;
 constexpr float kLog2e = 1.4426950408889634f;
+// Pool-before-max: probabilities of kPoolHalo keys each side of a 32-key
+// output tile are on chip, so a row pool reaches at most that far.
+constexpr int kPoolHalo = 16;
+constexpr int kPoolSpan = 64;                     // kTile + 2 * kPoolHalo
+constexpr int kMaxRowPool = 2 * kPoolHalo + 1;
 
 // Per-prompt prefix table passed to kernels by value (about 1 KB). unit_off
 // holds a host-computed prefix of per-prompt unit counts (tiles, chunks or
@@ -46,6 +51,7 @@ struct AttnShape {
   int G;
   int La;                           // lookahead keys per prompt (K rows past the prompt)
   int pre;                          // 1: step 0 is the prompt's last row (position N - 1)
+  int row_pool;                     // 1, or odd W > 1: pool each probability row first
   float scale_log2;                 // scale * log2(e): logits kept in base-2 units
   int dtype;
 };

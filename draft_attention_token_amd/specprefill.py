@@ -58,7 +58,8 @@ class sp_attn_desc(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("n_lookahead", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("algo", ctypes.c_int32),
-                ("k_scales", ctypes.POINTER(ctypes.c_float)), ("prefill_row", ctypes.c_int32)]
+                ("k_scales", ctypes.POINTER(ctypes.c_float)), ("prefill_row", ctypes.c_int32),
+                ("row_pool", ctypes.c_int32)]
 
 
 class sp_pool_desc(ctypes.Structure):
@@ -151,11 +152,13 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 
 
 def attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype, scale=None,
-              algo="auto", k_dtype=None, k_scales=None, prefill_row=False) -> sp_attn_desc:
+              algo="auto", k_dtype=None, k_scales=None, prefill_row=False,
+              row_pool=1) -> sp_attn_desc:
     """dtype: Q's torch dtype (and K's unless k_dtype says otherwise).
     k_dtype=torch.float8_e4m3fn with bf16 Q selects fp8 K codes; k_scales
     is then the [n_layers * n_kv_heads] fp32 host array of key scales.
-    prefill_row: Q carries one more step in front, the prompt's last row."""
+    prefill_row: Q carries one more step in front, the prompt's last row.
+    row_pool: odd W > 1 pools every probability row before the max."""
     if k_dtype is None or k_dtype == dtype:
         dt = {torch.float32: SP_DTYPE_F32, torch.bfloat16: SP_DTYPE_BF16}.get(dtype, -1)
     elif dtype == torch.bfloat16 and k_dtype == torch.float8_e4m3fn:
@@ -166,7 +169,8 @@ def attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype, sca
         scale = 1.0 / math.sqrt(head_dim)
     desc = sp_attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dt, float(scale),
                         _ALGOS[algo] if isinstance(algo, str) else int(algo), None,
-                        int(prefill_row) if isinstance(prefill_row, (bool, int)) else -1)
+                        int(prefill_row) if isinstance(prefill_row, (bool, int)) else -1,
+                        int(row_pool))
     if k_scales is not None:
         ks = np.ascontiguousarray(np.asarray(
             k_scales.cpu() if isinstance(k_scales, torch.Tensor) else k_scales,
@@ -213,14 +217,15 @@ def sp_score_attention(q: torch.Tensor, k: torch.Tensor, offsets, n_layers: int,
                        n_kv_heads: int, head_dim: int, n_lookahead: int, scale=None,
                        algo="auto", out: Optional[torch.Tensor] = None,
                        ws: Optional[torch.Tensor] = None, k_scales=None,
-                       prefill_row=False) -> torch.Tensor:
+                       prefill_row=False, row_pool=1) -> torch.Tensor:
     """Token importance [sum N_b] fp32 (see the C header for layouts). K may
     be fp8 e4m3 codes with bf16 Q; k_scales ([n_layers * n_kv_heads]) then
     gives each (layer, KV head)'s key scale. prefill_row: q holds
     n_lookahead + 1 steps, the first the prompt's last row."""
     batch = offsets if isinstance(offsets, Batch) else Batch(offsets)
     desc = attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, q.dtype, scale, algo,
-                     k_dtype=k.dtype, k_scales=k_scales, prefill_row=prefill_row)
+                     k_dtype=k.dtype, k_scales=k_scales, prefill_row=prefill_row,
+                     row_pool=row_pool)
     steps = n_lookahead + int(bool(prefill_row))
     if not (q.is_contiguous() and k.is_contiguous()):
         raise ValueError("q and k must be contiguous")
@@ -335,13 +340,14 @@ class Pipeline:
     def __init__(self, offsets, n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype,
                  device, W=13, C=32, normalize=True, boost=True, mode="mass", param=0.85,
                  algo="auto", scale=None, token_scores=True, k_dtype=None, k_scales=None,
-                 prefill_row=False):
+                 prefill_row=False, pool_before_max=False):
         self.batch = offsets if isinstance(offsets, Batch) else Batch(offsets)
         fm, lm = (1.5, 1.3) if boost else (1.0, 1.0)
         self.adesc = attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype,
                                scale, algo, k_dtype=k_dtype, k_scales=k_scales,
-                               prefill_row=prefill_row)
-        self.pdesc = pool_desc(W, C, normalize, 64, fm, 128, lm)
+                               prefill_row=prefill_row, row_pool=W if pool_before_max else 1)
+        # Pool-before-max pools the probability rows inside the scoring call.
+        self.pdesc = pool_desc(1 if pool_before_max else W, C, normalize, 64, fm, 128, lm)
         self.C, self.mode, self.param = C, _MODES[mode], float(param)
         self.shape = (n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead)
         B, T, nc = self.batch.B, self.batch.total, self.batch.n_chunks(C)

@@ -109,6 +109,8 @@ typedef struct {
                             SP_DTYPE_BF16_FP8K only (n_layers * n_kv_heads
                             <= 128); NULL otherwise */
   int32_t prefill_row;  /* 0 or 1: step 0 is the prompt's last row */
+  int32_t row_pool;     /* 0 or 1: off. Odd W in 3..33: pool-before-max, see
+                           sp_score_attention; two-pass kernels, bf16 or f32 K */
 } sp_attn_desc;
 
 /* Smoothing, normalisation, boosts and chunking ([PR] Approach step 3;
@@ -144,6 +146,12 @@ sp_status sp_gather_workspace_bytes(const sp_batch *batch, int32_t chunk_size, s
  * with logits scale * <q, k> against the key head h / G. Only the prompt
  * columns go forward ([G] capture callback).
  *   importance[b][k] = (1/S) * sum_j max_{l, h} p[b][l][j][h][k],  k < N_b
+ * Pool-before-max (row_pool = W > 1; [PR] Approach step 3 lists the
+ * smoothing before the max over heads and layers): each row's prompt
+ * columns are first replaced by their centred W-key means over the prompt
+ * keys inside the window (divided by that count),
+ *   importance[b][k] = (1/S) * sum_j max_{l, h} pool_W(p[b][l][j][h])[k];
+ * the caller then pools no more (sp_pool_chunk with pool_window 1).
  *
  *   q:  [B][n_layers][S][Hq][d] of dtype (bf16 for SP_DTYPE_BF16_FP8K),
  *       contiguous; S = L + prefill_row, step 0 the prefill row if any.

@@ -66,6 +66,12 @@ def _desc(**kw):
     (dict(n_lookahead=-1), sp.SP_ERR_INVALID_ARGUMENT),
     (dict(prefill_row=2), sp.SP_ERR_INVALID_ARGUMENT),
     (dict(n_lookahead=8, prefill_row=True), sp.SP_ERR_UNSUPPORTED),   # (8 + 1) * 4 > 32
+    (dict(row_pool=-1), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(row_pool=12), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(row_pool=35), sp.SP_ERR_UNSUPPORTED),
+    (dict(row_pool=13, algo="stream"), sp.SP_ERR_UNSUPPORTED),
+    (dict(row_pool=13, dtype=torch.bfloat16, k_dtype=torch.float8_e4m3fn, k_scales=[0.01] * 24),
+     sp.SP_ERR_UNSUPPORTED),
 ])
 def test_score_rejects_bad_descriptors(kw, want):
     assert _score(_desc(**kw), sp.Batch([0, 100])) == want
