@@ -177,7 +177,8 @@ def main():
     pipe = sp.Pipeline(inp.offsets, w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim,
                        w.n_lookahead, w.dtype, dev, W=w.pool_window, C=w.chunk_size,
                        normalize=w.normalize, boost=w.boost, mode=mode, param=param,
-                       algo=args.algo, k_dtype=inp.k.dtype, k_scales=inp.k_scales)
+                       algo=args.algo, k_dtype=inp.k.dtype, k_scales=inp.k_scales,
+                       prefill_row=w.prefill_row, pool_before_max=w.pool_before_max)
     fp8k = inp.k.dtype == torch.float8_e4m3fn
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -245,10 +246,13 @@ def main():
                    "chunk": w.chunk_size, "normalize": w.normalize, "boost": w.boost,
                    "select": f"{mode} {param}", "score_algo": args.algo, "kept_tokens": kept,
                    "k_cache": "fp8 e4m3 codes, fp32 scale per (layer, KV head)" if fp8k
-                   else "same type as Q"},
+                   else "same type as Q",
+                   "prefill_row": w.prefill_row, "pool_before_max": w.pool_before_max},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": f"k_stream<{w.head_dim}, fp8 K={fp8k}> (sp_score_attention)",
+                     "kernel": ("k_stats + k_lse + k_score_pooled (sp_score_attention)"
+                                if w.pool_before_max else
+                                f"k_stream<{w.head_dim}, fp8 K={fp8k}> (sp_score_attention)"),
                      "launch_us": ms_score * 1e3,
                      "algorithmic_bytes": alg_bytes,
                      "achievable": {"read": read_gbs, "frac": achieved / read_gbs,

@@ -139,9 +139,10 @@ __global__ __launch_bounds__(64) void k_score(AttnShape s, SegTable tiles, int64
 // number of prompt keys inside it) before the max over heads and layers.
 // A block owns one 32-key output tile at k0 and computes the probabilities
 // of keys [k0 - 16, k0 + 48) as two logit tiles (the window's reach is at
-// most 16 keys each side), parks them in LDS, and sums each output key's
-// window there: every window sum adds its terms afresh (no running sum that
-// subtracts, which would cancel near a large probability).
+// most 16 keys each side) and parks them in LDS; a lane then reads one row's
+// 48 probabilities around its 16 output keys into registers and adds each
+// window afresh (no running sum that subtracts, which would cancel near a
+// large probability).
 // Blocks take tiles die by die (block i runs on die i % 8 and gets the i / 8-th
 // tile of that die's contiguous share), so neighbouring tiles, which read each
 // other's halo keys, meet in the same L2.
@@ -194,13 +195,21 @@ __global__ __launch_bounds__(64) void k_score_pooled(AttnShape s, SegTable tiles
     }
     __syncthreads();
     if (col < rows) {
-      for (int c = c0; c < c0 + 16; ++c) {
-        const int kk = k0 + c;
-        if (kk >= N) break;
+      // The row's probabilities of keys k0 + c0 - 16 .. k0 + c0 + 31 (pv rows
+      // c0 .. c0 + 47), all read up front; each window sum then adds its
+      // terms in key order, zeros outside the window.
+      float v[kTile / 2 + 2 * kPoolHalo];
+#pragma unroll
+      for (int x = 0; x < kTile / 2 + 2 * kPoolHalo; ++x) v[x] = pv[c0 + x][col];
+#pragma unroll
+      for (int c = 0; c < kTile / 2; ++c) {
         float w = 0.f;
-        for (int x = kk - r; x <= kk + r; ++x) w += pv[x - (k0 - kPoolHalo)][col];
+#pragma unroll
+        for (int o = -kPoolHalo; o <= kPoolHalo; ++o)
+          w += (o >= -r && o <= r) ? v[c + kPoolHalo + o] : 0.f;
+        const int kk = k0 + c0 + c;
         const int lo = max(0, kk - r), hi = min(N - 1, kk + r);
-        atomicMax(&smax[col / s.G][c], __float_as_uint(w / (float)(hi - lo + 1)));
+        if (kk < N) atomicMax(&smax[col / s.G][c0 + c], __float_as_uint(w / (float)(hi - lo + 1)));
       }
     }
     __syncthreads();
