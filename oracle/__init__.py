@@ -22,6 +22,7 @@ pages; there they rest on the pins above.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -240,3 +241,113 @@ def break_even(n_tokens: int, n_kept: int, spec_tps: float = 600.0, target_tps: 
     scoring_time = n_tokens / spec_tps
     saved_time = (n_tokens - n_kept) / target_tps
     return not (saved_time < scoring_time * safety)
+
+
+# ----------------------------------------------------------------------------
+# Standalone-tool semantics: sliding windows, legacy chunk selection, thinning
+# ("SpecPrefill — Implementation Guide": Sliding Window, v3.1 Optimizations &
+# Bug Fixes items 6-7, Sliding Window Loop (v3.1 — fixed), Configuration
+# Reference, and the chunk-selection and main-loop parts of Full Source Code).
+# ----------------------------------------------------------------------------
+
+def window_plan(n_tokens: int, window: int, stride: int):
+    """Windows of the v3.1 loop as (start, length, keep) triples.
+
+    A window starts at pos (0, then every stride) and spans
+    min(window, n_tokens - pos) tokens. It is the last one when it reaches
+    the end of the prompt or when the next start would (pos + stride >=
+    n_tokens); the loop stops after it. Every window keeps the scores of
+    its first `stride` tokens, the last one keeps all of its tokens.
+    """
+    assert n_tokens >= 1 and window >= 1 and 1 <= stride <= window
+    plan, pos = [], 0
+    while pos < n_tokens:
+        end = min(pos + window, n_tokens)
+        last = end >= n_tokens or pos + stride >= n_tokens
+        plan.append((pos, end - pos, end - pos if last else stride))
+        if last:
+            break
+        pos += stride
+    return plan
+
+
+def stitch(plan, window_scores, n_tokens: int) -> np.ndarray:
+    """Prompt scores from per-window scores: each window adds its kept
+    tokens' scores, overlaps are averaged, and a token no window scored gets
+    1.0 (the guide's default)."""
+    acc = np.zeros(n_tokens)
+    cnt = np.zeros(n_tokens, dtype=np.int64)
+    for (start, length, keep), ws in zip(plan, window_scores):
+        ws = np.asarray(ws, dtype=np.float64)
+        assert ws.size == length
+        acc[start:start + keep] += ws[:keep]
+        cnt[start:start + keep] += 1
+    out = np.ones(n_tokens)
+    m = cnt > 0
+    out[m] = acc[m] / cnt[m]
+    return out
+
+
+def legacy_keep_count(n_chunks: int, keep_pct: float) -> int:
+    """Chunks the legacy rule ranks in: ceil(n_chunks * keep_pct), at least
+    one, with the fraction and the product in single precision (the tool
+    reads the fraction into a float)."""
+    prod = np.float32(n_chunks) * np.float32(keep_pct)
+    return max(1, int(math.ceil(float(prod))))
+
+
+def select_legacy(scores, chunk_size: int = 32, keep_pct: float = 0.3,
+                  min_tokens: int = 128) -> np.ndarray:
+    """Kept token indices, ascending, by the standalone tool's chunk rule.
+
+    - effective minimum: min(min_tokens, max(4, n // 10)); if keep_pct >= 1
+      or the prompt is no longer than it, every token is kept;
+    - chunk means over the tokens each chunk holds (sums in double, the mean
+      rounded to single precision);
+    - threshold: the kc-th largest chunk mean (kc from legacy_keep_count);
+      every chunk whose mean reaches it is kept, ties included;
+    - tokens 0-3 and, when there are more than 4 tokens, the last two are
+      always kept;
+    - while fewer than the effective minimum are kept, tokens of the chunks
+      below the threshold are added in index order.
+    """
+    x = np.asarray(scores, dtype=np.float64)
+    n = x.size
+    eff_min = min(min_tokens, max(4, n // 10))
+    if keep_pct >= 1.0 or n <= eff_min:
+        return np.arange(n, dtype=np.int64)
+    nc = (n + chunk_size - 1) // chunk_size
+    means = np.array([np.float32(x[c * chunk_size:min(n, (c + 1) * chunk_size)].sum()
+                                 / (min(n, (c + 1) * chunk_size) - c * chunk_size))
+                      for c in range(nc)], dtype=np.float32)
+    kc = legacy_keep_count(nc, keep_pct)
+    th = np.sort(means)[::-1][kc - 1]
+    kept = set()
+    for c in range(nc):
+        if means[c] >= th:
+            kept.update(range(c * chunk_size, min(n, (c + 1) * chunk_size)))
+    always = [0, 1, 2, 3] + ([n - 2, n - 1] if n > 4 else [])
+    kept.update(a for a in always if a < n)
+    for c in range(nc):
+        if len(kept) >= eff_min:
+            break
+        if means[c] < th:
+            for t in range(c * chunk_size, min(n, (c + 1) * chunk_size)):
+                if len(kept) >= eff_min:
+                    break
+                kept.add(t)
+    return np.array(sorted(kept), dtype=np.int64)
+
+
+def thin(kept, max_keep: int) -> np.ndarray:
+    """The tool's cap on tokens sent to the target: above max_keep kept
+    tokens, keep every step-th one (step = count // max_keep) up to max_keep
+    of them, the last of which is replaced by the final kept token."""
+    kept = np.asarray(kept, dtype=np.int64)
+    k = kept.size
+    if k <= max_keep:
+        return kept.copy()
+    step = k // max_keep
+    out = kept[::step][:max_keep].copy()
+    out[-1] = kept[-1]
+    return out

@@ -705,3 +705,116 @@ def test_break_even_threshold_is_a_kept_fraction():
     for n in (1000, 50000, 10 ** 7):
         assert oracle.break_even(n, int(0.45 * n))
         assert not oracle.break_even(n, int(0.47 * n))
+
+
+# ----------------------------------------------------------------------------
+# Standalone-tool semantics: window plan, stitching, legacy selection, thinning
+# ----------------------------------------------------------------------------
+
+def test_window_plan_worked_example_from_the_guide():
+    lines = [l.split() for l in open(os.path.join(GOLDEN, "window_plan_4471.txt"))
+             if l.strip() and not l.startswith("#")]
+    hdr = dict(zip(lines[0][0::2], map(int, lines[0][1::2])))
+    want = [tuple(map(int, l)) for l in lines[1:]]
+    plan = oracle.window_plan(hdr["n_tokens"], hdr["window"], hdr["stride"])
+    got = [(s, s + n, s, s + k) for s, n, k in plan]
+    assert got == want
+
+
+@pytest.mark.parametrize("n, W, s", [(1, 2000, 1000), (999, 2000, 1000), (2000, 2000, 1000),
+                                     (2001, 2000, 1000), (3000, 2000, 1000), (3001, 2000, 1000),
+                                     (131072, 8192, 4096), (5000, 1000, 300), (777, 100, 100)])
+def test_window_plan_covers_each_token_once_and_stops(n, W, s):
+    plan = oracle.window_plan(n, W, s)
+    cover = np.zeros(n, dtype=np.int64)
+    for start, length, keep in plan:
+        assert 1 <= keep <= length <= W and start + length <= n
+        cover[start:start + keep] += 1
+    assert np.all(cover == 1)
+    # windows at 0, s, 2s, ... up to the first one that reaches the end
+    assert len(plan) == max(0, -(-(n - W) // s)) + 1
+    assert plan[-1][0] + plan[-1][1] == n
+
+
+def test_stitch_averages_overlaps_and_defaults_to_one():
+    plan = [(0, 4, 3), (2, 4, 2)]          # token 2 twice, token 5 never
+    w0, w1 = [1.0, 2.0, 3.0, 9.0], [5.0, 7.0, 9.0, 9.0]
+    got = oracle.stitch(plan, [w0, w1], 6)
+    np.testing.assert_array_equal(got, [1.0, 2.0, 4.0, 7.0, 1.0, 1.0])
+
+
+def test_stitch_of_a_v31_plan_is_a_plain_copy():
+    plan = oracle.window_plan(4471, 2000, 1000)
+    rng = np.random.default_rng(41)
+    ws = [rng.random(n) for _, n, _ in plan]
+    got = oracle.stitch(plan, ws, 4471)
+    for (start, n, keep), w in zip(plan, ws):
+        np.testing.assert_array_equal(got[start:start + keep], w[:keep])
+
+
+def test_legacy_select_keeps_threshold_ties():
+    scores = np.repeat([5.0, 5.0, 5.0, 1.0, 2.0], 32)          # 160 tokens, 5 chunks
+    kept = oracle.select_legacy(scores, 32, 0.2, 4)           # kc = 1, threshold 5
+    np.testing.assert_array_equal(kept, np.r_[0:96, 158, 159])
+
+
+def test_legacy_select_always_tokens_and_min_fill():
+    n = 1170                                                   # eff_min = 117
+    scores = np.zeros(n)
+    scores[320:352] = 1.0                                      # chunk 10 best
+    scores[640:672] = 0.5                                      # chunk 20 second
+    kept = oracle.select_legacy(scores, 32, 0.05, 128)         # nc 37, kc = ceil(1.85) = 2
+    base = set(range(320, 352)) | set(range(640, 672)) | {0, 1, 2, 3, n - 2, n - 1}
+    assert len(base) == 70
+    fill = [t for t in range(n) if t not in base][:117 - 70]  # index order, low chunks first
+    assert list(kept) == sorted(base | set(fill))
+    assert len(kept) == 117
+
+
+def test_legacy_select_keeps_everything_when_short_or_full():
+    # the effective minimum is below n for every n > 4, so only n <= 4 keeps all
+    np.testing.assert_array_equal(oracle.select_legacy(np.arange(4.0), 32, 0.3, 128), np.arange(4))
+    np.testing.assert_array_equal(oracle.select_legacy(np.arange(3.0), 32, 0.3, 128), np.arange(3))
+    # n = 40: the tail chunk (tokens 32-39, the larger mean) plus tokens 0-3
+    np.testing.assert_array_equal(oracle.select_legacy(np.arange(40.0), 32, 0.01, 128),
+                                  np.r_[0:4, 32:40])
+    np.testing.assert_array_equal(oracle.select_legacy(np.arange(500.0), 32, 1.0, 128),
+                                  np.arange(500))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_legacy_select_matches_rank_formulation(seed):
+    """Independent route: a chunk is in iff fewer than kc chunk means are
+    strictly larger (same as reaching the kc-th largest, ties included)."""
+    rng = np.random.default_rng(50 + seed)
+    n = int(rng.integers(200, 3000))
+    C = int(rng.choice([16, 32, 64]))
+    scores = np.round(rng.random(n) * 4) / 4                   # many ties
+    p = float(rng.choice([0.1, 0.3, 0.5]))
+    kept = set(oracle.select_legacy(scores, C, p, 10 ** 9 if seed % 2 else 4).tolist())
+    nc = -(-n // C)
+    means = np.array([np.float32(scores[c * C:(c + 1) * C].mean()) for c in range(nc)])
+    kc = oracle.legacy_keep_count(nc, p)
+    chunk_in = [(means > means[c]).sum() < kc for c in range(nc)]
+    want = {t for c in range(nc) if chunk_in[c] for t in range(c * C, min(n, (c + 1) * C))}
+    want |= {0, 1, 2, 3, n - 2, n - 1}
+    eff_min = min(10 ** 9 if seed % 2 else 4, max(4, n // 10))
+    rest = [t for t in range(n) if t not in want]
+    want |= set(rest[:max(0, eff_min - len(want))])
+    assert kept == want
+
+
+def test_legacy_keep_count_is_single_precision():
+    assert oracle.legacy_keep_count(37, 0.3) == 12
+    assert oracle.legacy_keep_count(1, 0.01) == 1
+    # float32(0.7) * 10 rounds to 7.0000000 in single precision: no ceil to 8
+    assert oracle.legacy_keep_count(10, 0.7) == 7
+
+
+def test_thin_hand_values():
+    np.testing.assert_array_equal(oracle.thin(np.arange(10), 3), [0, 3, 9])
+    np.testing.assert_array_equal(oracle.thin(np.arange(7), 3), [0, 2, 6])
+    np.testing.assert_array_equal(oracle.thin(np.arange(5), 5), np.arange(5))
+    k = np.arange(0, 20000, 3)
+    out = oracle.thin(k, 2000)                                 # step 3
+    assert out.size == 2000 and out[-1] == k[-1] and np.all(out[:-1] == k[:3 * 1999:3])
