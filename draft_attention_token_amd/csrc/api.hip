@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "sp_internal.h"
 
 #include <atomic>
@@ -334,6 +336,118 @@ sp_status sp_gather_kept(const sp_batch *batch, int32_t chunk_size, const uint8_
   return launched(launch_gather(chunks, blocks, blocks.unit_off[blocks.B], chunk_size, keep,
                                 token_ids, kept_ids, kept_pos, kept_offsets, ws,
                                 reinterpret_cast<hipStream_t>(stream)));
+}
+
+sp_status sp_window_plan(int64_t n_tokens, int32_t window, int32_t stride, int32_t capacity,
+                         int64_t *starts, int32_t *lengths, int32_t *keep_lengths,
+                         int32_t *n_windows) {
+  if (!n_windows) return SP_ERR_INVALID_ARGUMENT;
+  *n_windows = 0;
+  if (n_tokens < 1 || n_tokens >= kMaxTotalTokens || window < 1 || stride < 1 || stride > window)
+    return SP_ERR_INVALID_ARGUMENT;
+  // Windows start at 0, stride, 2 stride, ...; the first one that reaches the
+  // end of the prompt, or whose successor would start at or past it, is the
+  // last, and it keeps all of its tokens (the others keep their first stride).
+  int64_t count = 0;
+  for (int64_t pos = 0;; pos += stride) {
+    const int64_t end = pos + window < n_tokens ? pos + window : n_tokens;
+    const bool last = end >= n_tokens || pos + stride >= n_tokens;
+    if (count < capacity && starts && lengths && keep_lengths) {
+      starts[count] = pos;
+      lengths[count] = (int32_t)(end - pos);
+      keep_lengths[count] = (int32_t)(last ? end - pos : stride);
+    }
+    ++count;
+    if (last) break;
+  }
+  *n_windows = (int32_t)count;
+  if (count > capacity || !starts || !lengths || !keep_lengths) return SP_ERR_INVALID_ARGUMENT;
+  return SP_OK;
+}
+
+sp_status sp_stitch_windows(const sp_batch *windows, const int64_t *starts,
+                            const int32_t *keep_lengths, int64_t n_tokens,
+                            const float *window_importance, float *scores, void *stream) {
+  int64_t total;
+  sp_status st = check_batch(windows, &total);
+  if (st != SP_OK) return st;
+  if (!starts || !keep_lengths || !window_importance || !scores) return SP_ERR_INVALID_ARGUMENT;
+  if (n_tokens < 1 || n_tokens >= kMaxTotalTokens) return SP_ERR_INVALID_ARGUMENT;
+  StitchTable t;
+  memset(&t, 0, sizeof(t));
+  t.n_windows = windows->n_prompts;
+  for (int w = 0; w < t.n_windows; ++w) {
+    const int64_t len = windows->token_offsets[w + 1] - windows->token_offsets[w];
+    if (starts[w] < 0 || keep_lengths[w] < 0 || keep_lengths[w] > len ||
+        starts[w] + keep_lengths[w] > n_tokens)
+      return SP_ERR_INVALID_ARGUMENT;
+    t.start[w] = (int32_t)starts[w];
+    t.keep[w] = keep_lengths[w];
+    t.win_off[w] = (int32_t)windows->token_offsets[w];
+  }
+  return launched(launch_stitch(t, (int32_t)n_tokens, window_importance, scores,
+                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+sp_status sp_select_legacy_workspace_bytes(const sp_batch *batch, int32_t chunk_size,
+                                           size_t *bytes) {
+  if (!bytes) return SP_ERR_INVALID_ARGUMENT;
+  int64_t total;
+  int max_nc;
+  sp_status st = check_batch(batch, &total);
+  if (st != SP_OK) return st;
+  if ((st = check_chunks(batch, chunk_size, &max_nc)) != SP_OK) return st;
+  const SegTable chunks = make_table(batch, 0, chunk_size, 0);
+  *bytes = align_up((size_t)chunks.unit_off[chunks.B]) + align_up(sizeof(int32_t) * chunks.B);
+  return SP_OK;
+}
+
+sp_status sp_select_legacy(const sp_batch *batch, int32_t chunk_size, float keep_pct,
+                           int32_t min_tokens, int32_t max_keep, const float *chunk_scores,
+                           const int32_t *token_ids, int32_t *kept_ids, int32_t *kept_pos,
+                           int64_t *kept_offsets, void *ws, size_t ws_bytes, void *stream) {
+  int64_t total;
+  int max_nc;
+  sp_status st = check_batch(batch, &total);
+  if (st != SP_OK) return st;
+  if ((st = check_chunks(batch, chunk_size, &max_nc)) != SP_OK) return st;
+  if (!(keep_pct > 0.f) || !isfinite(keep_pct) || min_tokens < 0 || max_keep < 1)
+    return SP_ERR_INVALID_ARGUMENT;
+  if (!chunk_scores || !token_ids || !kept_ids || !kept_pos || !kept_offsets)
+    return SP_ERR_INVALID_ARGUMENT;
+  const SegTable chunks = make_table(batch, 0, chunk_size, 0);
+  const size_t flags_bytes = align_up((size_t)chunks.unit_off[chunks.B]);
+  if (!ws || ws_bytes < flags_bytes + align_up(sizeof(int32_t) * chunks.B))
+    return SP_ERR_WORKSPACE_TOO_SMALL;
+  LegacyTable t;
+  memset(&t, 0, sizeof(t));
+  t.B = chunks.B;
+  t.C = chunk_size;
+  t.max_keep = max_keep;
+  for (int b = 0; b < t.B; ++b) {
+    const int32_t n = chunks.tok_off[b + 1] - chunks.tok_off[b];
+    const int32_t nc = chunks.unit_off[b + 1] - chunks.unit_off[b];
+    t.tok_off[b] = chunks.tok_off[b];
+    t.chunk_off[b] = chunks.unit_off[b];
+    t.blk_off[b + 1] = t.blk_off[b] + legacy_rank_blocks(nc);
+    // Effective minimum min(min_tokens, max(4, n / 10)); a prompt no longer
+    // than it, or keep_pct >= 1, keeps every chunk and needs no fill.
+    const int32_t eff = std::min(min_tokens, std::max(4, n / 10));
+    if (keep_pct >= 1.f || n <= eff) {
+      t.kc[b] = nc;
+      t.eff_min[b] = 0;
+    } else {
+      const float prod = (float)nc * keep_pct;   // single precision, as the tool reads it
+      t.kc[b] = std::min(nc, std::max(1, (int32_t)ceilf(prod)));
+      t.eff_min[b] = eff;
+    }
+  }
+  t.tok_off[t.B] = chunks.tok_off[t.B];
+  t.chunk_off[t.B] = chunks.unit_off[t.B];
+  uint8_t *in = reinterpret_cast<uint8_t *>(ws);
+  int32_t *counts = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(ws) + flags_bytes);
+  return launched(launch_legacy(t, chunk_scores, token_ids, in, counts, kept_ids, kept_pos,
+                                kept_offsets, reinterpret_cast<hipStream_t>(stream)));
 }
 
 sp_status sp_break_even(int64_t n_tokens, int64_t n_kept, double spec_tps, double target_tps,

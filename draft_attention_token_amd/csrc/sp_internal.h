@@ -117,4 +117,27 @@ hipError_t launch_gather(const SegTable &chunks, const SegTable &blocks, int tot
 constexpr int kGatherBlockTokens = 1024;
 size_t gather_ws(int B, int total_chunks);
 
+// Standalone-tool semantics (tool.hip).
+struct StitchTable {
+  int32_t n_windows;
+  int32_t start[SP_MAX_PROMPTS];     // window's first token in the prompt
+  int32_t keep[SP_MAX_PROMPTS];      // tokens of the window whose scores count
+  int32_t win_off[SP_MAX_PROMPTS];   // window's offset in the window batch
+};
+hipError_t launch_stitch(const StitchTable &t, int32_t n, const float *win_imp, float *out,
+                         hipStream_t st);
+
+struct LegacyTable {
+  int32_t B, C, max_keep;
+  int32_t tok_off[SP_MAX_PROMPTS + 1];
+  int32_t chunk_off[SP_MAX_PROMPTS + 1];
+  int32_t blk_off[SP_MAX_PROMPTS + 1];     // rank-kernel block prefix per prompt
+  int32_t kc[SP_MAX_PROMPTS];              // chunks ranked in (all of them: keep everything)
+  int32_t eff_min[SP_MAX_PROMPTS];         // kept-token floor (0: none)
+};
+int legacy_rank_blocks(int nc);
+hipError_t launch_legacy(const LegacyTable &t, const float *chunk_scores, const int32_t *ids,
+                         uint8_t *in, int32_t *counts, int32_t *kept_ids, int32_t *kept_pos,
+                         int64_t *kept_offsets, hipStream_t st);
+
 }  // namespace sp

@@ -37,6 +37,7 @@ EXPORTED = [
     "sp_abi_version", "sp_status_string", "sp_score_workspace_bytes", "sp_pool_workspace_bytes",
     "sp_select_workspace_bytes", "sp_gather_workspace_bytes", "sp_score_attention",
     "sp_pool_chunk", "sp_select_chunks", "sp_gather_kept", "sp_score_status", "sp_break_even",
+    "sp_window_plan", "sp_stitch_windows", "sp_select_legacy_workspace_bytes", "sp_select_legacy",
 ]
 
 _ALGOS = {"auto": SP_SCORE_AUTO, "two_pass": SP_SCORE_TWO_PASS, "stream": SP_SCORE_STREAM}
@@ -97,6 +98,13 @@ def lib():
         L.sp_score_status.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
         L.sp_break_even.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
                                     ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_int32)]
+        i32p, i64p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+        L.sp_window_plan.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     i64p, i32p, i32p, i32p]
+        L.sp_stitch_windows.argtypes = [bp, i64p, i32p, ctypes.c_int64, vp, vp, vp]
+        L.sp_select_legacy_workspace_bytes.argtypes = [bp, ctypes.c_int32, szp]
+        L.sp_select_legacy.argtypes = [bp, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                                       ctypes.c_int32, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in EXPORTED[2:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -255,6 +263,56 @@ def break_even(n_tokens: int, n_kept: int, spec_tps: float = 0.0, target_tps: fl
     return bool(run.value)
 
 
+def window_plan(n_tokens: int, window: int, stride: int):
+    """(starts, lengths, keep_lengths) of the tool's sliding windows
+    (sp_window_plan), as lists."""
+    n = ctypes.c_int32()
+    lib().sp_window_plan(int(n_tokens), int(window), int(stride), 0, None, None, None,
+                         ctypes.byref(n))
+    cap = n.value
+    starts = (ctypes.c_int64 * cap)()
+    lengths, keeps = (ctypes.c_int32 * cap)(), (ctypes.c_int32 * cap)()
+    _check(lib().sp_window_plan(int(n_tokens), int(window), int(stride), cap, starts, lengths,
+                                keeps, ctypes.byref(n)), "sp_window_plan")
+    return list(starts), list(lengths), list(keeps)
+
+
+def stitch_windows(windows: Batch, starts, keep_lengths, n_tokens: int,
+                   window_importance: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """Prompt scores [n_tokens] fp32 from the window batch's importance."""
+    if out is None:
+        out = torch.empty(n_tokens, dtype=torch.float32, device=window_importance.device)
+    st = (ctypes.c_int64 * len(starts))(*starts)
+    kl = (ctypes.c_int32 * len(keep_lengths))(*keep_lengths)
+    _check(lib().sp_stitch_windows(windows.ref(), st, kl, int(n_tokens), _ptr(window_importance),
+                                   _ptr(out), _stream(window_importance.device)),
+           "sp_stitch_windows")
+    return out
+
+
+def select_legacy_workspace_bytes(batch: Batch, C: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().sp_select_legacy_workspace_bytes(batch.ref(), C, ctypes.byref(n)),
+           "sp_select_legacy_workspace_bytes")
+    return n.value
+
+
+def select_legacy(batch: Batch, C: int, keep_pct: float, min_tokens: int, max_keep: int,
+                  chunk_scores: torch.Tensor, token_ids: torch.Tensor):
+    """(kept_ids, kept_pos, kept_offsets) by the tool's legacy rule and cap."""
+    dev = chunk_scores.device
+    T = batch.total
+    kept_ids = torch.empty(T, dtype=torch.int32, device=dev)
+    kept_pos = torch.empty(T, dtype=torch.int32, device=dev)
+    kept_off = torch.empty(batch.B + 1, dtype=torch.int64, device=dev)
+    ws = _ws(select_legacy_workspace_bytes(batch, C), dev)
+    _check(lib().sp_select_legacy(batch.ref(), C, float(keep_pct), int(min_tokens), int(max_keep),
+                                  _ptr(chunk_scores), _ptr(token_ids), _ptr(kept_ids),
+                                  _ptr(kept_pos), _ptr(kept_off), _ptr(ws), ws.numel(),
+                                  _stream(dev)), "sp_select_legacy")
+    return kept_ids, kept_pos, kept_off
+
+
 def score_status(ws: torch.Tensor) -> int:
     """Status word of the last finished sp_score_attention on this workspace
     (0 = ok; 1 = a cross-block wait timed out and the importance is invalid)."""
@@ -387,3 +445,58 @@ class Pipeline:
                                 _ptr(self.kept_pos), _ptr(self.kept_offsets),
                                 _ptr(self.ws_gather), self.ws_gather.numel(), st),
                "sp_gather_kept")
+
+
+class ToolPipeline:
+    """The standalone tool's path for one prompt: the windows of
+    sp_window_plan scored as one batch, stitched, pooled/normalised/boosted,
+    then the legacy chunk rule with its cap. Buffers are preallocated."""
+
+    def __init__(self, n_tokens, window, stride, n_layers, n_q_heads, n_kv_heads, head_dim,
+                 n_lookahead, dtype, device, C=32, W=1, normalize=True, boost=True,
+                 keep_pct=0.3, min_tokens=128, max_keep=2000, prefill_row=True, algo="auto"):
+        self.n = int(n_tokens)
+        self.starts, self.lengths, self.keeps = window_plan(n_tokens, window, stride)
+        self.windows = Batch(np.concatenate([[0], np.cumsum(self.lengths)]))
+        self.prompt = Batch([0, self.n])
+        fm, lm = (1.5, 1.3) if boost else (1.0, 1.0)
+        self.adesc = attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype,
+                               None, algo, prefill_row=prefill_row)
+        self.pdesc = pool_desc(W, C, normalize, 64, fm, 128, lm)
+        self.C, self.keep_pct, self.min_tokens, self.max_keep = C, keep_pct, min_tokens, max_keep
+        f32 = dict(dtype=torch.float32, device=device)
+        self.importance = torch.empty(self.windows.total, **f32)
+        self.scores = torch.empty(self.n, **f32)
+        self.token_scores = torch.empty(self.n, **f32)
+        self.chunk_scores = torch.empty(self.prompt.n_chunks(C), **f32)
+        self.kept_ids = torch.empty(self.n, dtype=torch.int32, device=device)
+        self.kept_pos = torch.empty(self.n, dtype=torch.int32, device=device)
+        self.kept_offsets = torch.empty(2, dtype=torch.int64, device=device)
+        self.ws_score = _ws(score_workspace_bytes(self.adesc, self.windows), device)
+        self.ws_pool = _ws(pool_workspace_bytes(self.pdesc, self.prompt), device)
+        self.ws_legacy = _ws(select_legacy_workspace_bytes(self.prompt, C), device)
+        self._starts = (ctypes.c_int64 * len(self.starts))(*self.starts)
+        self._keeps = (ctypes.c_int32 * len(self.keeps))(*self.keeps)
+        self.device = device
+
+    def score_status(self) -> int:
+        return score_status(self.ws_score)
+
+    def run(self, q: torch.Tensor, k: torch.Tensor, token_ids: torch.Tensor):
+        """q, k: the window batch's Q and K; token_ids: [n_tokens] of the prompt."""
+        L = lib()
+        st = _stream(self.device)
+        _check(L.sp_score_attention(ctypes.byref(self.adesc), self.windows.ref(), _ptr(q), _ptr(k),
+                                    _ptr(self.importance), _ptr(self.ws_score),
+                                    self.ws_score.numel(), st), "sp_score_attention")
+        _check(L.sp_stitch_windows(self.windows.ref(), self._starts, self._keeps, self.n,
+                                   _ptr(self.importance), _ptr(self.scores), st),
+               "sp_stitch_windows")
+        _check(L.sp_pool_chunk(ctypes.byref(self.pdesc), self.prompt.ref(), _ptr(self.scores),
+                               _ptr(self.token_scores), _ptr(self.chunk_scores),
+                               _ptr(self.ws_pool), self.ws_pool.numel(), st), "sp_pool_chunk")
+        _check(L.sp_select_legacy(self.prompt.ref(), self.C, float(self.keep_pct),
+                                  int(self.min_tokens), int(self.max_keep), _ptr(self.chunk_scores),
+                                  _ptr(token_ids), _ptr(self.kept_ids), _ptr(self.kept_pos),
+                                  _ptr(self.kept_offsets), _ptr(self.ws_legacy),
+                                  self.ws_legacy.numel(), st), "sp_select_legacy")

@@ -12,6 +12,8 @@
  *   sp_select_chunks    chunk_scores    -> keep[chunk], n_kept_chunks[prompt]
  *   sp_gather_kept      keep, token ids -> kept ids + original positions
  *   sp_break_even       host-side estimate: is sparse prefill worth running?
+ * and the standalone tool's window and legacy-selection steps:
+ *   sp_window_plan, sp_stitch_windows, sp_select_legacy
  *
  * Sources (web pages on SpecPrefill):
  *   [G]  "SpecPrefill — Implementation Guide": How It Works (Core Algorithm,
@@ -241,6 +243,65 @@ sp_status sp_select_chunks(int32_t mode, double param, const sp_batch *batch, in
 sp_status sp_gather_kept(const sp_batch *batch, int32_t chunk_size, const uint8_t *keep,
                          const int32_t *token_ids, int32_t *kept_ids, int32_t *kept_pos,
                          int64_t *kept_offsets, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Standalone-tool semantics ([G] Sliding Window and its worked example,
+ * v3.1 Optimizations & Bug Fixes items 6-7, Sliding Window Loop (v3.1 —
+ * fixed), Configuration Reference: SP_CHUNK, SP_KEEP_PCT, SP_MAX_KEEP; the
+ * chunk-selection and main-loop parts of [G] Full Source Code). The tool
+ * scores a long prompt window by window, each window a prompt of its own for
+ * the draft model; the windows go to sp_score_attention as one batch.
+ */
+
+/* Window plan (host arithmetic, no device work): windows start at 0, stride,
+ * 2 stride, ... and span min(window, n_tokens - start) tokens. A window is the
+ * last one when it reaches the end of the prompt or when the next start would
+ * (start + stride >= n_tokens); it keeps all of its tokens' scores, every
+ * other window the first `stride` ones. Writes up to `capacity` entries of
+ * starts, lengths and keep_lengths (host arrays) and the number of windows to
+ * *n_windows; returns SP_ERR_INVALID_ARGUMENT if that exceeds capacity
+ * (*n_windows then tells the size needed) or for n_tokens < 1, window < 1,
+ * stride outside 1..window. */
+sp_status sp_window_plan(int64_t n_tokens, int32_t window, int32_t stride, int32_t capacity,
+                         int64_t *starts, int32_t *lengths, int32_t *keep_lengths,
+                         int32_t *n_windows);
+
+/* Prompt scores from window scores: token t gets the mean of the scores that
+ * the windows holding t in their kept range give it (window w's token
+ * t - starts[w]), and 1.0 if no window does.
+ *   windows: the window batch (window w = prompt w, host offsets).
+ *   starts, keep_lengths: host, [n_windows]; keep_lengths[w] <= window
+ *     length, starts[w] + keep_lengths[w] <= n_tokens.
+ *   window_importance: [sum of window lengths] fp32 in (sp_score_attention
+ *     on the window batch).
+ *   scores: [n_tokens] fp32 out. */
+sp_status sp_stitch_windows(const sp_batch *windows, const int64_t *starts,
+                            const int32_t *keep_lengths, int64_t n_tokens,
+                            const float *window_importance, float *scores, void *stream);
+
+/* Legacy chunk rule of the tool, per prompt, plus its cap on tokens sent to
+ * the target. With eff_min = min(min_tokens, max(4, N / 10)): if
+ * keep_pct >= 1 or N <= eff_min every token is kept. Otherwise, with
+ * kc = max(1, ceil(nc * keep_pct)) computed in single precision, a chunk is
+ * kept when fewer than kc chunk scores of the prompt are strictly larger
+ * (its score reaches the kc-th largest: ties are all kept); tokens 0-3 and,
+ * for N > 4, the last two are kept too; while fewer than eff_min tokens are
+ * kept, the remaining tokens are added in index order. The kept tokens, in
+ * ascending order, are then capped: above max_keep of them, every step-th
+ * one is kept (step = count / max_keep, integer division) up to max_keep,
+ * the last slot taking the final kept token.
+ *   chunk_scores: [sum nc_b] fp32 in (e.g. sp_pool_chunk with pool_window 1).
+ *   token_ids: [sum N_b] int32 in.
+ *   kept_ids, kept_pos: [sum N_b] int32 out (capacity), prompt b's at
+ *     kept_offsets[b] .. kept_offsets[b + 1].
+ *   kept_offsets: [B + 1] int64 out.
+ *   ws: device workspace of sp_select_legacy_workspace_bytes() bytes. */
+sp_status sp_select_legacy_workspace_bytes(const sp_batch *batch, int32_t chunk_size,
+                                           size_t *bytes);
+sp_status sp_select_legacy(const sp_batch *batch, int32_t chunk_size, float keep_pct,
+                           int32_t min_tokens, int32_t max_keep, const float *chunk_scores,
+                           const int32_t *token_ids, int32_t *kept_ids, int32_t *kept_pos,
+                           int64_t *kept_offsets, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Break-even gate ([G] v3 Improvements item 4 and Configuration Reference:

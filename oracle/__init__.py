@@ -298,12 +298,25 @@ def legacy_keep_count(n_chunks: int, keep_pct: float) -> int:
 
 def select_legacy(scores, chunk_size: int = 32, keep_pct: float = 0.3,
                   min_tokens: int = 128) -> np.ndarray:
-    """Kept token indices, ascending, by the standalone tool's chunk rule.
+    """Kept token indices, ascending, by the standalone tool's chunk rule:
+    chunk means over the tokens each chunk holds (sums in double, the mean
+    rounded to single precision), then select_legacy_from_means."""
+    x = np.asarray(scores, dtype=np.float64)
+    n = x.size
+    nc = (n + chunk_size - 1) // chunk_size
+    means = np.array([np.float32(x[c * chunk_size:min(n, (c + 1) * chunk_size)].sum()
+                                 / (min(n, (c + 1) * chunk_size) - c * chunk_size))
+                      for c in range(nc)], dtype=np.float32)
+    return select_legacy_from_means(means, n, chunk_size, keep_pct, min_tokens)
+
+
+def select_legacy_from_means(means, n: int, chunk_size: int = 32, keep_pct: float = 0.3,
+                             min_tokens: int = 128) -> np.ndarray:
+    """The legacy rule on given chunk means (single precision) of an n-token
+    prompt.
 
     - effective minimum: min(min_tokens, max(4, n // 10)); if keep_pct >= 1
       or the prompt is no longer than it, every token is kept;
-    - chunk means over the tokens each chunk holds (sums in double, the mean
-      rounded to single precision);
     - threshold: the kc-th largest chunk mean (kc from legacy_keep_count);
       every chunk whose mean reaches it is kept, ties included;
     - tokens 0-3 and, when there are more than 4 tokens, the last two are
@@ -311,15 +324,12 @@ def select_legacy(scores, chunk_size: int = 32, keep_pct: float = 0.3,
     - while fewer than the effective minimum are kept, tokens of the chunks
       below the threshold are added in index order.
     """
-    x = np.asarray(scores, dtype=np.float64)
-    n = x.size
+    means = np.asarray(means, dtype=np.float32)
+    nc = means.size
+    assert nc == (n + chunk_size - 1) // chunk_size
     eff_min = min(min_tokens, max(4, n // 10))
     if keep_pct >= 1.0 or n <= eff_min:
         return np.arange(n, dtype=np.int64)
-    nc = (n + chunk_size - 1) // chunk_size
-    means = np.array([np.float32(x[c * chunk_size:min(n, (c + 1) * chunk_size)].sum()
-                                 / (min(n, (c + 1) * chunk_size) - c * chunk_size))
-                      for c in range(nc)], dtype=np.float32)
     kc = legacy_keep_count(nc, keep_pct)
     th = np.sort(means)[::-1][kc - 1]
     kept = set()
@@ -351,3 +361,23 @@ def thin(kept, max_keep: int) -> np.ndarray:
     out = kept[::step][:max_keep].copy()
     out[-1] = kept[-1]
     return out
+
+
+def tool_pipeline(win_inputs, plan, nthreads: int = 0):
+    """The standalone tool on a ``workloads.WindowInputs``: window importance,
+    stitched prompt scores, token scores (normalised and boosted, no pooling
+    unless the workload asks), the legacy kept tokens and the capped list."""
+    w = win_inputs.workload
+    bi = win_inputs.batch
+    imp = importance(bi.offsets.numpy(), bi.q, bi.k, w.n_layers, w.n_q_heads, w.n_kv_heads,
+                     w.head_dim, w.n_lookahead, bi.scale, nthreads, prefill_row=w.prefill_row)
+    off = bi.offsets.numpy()
+    per_window = [imp[off[i]:off[i + 1]] for i in range(len(plan))]
+    scores = stitch(plan, per_window, win_inputs.n_tokens)
+    fm, lm = (1.5, 1.3) if w.boost else (1.0, 1.0)
+    ts, cs = pool_chunk(scores, w.pool_window, w.chunk_size, w.normalize, 64, fm, 128, lm)
+    kept = select_legacy(ts, w.chunk_size, w.keep_pct, w.min_tokens)
+    final = thin(kept, w.max_keep)
+    ids = win_inputs.token_ids.numpy()
+    return {"imp": imp, "scores": scores, "token_scores": ts, "chunk_scores": cs, "kept": kept,
+            "final": final, "final_ids": ids[final]}

@@ -233,3 +233,53 @@ def test_break_even_matches_oracle_and_defaults():
 def test_break_even_rejects_bad_arguments(args):
     run = ctypes.c_int32()
     assert sp.lib().sp_break_even(*args, ctypes.byref(run)) == sp.SP_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("n, W, s", [(4471, 2000, 1000), (1, 2000, 1000), (2000, 2000, 1000),
+                                     (2001, 2000, 1000), (131072, 8192, 4096), (5000, 1000, 300),
+                                     (777, 100, 100)])
+def test_window_plan_matches_oracle(n, W, s):
+    import oracle
+    starts, lengths, keeps = sp.window_plan(n, W, s)
+    assert list(zip(starts, lengths, keeps)) == oracle.window_plan(n, W, s)
+
+
+def test_window_plan_rejects_bad_arguments_and_reports_size():
+    L = sp.lib()
+    n = ctypes.c_int32()
+    for args in [(0, 10, 5), (10, 0, 1), (10, 5, 6), (10, 5, 0)]:
+        assert L.sp_window_plan(*args, 0, None, None, None, ctypes.byref(n)) == \
+            sp.SP_ERR_INVALID_ARGUMENT
+    st, ln, kp = (ctypes.c_int64 * 2)(), (ctypes.c_int32 * 2)(), (ctypes.c_int32 * 2)()
+    assert L.sp_window_plan(4471, 2000, 1000, 2, st, ln, kp, ctypes.byref(n)) == \
+        sp.SP_ERR_INVALID_ARGUMENT
+    assert n.value == 4                                   # the capacity it needs
+    assert L.sp_window_plan(4471, 2000, 1000, 4, None, None, None, ctypes.byref(n)) == \
+        sp.SP_ERR_INVALID_ARGUMENT
+
+
+def test_stitch_and_legacy_reject_bad_arguments():
+    L = sp.lib()
+    vp = lambda v: ctypes.c_void_p(v)
+    win = sp.Batch([0, 2000, 4000])
+    st = (ctypes.c_int64 * 2)(0, 1000)
+    kp = (ctypes.c_int32 * 2)(1000, 2000)
+    assert L.sp_stitch_windows(win.ref(), st, kp, 3000, vp(4096), vp(0), None) == \
+        sp.SP_ERR_INVALID_ARGUMENT                        # null output
+    assert L.sp_stitch_windows(win.ref(), st, kp, 2999, vp(4096), vp(4096), None) == \
+        sp.SP_ERR_INVALID_ARGUMENT                        # keep range past the prompt
+    kp2 = (ctypes.c_int32 * 2)(1000, 2001)
+    assert L.sp_stitch_windows(win.ref(), st, kp2, 4000, vp(4096), vp(4096), None) == \
+        sp.SP_ERR_INVALID_ARGUMENT                        # keeps more than the window holds
+    b = sp.Batch([0, 500])
+    args = [vp(4096)] * 5
+    ok = dict(C=32, keep=0.3, mn=128, mx=2000)
+    def call(C=32, keep=0.3, mn=128, mx=2000, ws_bytes=1 << 20):
+        return L.sp_select_legacy(b.ref(), C, keep, mn, mx, *args, vp(4096), ws_bytes, None)
+    assert call(keep=0.0) == sp.SP_ERR_INVALID_ARGUMENT
+    assert call(keep=float("nan")) == sp.SP_ERR_INVALID_ARGUMENT
+    assert call(mn=-1) == sp.SP_ERR_INVALID_ARGUMENT
+    assert call(mx=0) == sp.SP_ERR_INVALID_ARGUMENT
+    assert call(C=0) == sp.SP_ERR_INVALID_ARGUMENT
+    assert call(ws_bytes=4) == sp.SP_ERR_WORKSPACE_TOO_SMALL
+    assert sp.select_legacy_workspace_bytes(b, 32) >= 16 + 4

@@ -349,3 +349,69 @@ def test_ragged_batch_sampled_prompts():
             want_ids, want_pos = oracle.gather(gp[b]["keep"], ids, w.chunk_size)
             assert np.array_equal(gp[b]["kept_ids"], want_ids)
             assert np.array_equal(gp[b]["kept_pos"], want_pos)
+
+
+# ----------------------------------------------------------------------------
+# Standalone-tool semantics: windows, stitching, legacy rule, cap
+# ----------------------------------------------------------------------------
+
+TOOL_CASES = [
+    # (name, base, overrides)
+    ("tool4471", "tool4471_bf16", dict()),
+    ("tool_fill_and_cap", "tool4471_bf16", dict(lengths=(900,), window=256, stride=128,
+                                                keep_pct=0.02, max_keep=70)),
+    ("tool_ragged_windows", "tool4471_bf16", dict(lengths=(1337,), window=300, stride=100,
+                                                  keep_pct=0.25, chunk_size=16)),
+    ("tool_one_window_no_norm", "tool4471_bf16", dict(lengths=(777,), window=2000, stride=1000,
+                                                      normalize=False, boost=False, n_lookahead=4)),
+    ("tool_128k", "tool128k_bf16", dict()),
+]
+
+
+@pytest.mark.parametrize("name, base, kw", TOOL_CASES, ids=[c[0] for c in TOOL_CASES])
+def test_tool_windows_legacy_selection(name, base, kw):
+    w = workloads.small_workload(base, **kw)
+    n = w.lengths[0]
+    starts, lengths, keeps = sp.window_plan(n, w.window, w.stride)
+    plan = oracle.window_plan(n, w.window, w.stride)
+    assert list(zip(starts, lengths, keeps)) == plan
+    wi = workloads.make_window_inputs(w, starts, lengths)
+    print(f"[gpu] {name}: n={n} windows={len(plan)} keep={w.keep_pct} cap={w.max_keep}", flush=True)
+    pipe = sp.ToolPipeline(n, w.window, w.stride, w.n_layers, w.n_q_heads, w.n_kv_heads,
+                           w.head_dim, w.n_lookahead, w.dtype, DEV, C=w.chunk_size,
+                           W=w.pool_window, normalize=w.normalize, boost=w.boost,
+                           keep_pct=w.keep_pct, min_tokens=w.min_tokens, max_keep=w.max_keep,
+                           prefill_row=w.prefill_row)
+    ids = wi.token_ids.to(DEV)
+    pipe.run(wi.batch.q.to(DEV), wi.batch.k.to(DEV), ids)
+    torch.cuda.synchronize()
+    assert pipe.score_status() == 0
+    ora = oracle.tool_pipeline(wi, plan)
+    assert_scores_close(pipe.importance.cpu().numpy(), ora["imp"], "window importance")
+    assert_scores_close(pipe.scores.cpu().numpy(), ora["scores"], "stitched scores")
+    assert_scores_close(pipe.token_scores.cpu().numpy(), ora["token_scores"], "token scores")
+    cs = pipe.chunk_scores.cpu().numpy()
+    assert_scores_close(cs, ora["chunk_scores"], "chunk scores")
+    off = pipe.kept_offsets.cpu().numpy()
+    got_pos = pipe.kept_pos.cpu().numpy()[off[0]:off[1]]
+    got_ids = pipe.kept_ids.cpu().numpy()[off[0]:off[1]]
+    # The rule and the cap, exactly, on the GPU's own chunk scores.
+    own = oracle.thin(oracle.select_legacy_from_means(cs, n, w.chunk_size, w.keep_pct,
+                                                      w.min_tokens), w.max_keep)
+    np.testing.assert_array_equal(got_pos, own)
+    np.testing.assert_array_equal(got_ids, wi.token_ids.numpy()[own])
+    # Against the oracle's own scores: identical unless a chunk mean sits
+    # within 1e-5 of the oracle's threshold.
+    means = np.float32(ora["chunk_scores"])
+    nc = means.size
+    kc = oracle.legacy_keep_count(nc, w.keep_pct)
+    th = np.sort(means)[::-1][kc - 1]
+    near = np.abs(means.astype(np.float64) - th) <= 1e-5
+    if near.sum() <= 1:                                   # only the threshold chunk itself
+        np.testing.assert_array_equal(got_pos, ora["final"])
+        np.testing.assert_array_equal(got_ids, ora["final_ids"])
+    else:
+        print(f"[gpu] {name}: {int(near.sum()) - 1} chunk(s) excused near the threshold", flush=True)
+    if ora["kept"].size <= w.max_keep and w.keep_pct >= 0.25:
+        for c in wi.spans:                                # planted spans survive an uncapped rule
+            assert np.isin(np.arange(32 * c, 32 * c + 32), got_pos).all(), c

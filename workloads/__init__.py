@@ -67,6 +67,11 @@ class Workload:
     k_fp8: bool = False               # K as fp8 e4m3 codes + per-(layer, KV head) scales
     prefill_row: bool = False         # one more query step: the prompt's last row
     pool_before_max: bool = False     # pool each probability row before the head/layer max
+    window: int = 0                   # >0: the standalone tool's sliding windows of this size
+    stride: int = 0                   # their stride
+    keep_pct: float = 0.3             # legacy chunk rule: fraction of chunks
+    min_tokens: int = 128             # legacy chunk rule: kept-token floor
+    max_keep: int = 2000              # cap on tokens sent to the target
 
     @property
     def group(self) -> int:
@@ -124,6 +129,16 @@ WORKLOADS = {
     "n128k_poolmax_bf16": Workload("n128k_poolmax_bf16", (131072,), 6, 16, 4, 128, 8,
                                    torch.bfloat16, 1004, 64, None,
                                    also_select=(("top_p", 0.15),), pool_before_max=True),
+    # The standalone tool: sliding windows (each a separate draft pass with the
+    # prefill's last row as a step and 2 lookahead steps), scores stitched,
+    # normalised and boosted, then the legacy chunk rule and the 2000-token cap.
+    # 4471 tokens in windows of 2000 at stride 1000: the guide's worked example.
+    "tool4471_bf16": Workload("tool4471_bf16", (4471,), 6, 16, 4, 128, 2, torch.bfloat16,
+                              1601, 5, 2.0, pool_window=1, select=("legacy", 0.3),
+                              prefill_row=True, window=2000, stride=1000),
+    "tool128k_bf16": Workload("tool128k_bf16", (131072,), 6, 16, 4, 128, 2, torch.bfloat16,
+                              1602, 64, None, pool_window=1, select=("legacy", 0.3),
+                              prefill_row=True, window=8192, stride=4096),
 }
 
 
@@ -238,3 +253,62 @@ def quantize_fp8(k: torch.Tensor):
 def small_workload(base: str, **overrides) -> Workload:
     """A copy of a named workload with some fields replaced (small cases)."""
     return dataclasses.replace(WORKLOADS[base], **overrides)
+
+
+@dataclasses.dataclass
+class WindowInputs:
+    """Inputs of the standalone tool's windows: every window is a prompt of
+    its own for the draft model (fresh context), so each one draws its own Q
+    and K; the planted spans and the token ids belong to the whole prompt."""
+    workload: Workload
+    n_tokens: int
+    starts: List[int]
+    batch: Inputs              # the windows as a batch of prompts
+    token_ids: torch.Tensor    # [n_tokens] int32, the whole prompt's ids
+    spans: List[int]           # planted chunk indices of the whole prompt
+    strengths: List[float]
+
+
+def make_window_inputs(w: Workload, starts: List[int], lengths: List[int]) -> WindowInputs:
+    """Seeded inputs for windows at the given starts and lengths (the caller
+    supplies the window plan). Window i draws Q [layers][S][Hq][d] and K
+    [layers][len_i + L][Hkv][d] from N(0, 1) with seed w.seed + 7919 * (i + 1);
+    a planted span adds s * u to the K rows of its tokens inside the window
+    (u: the unit mean query of the group in that window and layer)."""
+    n = int(w.lengths[0])
+    L, S, Hq, Hkv, d, G = w.n_lookahead, w.steps, w.n_q_heads, w.n_kv_heads, w.head_dim, w.group
+    g = torch.Generator("cpu").manual_seed(w.seed)
+    first, last = 2, (n - 128) // 32 - 1
+    eligible = max(0, last - first + 1)
+    ns = min(w.n_spans if w.n_spans is not None else n // 2048, eligible)
+    perm = torch.randperm(eligible, generator=g)[:ns] if eligible > 0 else torch.empty(0, dtype=torch.long)
+    spans = sorted(int(first + c) for c in perm)
+    if w.span_strength is None:
+        strengths = (0.5 + 2.5 * torch.rand(ns, generator=g, dtype=torch.float64)).tolist()
+    else:
+        strengths = [float(w.span_strength)] * ns
+    ids = torch.randint(0, VOCAB, (n,), generator=g, dtype=torch.int64).to(torch.int32)
+    B = len(starts)
+    offsets = torch.zeros(B + 1, dtype=torch.int64)
+    for i, ln in enumerate(lengths):
+        offsets[i + 1] = offsets[i] + ln
+    q = torch.empty(B, w.n_layers, S, Hq, d, dtype=w.dtype)
+    k = torch.empty(w.n_layers, int(offsets[-1]) + B * L, Hkv, d, dtype=w.dtype)
+    for i, (s0, ln) in enumerate(zip(starts, lengths)):
+        gw = torch.Generator("cpu").manual_seed(w.seed + 7919 * (i + 1))
+        kb = int(offsets[i]) + i * L
+        for layer in range(w.n_layers):
+            qq = torch.randn(S, Hq, d, generator=gw, dtype=torch.float32)
+            kk = torch.randn(ln + L, Hkv, d, generator=gw, dtype=torch.float32)
+            for grp in range(Hkv):
+                v = qq[:, grp * G:(grp + 1) * G, :].reshape(-1, d).mean(dim=0)
+                u = v / v.norm()
+                for c, st in zip(spans, strengths):
+                    a, b = max(32 * c, s0), min(32 * c + 32, s0 + ln)
+                    if a < b:
+                        kk[a - s0:b - s0, grp, :] += float(st) * u
+            q[i, layer].copy_(qq.to(q.dtype))
+            k[layer, kb:kb + ln + L].copy_(kk.to(k.dtype))
+    batch = Inputs(w, list(lengths), offsets, q, k, torch.zeros(int(offsets[-1]), dtype=torch.int32),
+                   [[] for _ in range(B)], [[] for _ in range(B)])
+    return WindowInputs(w, n, list(starts), batch, ids, spans, strengths)
