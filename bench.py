@@ -139,6 +139,24 @@ def cpu_baseline(inp, mode, param):
             "seconds": dt, "host_threads": threads}
 
 
+def cpu_baseline_tool(win_inp):
+    """The oracle as it stands on the standalone tool's path (its own window
+    plan), on the host cores, over the whole prompt."""
+    import oracle
+    w = win_inp.workload
+    plan = oracle.window_plan(win_inp.n_tokens, w.window, w.stride)
+    threads = oracle.max_threads()
+    used = min(threads, len(plan) * w.steps)
+    t0 = time.perf_counter()
+    oracle.tool_pipeline(win_inp, plan)
+    dt = time.perf_counter() - t0
+    toks = win_inp.n_tokens
+    return {"value": toks / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"whole workload {w.name}: {toks} tokens in {len(plan)} windows; fp64 C "
+                      f"loops with OpenMP over (window, step) pairs; {dt:.2f} s",
+            "seconds": dt, "host_threads": threads}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,15 +188,33 @@ def main():
     w = workloads.WORKLOADS[args.workload]
     mode, param = (args.mode, args.param) if args.mode else w.select
     log(f"generating {w.name}")
-    inp = workloads.make_inputs(w)
-    q, k, ids = inp.q.to(dev), inp.k.to(dev), inp.token_ids.to(dev)
+    tool = w.window > 0
+    if tool:
+        # The standalone tool: the prompt's windows (planned by the library)
+        # are scored as one batch, then stitched and selected.
+        n_tok = int(w.lengths[0])
+        starts, lengths, _ = sp.window_plan(n_tok, w.window, w.stride)
+        win_inp = workloads.make_window_inputs(w, starts, lengths)
+        inp = win_inp.batch
+        ids = win_inp.token_ids.to(dev)
+        tokens = n_tok
+        pipe = sp.ToolPipeline(n_tok, w.window, w.stride, w.n_layers, w.n_q_heads, w.n_kv_heads,
+                               w.head_dim, w.n_lookahead, w.dtype, dev, C=w.chunk_size,
+                               W=w.pool_window, normalize=w.normalize, boost=w.boost,
+                               keep_pct=w.keep_pct, min_tokens=w.min_tokens,
+                               max_keep=w.max_keep, prefill_row=w.prefill_row, algo=args.algo)
+        mode, param = "legacy", w.keep_pct
+    else:
+        inp = workloads.make_inputs(w)
+        ids = inp.token_ids.to(dev)
+        tokens = int(inp.offsets[-1])
+        pipe = sp.Pipeline(inp.offsets, w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                           w.n_lookahead, w.dtype, dev, W=w.pool_window, C=w.chunk_size,
+                           normalize=w.normalize, boost=w.boost, mode=mode, param=param,
+                           algo=args.algo, k_dtype=inp.k.dtype, k_scales=inp.k_scales,
+                           prefill_row=w.prefill_row, pool_before_max=w.pool_before_max)
+    q, k = inp.q.to(dev), inp.k.to(dev)
     torch.cuda.synchronize()
-    tokens = int(inp.offsets[-1])
-    pipe = sp.Pipeline(inp.offsets, w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim,
-                       w.n_lookahead, w.dtype, dev, W=w.pool_window, C=w.chunk_size,
-                       normalize=w.normalize, boost=w.boost, mode=mode, param=param,
-                       algo=args.algo, k_dtype=inp.k.dtype, k_scales=inp.k_scales,
-                       prefill_row=w.prefill_row, pool_before_max=w.pool_before_max)
     fp8k = inp.k.dtype == torch.float8_e4m3fn
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -227,6 +263,12 @@ def main():
     log(f"plain 1 GiB streaming read: {read_gbs:.0f} GB/s ({read_shape} blocks per CU)")
 
     kept = int(pipe.kept_offsets[-1])
+    if tool:
+        kernel_name = "k_stream (sp_score_attention on the window batch)"
+    elif w.pool_before_max:
+        kernel_name = "k_stats + k_lse + k_score_pooled (sp_score_attention)"
+    else:
+        kernel_name = f"k_stream<{w.head_dim}, fp8 K={fp8k}> (sp_score_attention)"
     result = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -247,12 +289,13 @@ def main():
                    "select": f"{mode} {param}", "score_algo": args.algo, "kept_tokens": kept,
                    "k_cache": "fp8 e4m3 codes, fp32 scale per (layer, KV head)" if fp8k
                    else "same type as Q",
-                   "prefill_row": w.prefill_row, "pool_before_max": w.pool_before_max},
+                   "prefill_row": w.prefill_row, "pool_before_max": w.pool_before_max,
+                   **({"window": w.window, "stride": w.stride, "windows": len(inp.lengths),
+                       "window_tokens": int(inp.offsets[-1]), "max_keep": w.max_keep}
+                      if tool else {})},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": ("k_stats + k_lse + k_score_pooled (sp_score_attention)"
-                                if w.pool_before_max else
-                                f"k_stream<{w.head_dim}, fp8 K={fp8k}> (sp_score_attention)"),
+                     "kernel": kernel_name,
                      "launch_us": ms_score * 1e3,
                      "algorithmic_bytes": alg_bytes,
                      "achievable": {"read": read_gbs, "frac": achieved / read_gbs,
@@ -261,7 +304,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(inp, mode, param)
+        result["cpu_baseline"] = (cpu_baseline_tool(win_inp) if tool else
+                                  cpu_baseline(inp, mode, param))
     print(json.dumps(result), flush=True)
 
 

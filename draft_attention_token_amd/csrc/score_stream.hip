@@ -48,10 +48,14 @@
 //    in LDS. Compute and control waves hand data over through LDS flags
 //    rather than block barriers, so a late lse only stalls the compute
 //    waves when they need it.
-//  * The compute waves fold problem i - 2 while working on problem i: they
-//    park e in LDS (two problem slots) and turn it into probabilities
+//  * The compute waves fold problem i - lag while working on problem i: they
+//    park e in LDS (lag problem slots) and turn it into probabilities
 //    p = e * 2^(m_tile - lse) once the lse is staged, kept as a running max
-//    per (row, key) in registers (max over layers and KV groups).
+//    per (row, key) in registers (max over layers and KV groups). The parked
+//    tiles fill the same LDS whatever the lag: 2 problems of 3 tiles per
+//    wave, 3 of 2, or 6 of 1. A launch whose blocks own few tiles (shorter
+//    prompts) takes the deepest lag that fits, so that more problems pass
+//    while the exchange of one is in flight.
 //  * Finally: max over the G heads of a step (lanes of a group), mean over
 //    the L steps (a butterfly across groups of lanes), store.
 //
@@ -69,6 +73,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "score_common.h"
 
@@ -79,9 +84,9 @@ constexpr int kCompute = 6;                       // compute waves per block
 constexpr int kControl = 2;                       // control waves (even / odd problems)
 constexpr int kWaves = kCompute + kControl;
 constexpr int kThreads = kWaves * 64;
-constexpr int kTPW = 3;                           // tiles per compute wave
-constexpr int kTilesPerCta = kCompute * kTPW;     // 18
-constexpr int kLag = 2;                           // problems between logits and fold
+constexpr int kSlots = 6;                         // parked tiles per wave: lag x tiles per wave
+constexpr int kMaxTPW = 3;                        // tiles per compute wave at the shortest lag
+constexpr int kTilesPerCta = kCompute * kMaxTPW;  // 18
 constexpr uint64_t kWaitTicks = 200000000ull;     // wall clock runs at 100 MHz: 2 s
 constexpr int kQPad = 8;                          // bf16 padding per staged Q row
 constexpr int kDies = 8;                          // XCDs; block c runs on die c % 8
@@ -119,19 +124,19 @@ __host__ __device__ constexpr int64_t die_slot(int x, int bb, int die) {
   return (((int64_t)x * SP_MAX_PROMPTS + bb) * kDies + die) * kRows;
 }
 
-template <int D>
+template <int D, int kLag>
 struct Smem {
-  f32x4 eprev[kLag][kCompute][kTPW][4][64];   // parked e values (16-byte slots per lane)
+  f32x4 eprev[kLag][kCompute][kSlots / kLag][4][64];   // parked e (16-byte slots per lane)
   __bf16 q[kRows][D + kQPad];                 // staged Q rows of the next problem
   float2 red[2][kCompute][kRows];             // per-wave (m, z) of a problem, by parity
-  float lse[2][kRows];                        // staged row lse, by problem parity
+  float lse[kLag][kRows];                     // staged row lse, by problem mod lag
   // Hand-offs between the compute waves and the control waves (no block
   // barrier inside the main loop, so neither side waits for the other
   // unless it needs the other's data). Counters are cumulative.
   int q_seq;         // Q of problems < q_seq has been staged (one at a time)
   int q_used;        // compute waves that have read the staged Q
   int stats_cnt;     // compute waves that have written their statistics
-  int lse_ready[2];  // lse[s] holds problem lse_ready[s] - 1 (0: nothing yet)
+  int lse_ready[kLag];  // lse[s] holds problem lse_ready[s] - 1 (0: nothing yet)
   int lse_used;      // compute waves that have folded with a staged lse
 };
 
@@ -196,8 +201,8 @@ __device__ __forceinline__ void load_q(QRegs<D> &qr, const AttnShape &s, const _
   }
 }
 
-template <int D>
-__device__ __forceinline__ void store_q(Smem<D> &sm, const QRegs<D> &qr, int lane) {
+template <int D, typename S>
+__device__ __forceinline__ void store_q(S &sm, const QRegs<D> &qr, int lane) {
   const int row = lane >> 1, h = lane & 1;
   u32x4 *dst = reinterpret_cast<u32x4 *>(&sm.q[row][h * (D / 2)]);
 #pragma unroll
@@ -370,7 +375,7 @@ __device__ void merge_block(const AttnShape &s, const StreamTable &tb, int d, in
 // One level of the final butterfly on every value of the wave's tiles:
 // Ctrl >= 0 is a DPP control (within rows of 16 lanes), -1 the swizzle that
 // exchanges lane bit 4 (within groups of 32 lanes). Max or sum.
-template <int Ctrl>
+template <int Ctrl, int kTPW>
 __device__ __forceinline__ void butterfly_level(f32x16 (&run)[kTPW], bool use_max) {
 #pragma unroll
   for (int t = 0; t < kTPW; ++t)
@@ -387,14 +392,15 @@ __device__ __forceinline__ void butterfly_level(f32x16 (&run)[kTPW], bool use_ma
 // kF8: K holds fp8 e4m3 codes, key value = kscale[problem] * code; each code
 // becomes a bf16 exactly (v_cvt_scalef32_pk_bf16_fp8 with scale 1) and the
 // scale joins the logit scale of its problem.
-template <int D, bool kF8>
+template <int D, bool kF8, int kLag>
 __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable tb,
                                                         int64_t total_keys,
                                                         const __bf16 *__restrict__ q,
                                                         const uint8_t *__restrict__ k,
                                                         float *__restrict__ imp, StreamWs ws,
                                                         KScales ks) {
-  __shared__ Smem<D> sm;
+  constexpr int kTPW = kSlots / kLag;           // tiles per compute wave
+  __shared__ Smem<D, kLag> sm;
   const int cta = blockIdx.x;
   // The wave index is uniform across a wave; saying so keeps every value
   // derived from it in scalar registers and every branch on it scalar.
@@ -413,8 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
     sm.q_seq = 0;
     sm.q_used = 0;
     sm.stats_cnt = 0;
-    sm.lse_ready[0] = 0;
-    sm.lse_ready[1] = 0;
+    for (int i = 0; i < kLag; ++i) sm.lse_ready[i] = 0;
     sm.lse_used = 0;
     __hip_atomic_store(ws.hdr + 1, ws.call_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -678,8 +683,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
       // Fold problem it - kLag once its lse is staged: p = e * 2^(m_tile -
       // lse), max into run; then its LDS slot takes this problem's e (same
       // lane, in order).
-      lds_wait_ge(&sm.lse_ready[(it - kLag) & 1], it - kLag + 1, ws);
-      const float l2 = sm.lse[(it - kLag) & 1][r];
+      lds_wait_ge(&sm.lse_ready[(it - kLag) % kLag], it - kLag + 1, ws);
+      const float l2 = sm.lse[(it - kLag) % kLag][r];
       if (lane == 0) lds_inc(&sm.lse_used);
 #pragma unroll
       for (int t = 0; t < kTPW; ++t) {
@@ -732,6 +737,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
 struct DeviceInfo {
   int cus = 0;
   int occ64 = 0, occ128 = 0;
+  int occ_deep = 0;   // the deepest-lag form (the most shared memory)
 };
 
 const DeviceInfo &device_info() {
@@ -744,10 +750,12 @@ const DeviceInfo &device_info() {
   if (!done[dev]) {
     DeviceInfo d;
     if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.occ64, k_stream<64, false>, kThreads, 0) !=
-            hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.occ128, k_stream<128, false>, kThreads,
-                                                     0) != hipSuccess)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.occ64, k_stream<64, false, 2>, kThreads,
+                                                     0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.occ128, k_stream<128, false, 2>, kThreads,
+                                                     0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.occ_deep, k_stream<128, false, 6>,
+                                                     kThreads, 0) != hipSuccess)
       d = DeviceInfo();
     info[dev] = d;
     done[dev] = true;
@@ -762,6 +770,7 @@ struct Plan {
   int n_launch = 0;
   StreamTable t[SP_MAX_PROMPTS];
   int grid[SP_MAX_PROMPTS];
+  int max_tiles[SP_MAX_PROMPTS];   // most tiles a streaming block of the launch owns
 };
 
 bool make_plan(const SegTable &tok, int L, int n_stream, Plan &plan) {
@@ -808,6 +817,14 @@ bool make_plan(const SegTable &tok, int L, int n_stream, Plan &plan) {
       t.cta_off[i + 1] = t.cta_off[i] + need[i];
     }
     t.tok_off[B] = tok.tok_off[p0 + B];
+    // A block owns ceil(keys / blocks) keys at most, counted in tiles from
+    // its first key.
+    int most = 1;
+    for (int i = 0; i < B; ++i) {
+      const int nk = tok.tok_off[p0 + i + 1] - tok.tok_off[p0 + i] + L;
+      most = std::max(most, ((nk + need[i] - 1) / need[i] + kTile - 1) / kTile);
+    }
+    plan.max_tiles[plan.n_launch] = most;
     t.n_stream = t.cta_off[B];
     t.merge0 = (t.n_stream + kDies - 1) / kDies * kDies;
     plan.grid[plan.n_launch] = t.merge0 + kDies;
@@ -820,7 +837,7 @@ bool make_plan(const SegTable &tok, int L, int n_stream, Plan &plan) {
 // blocks, so that every block of a launch is resident at once.
 int stream_ctas(const AttnShape &s) {
   const DeviceInfo &d = device_info();
-  const int occ = s.d == 128 ? d.occ128 : d.occ64;
+  const int occ = std::min(s.d == 128 ? d.occ128 : d.occ64, d.occ_deep);
   if (occ < 1 || d.cus < 2 * kDies) return 0;
   return std::min(d.cus / kDies * kDies, kMaxCtas) - kDies;
 }
@@ -873,8 +890,18 @@ hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const 
   const uint8_t *kp = reinterpret_cast<const uint8_t *>(k);
   const bool f8 = s.dtype == SP_DTYPE_BF16_FP8K;
   for (int li = 0; li < plan.n_launch; ++li) {
-    auto kern = s.d == 128 ? (f8 ? k_stream<128, true> : k_stream<128, false>)
-                           : (f8 ? k_stream<64, true> : k_stream<64, false>);
+    // The deepest lag whose tiles per wave cover the launch's largest block.
+    const int need_tpw = (plan.max_tiles[li] + kCompute - 1) / kCompute;
+    const int lag = need_tpw <= 1 ? 6 : need_tpw == 2 ? 3 : 2;
+    auto pick = [&](auto d_tag, auto f8_tag) {
+      constexpr int Dv = decltype(d_tag)::value;
+      constexpr bool F8v = decltype(f8_tag)::value;
+      return lag == 6 ? k_stream<Dv, F8v, 6> : lag == 3 ? k_stream<Dv, F8v, 3> : k_stream<Dv, F8v, 2>;
+    };
+    using D64 = std::integral_constant<int, 64>;
+    using D128 = std::integral_constant<int, 128>;
+    auto kern = s.d == 128 ? (f8 ? pick(D128{}, std::true_type{}) : pick(D128{}, std::false_type{}))
+                           : (f8 ? pick(D64{}, std::true_type{}) : pick(D64{}, std::false_type{}));
     hipLaunchKernelGGL(kern, dim3(plan.grid[li]), dim3(kThreads), 0, st, s, plan.t[li], total_keys,
                        qp, kp, imp, w, ks);
     const hipError_t e = hipGetLastError();

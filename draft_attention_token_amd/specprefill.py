@@ -458,6 +458,7 @@ class ToolPipeline:
         self.n = int(n_tokens)
         self.starts, self.lengths, self.keeps = window_plan(n_tokens, window, stride)
         self.windows = Batch(np.concatenate([[0], np.cumsum(self.lengths)]))
+        self.batch = self.windows          # the batch sp_score_attention scores
         self.prompt = Batch([0, self.n])
         fm, lm = (1.5, 1.3) if boost else (1.0, 1.0)
         self.adesc = attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype,

@@ -317,6 +317,19 @@ def test_full_size_single_prompt(name):
             assert keep[c] == 1 or st < floor, f"planted chunk {c} dropped"
 
 
+@pytest.mark.parametrize("n", [70000, 9000])
+def test_fold_lag_forms(n):
+    """The single-pass kernel folds 2, 3 or 6 problems behind, by how many
+    tiles its blocks own: 70000 tokens over 248 blocks give 9 tiles per block
+    (lag 3), 9000 tokens 2 (lag 6); the 128K prompts above run at lag 2."""
+    w = workloads.small_workload("n32k_bf16", lengths=(n,), n_spans=8)
+    inp = workloads.make_inputs(w)
+    mode, param = w.select
+    pipe = run_gpu(inp, mode, param)
+    excused, _ = compare(inp, pipe, mode, param)
+    print(f"[gpu] lag form n={n}: excused differing chunks = {excused}", flush=True)
+
+
 def test_ragged_batch_sampled_prompts():
     """16 prompts, 2K-64K tokens: the four shortest prompts are compared end
     to end (oracle on a sub-batch of their own Q/K); every prompt is checked
