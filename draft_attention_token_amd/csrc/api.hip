@@ -398,7 +398,7 @@ sp_status sp_select_legacy_workspace_bytes(const sp_batch *batch, int32_t chunk_
   if (st != SP_OK) return st;
   if ((st = check_chunks(batch, chunk_size, &max_nc)) != SP_OK) return st;
   const SegTable chunks = make_table(batch, 0, chunk_size, 0);
-  *bytes = align_up((size_t)chunks.unit_off[chunks.B]) + align_up(sizeof(int32_t) * chunks.B);
+  *bytes = legacy_ws(chunks.B, chunks.unit_off[chunks.B], nullptr).bytes;
   return SP_OK;
 }
 
@@ -416,8 +416,7 @@ sp_status sp_select_legacy(const sp_batch *batch, int32_t chunk_size, float keep
   if (!chunk_scores || !token_ids || !kept_ids || !kept_pos || !kept_offsets)
     return SP_ERR_INVALID_ARGUMENT;
   const SegTable chunks = make_table(batch, 0, chunk_size, 0);
-  const size_t flags_bytes = align_up((size_t)chunks.unit_off[chunks.B]);
-  if (!ws || ws_bytes < flags_bytes + align_up(sizeof(int32_t) * chunks.B))
+  if (!ws || ws_bytes < legacy_ws(chunks.B, chunks.unit_off[chunks.B], nullptr).bytes)
     return SP_ERR_WORKSPACE_TOO_SMALL;
   LegacyTable t;
   memset(&t, 0, sizeof(t));
@@ -430,6 +429,7 @@ sp_status sp_select_legacy(const sp_batch *batch, int32_t chunk_size, float keep
     t.tok_off[b] = chunks.tok_off[b];
     t.chunk_off[b] = chunks.unit_off[b];
     t.blk_off[b + 1] = t.blk_off[b] + legacy_rank_blocks(nc);
+    t.wblk_off[b + 1] = t.wblk_off[b] + legacy_write_blocks(n);
     // Effective minimum min(min_tokens, max(4, n / 10)); a prompt no longer
     // than it, or keep_pct >= 1, keeps every chunk and needs no fill.
     const int32_t eff = std::min(min_tokens, std::max(4, n / 10));
@@ -444,10 +444,8 @@ sp_status sp_select_legacy(const sp_batch *batch, int32_t chunk_size, float keep
   }
   t.tok_off[t.B] = chunks.tok_off[t.B];
   t.chunk_off[t.B] = chunks.unit_off[t.B];
-  uint8_t *in = reinterpret_cast<uint8_t *>(ws);
-  int32_t *counts = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(ws) + flags_bytes);
-  return launched(launch_legacy(t, chunk_scores, token_ids, in, counts, kept_ids, kept_pos,
-                                kept_offsets, reinterpret_cast<hipStream_t>(stream)));
+  return launched(launch_legacy(t, chunk_scores, token_ids, ws, kept_ids, kept_pos, kept_offsets,
+                                reinterpret_cast<hipStream_t>(stream)));
 }
 
 sp_status sp_break_even(int64_t n_tokens, int64_t n_kept, double spec_tps, double target_tps,

@@ -132,12 +132,23 @@ struct LegacyTable {
   int32_t tok_off[SP_MAX_PROMPTS + 1];
   int32_t chunk_off[SP_MAX_PROMPTS + 1];
   int32_t blk_off[SP_MAX_PROMPTS + 1];     // rank-kernel block prefix per prompt
+  int32_t wblk_off[SP_MAX_PROMPTS + 1];    // write-kernel block prefix per prompt
   int32_t kc[SP_MAX_PROMPTS];              // chunks ranked in (all of them: keep everything)
   int32_t eff_min[SP_MAX_PROMPTS];         // kept-token floor (0: none)
 };
+struct LegacyWs {
+  uint8_t *in;            // [chunks] chunk kept by rank
+  int32_t *kept_before;   // [chunks] kept tokens before the chunk (fill included)
+  int32_t *rest_before;   // [chunks] tokens outside the base set before the chunk
+  int32_t *counts;        // [B] kept tokens after the cap
+  int32_t *stats;         // [B][2] kept tokens before the cap, fill
+  size_t bytes;
+};
+LegacyWs legacy_ws(int B, int total_chunks, void *base);
 int legacy_rank_blocks(int nc);
+int legacy_write_blocks(int n);
 hipError_t launch_legacy(const LegacyTable &t, const float *chunk_scores, const int32_t *ids,
-                         uint8_t *in, int32_t *counts, int32_t *kept_ids, int32_t *kept_pos,
-                         int64_t *kept_offsets, hipStream_t st);
+                         void *ws, int32_t *kept_ids, int32_t *kept_pos, int64_t *kept_offsets,
+                         hipStream_t st);
 
 }  // namespace sp

@@ -12,14 +12,15 @@
 // k_legacy_rank: one thread per chunk; a chunk is in when fewer than kc
 //   chunk means of its prompt are strictly larger (the same set as "reaches
 //   the kc-th largest mean", ties included), counted over LDS stages.
-// k_legacy_list<false>, then <true>: one block per prompt, three sweeps over
-//   the prompt's tokens with block scans. A token is kept when its chunk is
-//   in, when it is one of the first four or last two tokens, or when it is
-//   among the first F remaining tokens in index order (F tops the count up to
-//   the effective minimum). The first launch stores each prompt's count
-//   after the cap; the second packs the prompts by those counts and writes
-//   ids and positions, keeping every step-th token and the final one when the
-//   count exceeds the cap.
+// A token is kept when its chunk is in, when it is one of the first four or
+// last two tokens, or when it is among the first F remaining tokens in index
+// order (F tops the count up to the effective minimum).
+// k_legacy_scan: one block per prompt, chunk-level exact integer scans of the
+//   kept and remaining tokens; each chunk gets its first kept index, the
+//   prompt its count before the cap and after it.
+// k_legacy_write: one thread per token; its kept index follows from its
+//   chunk's scan values in O(1), and the cap (above max_keep tokens: every
+//   step-th one, the final one in the last slot) picks its output slot.
 #include "sp_internal.h"
 
 namespace sp {
@@ -75,94 +76,128 @@ __global__ __launch_bounds__(kRankThreads) void k_legacy_rank(LegacyTable t,
   if (i < nc) in[c0 + i] = above < t.kc[b] ? 1 : 0;
 }
 
-// Exclusive scan of v over the block; *total gets the block's sum.
-__device__ __forceinline__ int block_scan(int v, int *total, int *wave_tot) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
+// Always-kept tokens (0-3 and, for n > 4, n - 2 and n - 1; a set, so n - 2
+// = 3 at n = 5 counts once) in [lo, x).
+__device__ __forceinline__ int always_before(int n, int lo, int x) {
+  int k = max(0, min(x, 4) - lo);
+  if (n > 4) {
+    k += (n - 2 >= 4 && n - 2 >= lo && n - 2 < x) ? 1 : 0;
+    k += (n - 1 >= lo && n - 1 < x) ? 1 : 0;
   }
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  int before = incl - v, tot = 0;
-  for (int w = 0; w < kListThreads / 64; ++w) {
-    before += w < wave ? wave_tot[w] : 0;
-    tot += wave_tot[w];
-  }
-  __syncthreads();
-  *total = tot;
-  return before;
+  return k;
 }
 
-template <bool kWrite>
-__global__ __launch_bounds__(kListThreads) void k_legacy_list(
-    LegacyTable t, const uint8_t *__restrict__ in, const int32_t *__restrict__ ids,
-    int32_t *__restrict__ counts, int32_t *__restrict__ kept_ids, int32_t *__restrict__ kept_pos,
-    int64_t *__restrict__ kept_offsets) {
-  __shared__ int wave_tot[kListThreads / 64];
-  __shared__ int64_t base_off;
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int n = t.tok_off[b + 1] - t.tok_off[b], c0 = t.chunk_off[b], C = t.C;
-  const int per = (n + kListThreads - 1) / kListThreads;
-  const int t0 = min(n, tid * per), t1 = min(n, t0 + per);
-  auto base = [&](int x) {
-    return in[c0 + x / C] != 0 || x < 4 || (n > 4 && x >= n - 2);
-  };
-  // Sweep 1: chunk, first-four and last-two tokens.
-  int nb = 0;
-  for (int x = t0; x < t1; ++x) nb += base(x) ? 1 : 0;
-  int k0;
-  const int base_before = block_scan(nb, &k0, wave_tot);
-  const int fill = max(0, t.eff_min[b] - k0);
-  // Sweep 2: the fill takes the first `fill` other tokens in index order (a
-  // token's rank among them is x minus the base tokens before it).
-  int nf = 0, bcount = base_before;
-  for (int x = t0; x < t1; ++x) {
-    const bool bs = base(x);
-    nf += (bs || x - bcount < fill) ? 1 : 0;
-    bcount += bs ? 1 : 0;
+// Per prompt, over its chunks (16 per thread, index order): base tokens
+// (kept chunks whole, plus the always-kept tokens of the others) and the
+// remaining tokens; exclusive scans of both give each chunk's first kept
+// index, with the fill (the first `fill` remaining tokens in index order)
+// counted in. Also the prompt's kept count before the cap, and the fill.
+__global__ __launch_bounds__(kListThreads) void k_legacy_scan(LegacyTable t,
+                                                              const uint8_t *__restrict__ in,
+                                                              int32_t *__restrict__ kept_before,
+                                                              int32_t *__restrict__ rest_before,
+                                                              int32_t *__restrict__ counts,
+                                                              int32_t *__restrict__ stats) {
+  constexpr int kEPT = SP_MAX_CHUNKS_PER_PROMPT / kListThreads;   // chunks per thread
+  __shared__ int tot_b[kListThreads / 64], tot_r[kListThreads / 64];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c0 = t.chunk_off[b], nc = t.chunk_off[b + 1] - c0;
+  const int n = t.tok_off[b + 1] - t.tok_off[b], C = t.C;
+  int nb[kEPT], nr[kEPT];
+  int mb = 0, mr = 0;
+#pragma unroll
+  for (int e = 0; e < kEPT; ++e) {
+    const int c = tid * kEPT + e;
+    const int lo = c * C, size = c < nc ? min(C, n - lo) : 0;
+    const int base = c < nc ? (in[c0 + c] ? size : always_before(n, lo, lo + size)) : 0;
+    nb[e] = base;
+    nr[e] = size - base;
+    mb += nb[e];
+    mr += nr[e];
   }
-  int K;
-  const int kept_before = block_scan(nf, &K, wave_tot);
-  if (!kWrite) {
-    if (tid == 0) counts[b] = min(K, t.max_keep);
-    return;
+  int ib = mb, ir = mr;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ob = __shfl_up(ib, off, 64), orr = __shfl_up(ir, off, 64);
+    if (lane >= off) { ib += ob; ir += orr; }
+  }
+  if (lane == 63) { tot_b[wave] = ib; tot_r[wave] = ir; }
+  __syncthreads();
+  int rb = ib - mb, rr = ir - mr, K0 = 0, R = 0;
+  for (int w = 0; w < kListThreads / 64; ++w) {
+    rb += w < wave ? tot_b[w] : 0;
+    rr += w < wave ? tot_r[w] : 0;
+    K0 += tot_b[w];
+    R += tot_r[w];
+  }
+  const int fill = min(R, max(0, t.eff_min[b] - K0));
+#pragma unroll
+  for (int e = 0; e < kEPT; ++e) {
+    const int c = tid * kEPT + e;
+    if (c < nc) {
+      kept_before[c0 + c] = rb + min(rr, fill);
+      rest_before[c0 + c] = rr;
+    }
+    rb += nb[e];
+    rr += nr[e];
   }
   if (tid == 0) {
+    const int K = K0 + fill;
+    counts[b] = min(K, t.max_keep);
+    stats[2 * b] = K;
+    stats[2 * b + 1] = fill;
+  }
+}
+
+// One thread per token, 1024 tokens per block: the token's kept index
+// follows from its chunk's scan values, then the cap picks its slot.
+__global__ __launch_bounds__(kListThreads) void k_legacy_write(
+    LegacyTable t, const uint8_t *__restrict__ in, const int32_t *__restrict__ kept_before,
+    const int32_t *__restrict__ rest_before, const int32_t *__restrict__ counts,
+    const int32_t *__restrict__ stats, const int32_t *__restrict__ ids,
+    int32_t *__restrict__ kept_ids, int32_t *__restrict__ kept_pos,
+    int64_t *__restrict__ kept_offsets) {
+  __shared__ int64_t s_off;
+  const int b = table_prompt(t.wblk_off, t.B, blockIdx.x);
+  const int n = t.tok_off[b + 1] - t.tok_off[b], C = t.C, c0 = t.chunk_off[b];
+  const int x = (blockIdx.x - t.wblk_off[b]) * kListThreads + threadIdx.x;
+  if (threadIdx.x == 0) {
     int64_t s = 0;
     for (int p = 0; p < b; ++p) s += counts[p];
-    base_off = s;
-    kept_offsets[b] = s;
-    if (b == t.B - 1) {
-      kept_offsets[0] = 0;
-      kept_offsets[t.B] = s + counts[b];
+    s_off = s;
+    if (blockIdx.x == t.wblk_off[b]) {
+      kept_offsets[b] = s;
+      if (b == t.B - 1) kept_offsets[t.B] = s + counts[b];
     }
   }
   __syncthreads();
-  const int64_t off = base_off;
-  // Sweep 3: write, thinned to max_keep (every step-th kept token, the last
-  // slot taking the final kept token) when there are more.
-  const bool thin = K > t.max_keep;
-  const int step = thin ? K / t.max_keep : 1;
-  int ki = kept_before;
-  bcount = base_before;
-  for (int x = t0; x < t1; ++x) {
-    const bool bs = base(x);
-    const bool f = bs || x - bcount < fill;
-    bcount += bs ? 1 : 0;
-    if (!f) continue;
-    int slot = ki;
-    if (thin) {
-      if (ki == K - 1) slot = t.max_keep - 1;
-      else if (ki % step == 0 && ki / step < t.max_keep - 1) slot = ki / step;
-      else slot = -1;
-    }
-    if (slot >= 0) {
-      kept_ids[off + slot] = ids[t.tok_off[b] + x];
-      kept_pos[off + slot] = x;
-    }
-    ++ki;
+  if (x >= n) return;
+  const int c = x / C, lo = c * C;
+  const int K = stats[2 * b], fill = stats[2 * b + 1];
+  bool kept;
+  int ki;
+  if (in[c0 + c]) {
+    kept = true;
+    ki = kept_before[c0 + c] + (x - lo);
+  } else {
+    // Before x in this chunk: a always-kept tokens and x - lo - a others,
+    // of which those with a rank below `fill` are kept.
+    const int a = always_before(n, lo, x);
+    const int rest_rank = rest_before[c0 + c] + (x - lo - a);
+    const bool always = x < 4 || (n > 4 && x >= n - 2);
+    kept = always || rest_rank < fill;
+    ki = kept_before[c0 + c] + a + max(0, min(fill, rest_rank) - min(fill, rest_before[c0 + c]));
+  }
+  if (!kept) return;
+  int slot = ki;
+  if (K > t.max_keep) {
+    const int step = K / t.max_keep;
+    if (ki == K - 1) slot = t.max_keep - 1;
+    else if (ki % step == 0 && ki / step < t.max_keep - 1) slot = ki / step;
+    else slot = -1;
+  }
+  if (slot >= 0) {
+    kept_ids[s_off + slot] = ids[t.tok_off[b] + x];
+    kept_pos[s_off + slot] = x;
   }
 }
 
@@ -178,15 +213,36 @@ hipError_t launch_stitch(const StitchTable &t, int32_t n, const float *win_imp, 
 }
 
 hipError_t launch_legacy(const LegacyTable &t, const float *chunk_scores, const int32_t *ids,
-                         uint8_t *in, int32_t *counts, int32_t *kept_ids, int32_t *kept_pos,
-                         int64_t *kept_offsets, hipStream_t st) {
+                         void *ws, int32_t *kept_ids, int32_t *kept_pos, int64_t *kept_offsets,
+                         hipStream_t st) {
+  const LegacyWs w = legacy_ws(t.B, t.chunk_off[t.B], ws);
   hipLaunchKernelGGL(k_legacy_rank, dim3(t.blk_off[t.B]), dim3(kRankThreads), 0, st, t,
-                     chunk_scores, in);
-  hipLaunchKernelGGL(k_legacy_list<false>, dim3(t.B), dim3(kListThreads), 0, st, t, in, ids,
-                     counts, kept_ids, kept_pos, kept_offsets);
-  hipLaunchKernelGGL(k_legacy_list<true>, dim3(t.B), dim3(kListThreads), 0, st, t, in, ids,
-                     counts, kept_ids, kept_pos, kept_offsets);
+                     chunk_scores, w.in);
+  hipLaunchKernelGGL(k_legacy_scan, dim3(t.B), dim3(kListThreads), 0, st, t, w.in, w.kept_before,
+                     w.rest_before, w.counts, w.stats);
+  hipLaunchKernelGGL(k_legacy_write, dim3(t.wblk_off[t.B]), dim3(kListThreads), 0, st, t, w.in,
+                     w.kept_before, w.rest_before, w.counts, w.stats, ids, kept_ids, kept_pos,
+                     kept_offsets);
   return hipGetLastError();
+}
+
+int legacy_write_blocks(int n) { return (n + kListThreads - 1) / kListThreads; }
+
+LegacyWs legacy_ws(int B, int total_chunks, void *base) {
+  LegacyWs w;
+  char *p = reinterpret_cast<char *>(base);
+  w.in = reinterpret_cast<uint8_t *>(p);
+  p += align_up((size_t)total_chunks);
+  w.kept_before = reinterpret_cast<int32_t *>(p);
+  p += align_up(sizeof(int32_t) * (size_t)total_chunks);
+  w.rest_before = reinterpret_cast<int32_t *>(p);
+  p += align_up(sizeof(int32_t) * (size_t)total_chunks);
+  w.counts = reinterpret_cast<int32_t *>(p);
+  p += align_up(sizeof(int32_t) * (size_t)B);
+  w.stats = reinterpret_cast<int32_t *>(p);
+  p += align_up(2 * sizeof(int32_t) * (size_t)B);
+  w.bytes = (size_t)(p - reinterpret_cast<char *>(base));
+  return w;
 }
 
 }  // namespace sp

@@ -428,3 +428,26 @@ def test_tool_windows_legacy_selection(name, base, kw):
     if ora["kept"].size <= w.max_keep and w.keep_pct >= 0.25:
         for c in wi.spans:                                # planted spans survive an uncapped rule
             assert np.isin(np.arange(32 * c, 32 * c + 32), got_pos).all(), c
+
+
+@pytest.mark.parametrize("C, keep, min_tok, max_keep", [(32, 0.3, 128, 2000), (1, 0.05, 4, 5),
+                                                         (16, 0.01, 10 ** 6, 70), (3, 0.9, 0, 1),
+                                                         (32, 1.0, 128, 100)])
+def test_select_legacy_edge_batch(C, keep, min_tok, max_keep):
+    """sp_select_legacy on given chunk scores (many ties) for a batch of 20
+    prompts from 1 to 5000 tokens: exactly the oracle's rule and cap."""
+    lengths = [1, 2, 3, 4, 5, 6, 7, 9, 31, 33, 64, 100, 250, 1000, 3000, 5000, 17, 129, 4, 777]
+    rng = np.random.default_rng(C * 1000 + max_keep)
+    batch = sp.Batch(np.concatenate([[0], np.cumsum(lengths)]))
+    means = [np.round(rng.random(-(-n // C)) * 4).astype(np.float32) / 4 for n in lengths]
+    cs = torch.from_numpy(np.concatenate(means)).to(DEV)
+    ids = torch.from_numpy(rng.integers(0, 1 << 17, batch.total).astype(np.int32)).to(DEV)
+    kid, kpos, koff = sp.select_legacy(batch, C, keep, min_tok, max_keep, cs, ids)
+    torch.cuda.synchronize()
+    kid, kpos, koff = kid.cpu().numpy(), kpos.cpu().numpy(), koff.cpu().numpy()
+    ids = ids.cpu().numpy()
+    assert koff[0] == 0
+    for b, n in enumerate(lengths):
+        want = oracle.thin(oracle.select_legacy_from_means(means[b], n, C, keep, min_tok), max_keep)
+        np.testing.assert_array_equal(kpos[koff[b]:koff[b + 1]], want, err_msg=f"prompt {b} n={n}")
+        np.testing.assert_array_equal(kid[koff[b]:koff[b + 1]], ids[batch.offsets[b] + want])
