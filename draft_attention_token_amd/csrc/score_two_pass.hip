@@ -46,7 +46,10 @@ __device__ __forceinline__ f32x16 tile_logits(const AttnShape &s, const TileCtx 
 }
 
 // Pass 1: per (tile, layer, group), the base-2 max and sum of 2^(logit - max)
-// of each of the 32 rows over the tile's visible keys.
+// of each of the 32 rows over the tile's visible keys. One wave per (tile,
+// problem). K is the MFMA A operand, so a lane holds one query row (lane %
+// 32) and 16 of the tile's keys: each row's max and sum reduce inside the
+// lane plus one swap of wave halves.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void k_stats(AttnShape s, SegTable tiles, int64_t total_keys,
                                               int total_tiles, const T *__restrict__ q,
@@ -54,44 +57,62 @@ __global__ __launch_bounds__(64) void k_stats(AttnShape s, SegTable tiles, int64
   const int t = blockIdx.x, prob = blockIdx.y;
   const int l = prob / s.Hkv, g = prob - l * s.Hkv;
   const int lane = threadIdx.x, half = lane >> 5, col = lane & 31;
-  const TileCtx c = tile_ctx(tiles, t, col);
-  const f32x16 acc = tile_logits<T, D>(s, c, total_keys, q, k, l, g, lane);
+  const TileCtx c = tile_ctx(tiles, t, col);       // c.kl: the key this lane loads
   const int rows = s.L * s.G;
+  Frag<T, D> a, bk;
+  if (col < rows) a.load_cached(q_row_ptr(q, s, c.b, l, g, col), half); else a.zero();
+  if (c.kl < c.nkeys) bk.load(k_row_ptr(k, s, total_keys, l, c.key0 + c.kl, g), half); else bk.zero();
+  const f32x16 acc = mfma_tile<D>(bk, a);          // acc[i]: key acc_row(i, half), row col
+  const int j = col / s.G;
+  const int64_t kbase = c.kl - col;                // the tile's first key
+  float x[16], m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int row = acc_row(i, half);
-    const int j = row / s.G;
-    const bool vis = row < rows && c.kl < c.nkeys && c.kl <= c.N - s.pre + j;
-    const float x = vis ? acc[i] * s.scale_log2 : -INFINITY;
-    const float m = wave_max32(x);
-    const float e = vis ? exp2f(x - m) : 0.f;
-    const float z = wave_sum32(e);
-    if (col == 0) part[((int64_t)prob * total_tiles + t) * kRows + row] = make_float2(m, z);
+    const int64_t key = kbase + acc_row(i, half);
+    const bool vis = col < rows && key < c.nkeys && key <= c.N - s.pre + j;
+    x[i] = vis ? acc[i] * s.scale_log2 : -INFINITY;
+    m = fmaxf(m, x[i]);
   }
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  float z = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z += x[i] == -INFINITY ? 0.f : exp2f(x[i] - m);
+  z += __shfl_xor(z, 32, 64);
+  if (half == 0) part[((int64_t)prob * total_tiles + t) * kRows + col] = make_float2(m, z);
 }
 
 // Combine the tile statistics of each (prompt, layer, group, row) in a fixed
-// order: lse2 = m + log2(z) (base-2 log-sum-exp of the row's logits).
-__global__ __launch_bounds__(256) void k_lse(SegTable tiles, int n_prob, int total_tiles,
-                                             const float2 *__restrict__ part,
-                                             float *__restrict__ lse, uint32_t *__restrict__ hdr,
-                                             uint32_t call_tag) {
+// order: lse2 = m + log2(z) (base-2 log-sum-exp of the row's logits). 32
+// contiguous tile ranges per row, eight loads in flight per thread, then the
+// ranges merged in order.
+constexpr int kLseParts = 32;
+__global__ __launch_bounds__(kLseParts * kRows) void k_lse(SegTable tiles, int n_prob,
+                                                           int total_tiles,
+                                                           const float2 *__restrict__ part,
+                                                           float *__restrict__ lse,
+                                                           uint32_t *__restrict__ hdr,
+                                                           uint32_t call_tag) {
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) hdr[1] = call_tag;   // no waits here
-  __shared__ float2 sm[8][kRows];
+  __shared__ float2 sm[kLseParts][kRows];
   const int b = blockIdx.x, prob = blockIdx.y;
   const int row = threadIdx.x & 31, p = threadIdx.x >> 5;
   const int t0 = tiles.unit_off[b], t1 = tiles.unit_off[b + 1];
-  const int per = (t1 - t0 + 7) / 8;
+  const int per = (t1 - t0 + kLseParts - 1) / kLseParts;
   const int ta = t0 + p * per, tb = min(t1, ta + per);
+  const float2 *src = part + (int64_t)prob * total_tiles * kRows + row;
   float M = -INFINITY, Z = 0.f;
-  for (int t = ta; t < tb; ++t) {
-    const float2 v = part[((int64_t)prob * total_tiles + t) * kRows + row];
-    stats_merge(M, Z, v.x, v.y);
+  for (int t = ta; t < tb; t += 8) {
+    float2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = t + u < tb ? src[(int64_t)(t + u) * kRows] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) stats_merge(M, Z, v[u].x, v[u].y);
   }
   sm[p][row] = make_float2(M, Z);
   __syncthreads();
   if (p == 0) {
-    for (int i = 1; i < 8; ++i) stats_merge(M, Z, sm[i][row].x, sm[i][row].y);
+    for (int i = 1; i < kLseParts; ++i) stats_merge(M, Z, sm[i][row].x, sm[i][row].y);
     lse[((int64_t)b * n_prob + prob) * kRows + row] = (Z > 0.f) ? M + log2f(Z) : INFINITY;
   }
 }
@@ -201,15 +222,29 @@ __global__ __launch_bounds__(64) void k_score_pooled(AttnShape s, SegTable tiles
       float v[kTile / 2 + 2 * kPoolHalo];
 #pragma unroll
       for (int x = 0; x < kTile / 2 + 2 * kPoolHalo; ++x) v[x] = pv[c0 + x][col];
-#pragma unroll
-      for (int c = 0; c < kTile / 2; ++c) {
-        float w = 0.f;
-#pragma unroll
-        for (int o = -kPoolHalo; o <= kPoolHalo; ++o)
-          w += (o >= -r && o <= r) ? v[c + kPoolHalo + o] : 0.f;
+      auto emit = [&](int c, float w) {
         const int kk = k0 + c0 + c;
         const int lo = max(0, kk - r), hi = min(N - 1, kk + r);
         if (kk < N) atomicMax(&smax[col / s.G][c0 + c], __float_as_uint(w / (float)(hi - lo + 1)));
+      };
+      if (r == kDefaultPoolRadius) {
+        // The default width: the window is known at compile time.
+#pragma unroll
+        for (int c = 0; c < kTile / 2; ++c) {
+          float w = 0.f;
+#pragma unroll
+          for (int o = -kDefaultPoolRadius; o <= kDefaultPoolRadius; ++o) w += v[c + kPoolHalo + o];
+          emit(c, w);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < kTile / 2; ++c) {
+          float w = 0.f;
+#pragma unroll
+          for (int o = -kPoolHalo; o <= kPoolHalo; ++o)
+            w += (o >= -r && o <= r) ? v[c + kPoolHalo + o] : 0.f;
+          emit(c, w);
+        }
       }
     }
     __syncthreads();
@@ -231,8 +266,8 @@ hipError_t run(const AttnShape &s, const SegTable &tiles, int total_tiles, const
                                          align_up((size_t)n_prob * total_tiles * kRows * sizeof(float2)));
   hipLaunchKernelGGL((k_stats<T, D>), dim3(total_tiles, n_prob), dim3(64), 0, st, s, tiles,
                      total_keys, total_tiles, (const T *)q, (const T *)k, part);
-  hipLaunchKernelGGL(k_lse, dim3(tiles.B, n_prob), dim3(256), 0, st, tiles, n_prob, total_tiles,
-                     part, lse, hdr, reserve_tags(1));
+  hipLaunchKernelGGL(k_lse, dim3(tiles.B, n_prob), dim3(kLseParts * kRows), 0, st, tiles, n_prob,
+                     total_tiles, part, lse, hdr, reserve_tags(1));
   if (s.row_pool > 1)
     hipLaunchKernelGGL((k_score_pooled<T, D>), dim3((total_tiles + 7) / 8 * 8), dim3(64), 0, st, s,
                        tiles, total_keys, total_tiles, (const T *)q, (const T *)k, lse, imp);

@@ -9,9 +9,10 @@
 //
 // k_stitch: one thread per prompt token; it averages the scores of the
 //   windows whose kept range holds the token (1.0 when none does).
-// k_legacy_rank: one thread per chunk; a chunk is in when fewer than kc
-//   chunk means of its prompt are strictly larger (the same set as "reaches
-//   the kc-th largest mean", ties included), counted over LDS stages.
+// k_legacy_rank: 16 chunks per block, 16 thread groups splitting the other
+//   chunks; a chunk is in when fewer than kc chunk means of its prompt are
+//   strictly larger (the same set as "reaches the kc-th largest mean", ties
+//   included), counted over LDS stages.
 // A token is kept when its chunk is in, when it is one of the first four or
 // last two tokens, or when it is among the first F remaining tokens in index
 // order (F tops the count up to the effective minimum).
@@ -28,6 +29,8 @@ namespace {
 
 constexpr int kStitchThreads = 256;
 constexpr int kRankThreads = 256;
+constexpr int kRankChunks = 16;                          // chunks per block
+constexpr int kRankGroups = kRankThreads / kRankChunks;  // thread groups per chunk
 constexpr int kRankStage = 4096;
 constexpr int kListThreads = 1024;
 
@@ -61,9 +64,11 @@ __global__ __launch_bounds__(kRankThreads) void k_legacy_rank(LegacyTable t,
                                                               const float *__restrict__ cs,
                                                               uint8_t *__restrict__ in) {
   __shared__ float stage[kRankStage];
+  __shared__ int part[kRankGroups][kRankChunks];
   const int b = table_prompt(t.blk_off, t.B, blockIdx.x);
   const int c0 = t.chunk_off[b], nc = t.chunk_off[b + 1] - c0;
-  const int i = (blockIdx.x - t.blk_off[b]) * kRankThreads + threadIdx.x;
+  const int ci = threadIdx.x % kRankChunks, grp = threadIdx.x / kRankChunks;
+  const int i = (blockIdx.x - t.blk_off[b]) * kRankChunks + ci;
   const float mine = i < nc ? cs[c0 + i] : 0.f;
   int above = 0;
   for (int j0 = 0; j0 < nc; j0 += kRankStage) {
@@ -71,9 +76,14 @@ __global__ __launch_bounds__(kRankThreads) void k_legacy_rank(LegacyTable t,
     __syncthreads();
     for (int j = threadIdx.x; j < len; j += kRankThreads) stage[j] = cs[c0 + j0 + j];
     __syncthreads();
-    for (int j = 0; j < len; ++j) above += stage[j] > mine ? 1 : 0;
+    for (int j = grp; j < len; j += kRankGroups) above += stage[j] > mine ? 1 : 0;
   }
-  if (i < nc) in[c0 + i] = above < t.kc[b] ? 1 : 0;
+  part[grp][ci] = above;
+  __syncthreads();
+  if (grp == 0) {
+    for (int g = 1; g < kRankGroups; ++g) above += part[g][ci];
+    if (i < nc) in[c0 + i] = above < t.kc[b] ? 1 : 0;
+  }
 }
 
 // Always-kept tokens (0-3 and, for n > 4, n - 2 and n - 1; a set, so n - 2
@@ -203,7 +213,7 @@ __global__ __launch_bounds__(kListThreads) void k_legacy_write(
 
 }  // namespace
 
-int legacy_rank_blocks(int nc) { return (nc + kRankThreads - 1) / kRankThreads; }
+int legacy_rank_blocks(int nc) { return (nc + kRankChunks - 1) / kRankChunks; }
 
 hipError_t launch_stitch(const StitchTable &t, int32_t n, const float *win_imp, float *out,
                          hipStream_t st) {
