@@ -875,6 +875,12 @@ hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const 
   if (n_stream < 1) return hipSuccess;
   static thread_local Plan plan;
   if (!make_plan(tiles, s.La, n_stream, plan)) return hipSuccess;
+  // Lanes address K by 32-bit byte offsets from their prompt's first key row.
+  const int64_t rowb = (int64_t)s.Hkv * s.d * (s.dtype == SP_DTYPE_BF16_FP8K ? 1 : 2);
+  for (int b = 0; b < tiles.B; ++b) {
+    const int64_t nk = (int64_t)tiles.tok_off[b + 1] - tiles.tok_off[b] + s.La;
+    if (nk * rowb + rowb > (int64_t)UINT32_MAX) return hipSuccess;
+  }
   *supported = true;
   StreamWs w;
   char *base = reinterpret_cast<char *>(ws);

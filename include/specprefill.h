@@ -257,11 +257,12 @@ sp_status sp_gather_kept(const sp_batch *batch, int32_t chunk_size, const uint8_
  * 2 stride, ... and span min(window, n_tokens - start) tokens. A window is the
  * last one when it reaches the end of the prompt or when the next start would
  * (start + stride >= n_tokens); it keeps all of its tokens' scores, every
- * other window the first `stride` ones. Writes up to `capacity` entries of
- * starts, lengths and keep_lengths (host arrays) and the number of windows to
- * *n_windows; returns SP_ERR_INVALID_ARGUMENT if that exceeds capacity
- * (*n_windows then tells the size needed) or for n_tokens < 1, window < 1,
- * stride outside 1..window. */
+ * other window the first `stride` ones. Writes the number of windows to
+ * *n_windows and, when it fits in `capacity`, the windows to starts, lengths
+ * and keep_lengths (host arrays). A count above capacity, or NULL arrays,
+ * returns SP_ERR_INVALID_ARGUMENT with *n_windows still set: call with
+ * capacity 0 and NULL arrays to learn the size. Also SP_ERR_INVALID_ARGUMENT
+ * for n_tokens < 1 (or >= 2^30), window < 1, stride outside 1..window. */
 sp_status sp_window_plan(int64_t n_tokens, int32_t window, int32_t stride, int32_t capacity,
                          int64_t *starts, int32_t *lengths, int32_t *keep_lengths,
                          int32_t *n_windows);
