@@ -45,22 +45,48 @@ __device__ __forceinline__ f32x16 tile_logits(const AttnShape &s, const TileCtx 
   return mfma_tile<D>(a, bk);
 }
 
+// The Q rows of (prompt b, layer l, KV group g) into LDS rows, 16 bytes per
+// thread and step (rows >= L * G are left alone: no lane reads them).
+template <typename T, int D>
+__device__ __forceinline__ void stage_q_rows(T (*qs)[D + 16 / sizeof(T)], const AttnShape &s,
+                                             const T *q, int b, int l, int g, int tid, int nthr) {
+  constexpr int kVecs = D * (int)sizeof(T) / 16;   // 16-byte vectors per row
+  const int rows = s.L * s.G;
+  for (int i = tid; i < rows * kVecs; i += nthr) {
+    const int row = i / kVecs, v = i - row * kVecs;
+    reinterpret_cast<u32x4 *>(&qs[row][0])[v] =
+        reinterpret_cast<const u32x4 *>(q_row_ptr(q, s, b, l, g, row))[v];
+  }
+}
+
 // Pass 1: per (tile, layer, group), the base-2 max and sum of 2^(logit - max)
 // of each of the 32 rows over the tile's visible keys. One wave per (tile,
-// problem). K is the MFMA A operand, so a lane holds one query row (lane %
-// 32) and 16 of the tile's keys: each row's max and sum reduce inside the
-// lane plus one swap of wave halves.
+// problem), four waves (four consecutive tiles) per block; the block stages
+// the problem's Q rows in LDS once (a wave whose tile lies in another prompt
+// reads its own). K is the MFMA A operand, so a lane holds one query row
+// (lane % 32) and 16 of the tile's keys: each row's max and sum reduce inside
+// the lane plus one swap of wave halves.
+constexpr int kStatsWaves = 4;
 template <typename T, int D>
-__global__ __launch_bounds__(64) void k_stats(AttnShape s, SegTable tiles, int64_t total_keys,
-                                              int total_tiles, const T *__restrict__ q,
-                                              const T *__restrict__ k, float2 *__restrict__ part) {
-  const int t = blockIdx.x, prob = blockIdx.y;
+__global__ __launch_bounds__(64 * kStatsWaves) void k_stats(AttnShape s, SegTable tiles,
+                                                            int64_t total_keys, int total_tiles,
+                                                            const T *__restrict__ q,
+                                                            const T *__restrict__ k,
+                                                            float2 *__restrict__ part) {
+  __shared__ __align__(16) T qs[kRows][D + 16 / sizeof(T)];   // padded rows
+  const int t = blockIdx.x * kStatsWaves + (int)(threadIdx.x >> 6), prob = blockIdx.y;
   const int l = prob / s.Hkv, g = prob - l * s.Hkv;
-  const int lane = threadIdx.x, half = lane >> 5, col = lane & 31;
-  const TileCtx c = tile_ctx(tiles, t, col);       // c.kl: the key this lane loads
+  const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
   const int rows = s.L * s.G;
+  const int b0 = seg_of(tiles, blockIdx.x * kStatsWaves);
+  stage_q_rows<T, D>(qs, s, q, b0, l, g, threadIdx.x, 64 * kStatsWaves);
+  __syncthreads();
+  if (t >= total_tiles) return;
+  const TileCtx c = tile_ctx(tiles, t, col);       // c.kl: the key this lane loads
   Frag<T, D> a, bk;
-  if (col < rows) a.load_cached(q_row_ptr(q, s, c.b, l, g, col), half); else a.zero();
+  if (col >= rows) a.zero();
+  else if (c.b == b0) a.load_cached(&qs[col][0], half);
+  else a.load_cached(q_row_ptr(q, s, c.b, l, g, col), half);
   if (c.kl < c.nkeys) bk.load(k_row_ptr(k, s, total_keys, l, c.key0 + c.kl, g), half); else bk.zero();
   const f32x16 acc = mfma_tile<D>(bk, a);          // acc[i]: key acc_row(i, half), row col
   const int j = col / s.G;
@@ -264,8 +290,9 @@ hipError_t run(const AttnShape &s, const SegTable &tiles, int total_tiles, const
   float2 *part = reinterpret_cast<float2 *>(region);
   float *lse = reinterpret_cast<float *>(reinterpret_cast<char *>(part) +
                                          align_up((size_t)n_prob * total_tiles * kRows * sizeof(float2)));
-  hipLaunchKernelGGL((k_stats<T, D>), dim3(total_tiles, n_prob), dim3(64), 0, st, s, tiles,
-                     total_keys, total_tiles, (const T *)q, (const T *)k, part);
+  hipLaunchKernelGGL((k_stats<T, D>), dim3((total_tiles + kStatsWaves - 1) / kStatsWaves, n_prob),
+                     dim3(64 * kStatsWaves), 0, st, s, tiles, total_keys, total_tiles,
+                     (const T *)q, (const T *)k, part);
   hipLaunchKernelGGL(k_lse, dim3(tiles.B, n_prob), dim3(kLseParts * kRows), 0, st, tiles, n_prob,
                      total_tiles, part, lse, hdr, reserve_tags(1));
   if (s.row_pool > 1)
