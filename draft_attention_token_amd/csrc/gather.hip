@@ -85,12 +85,16 @@ __global__ __launch_bounds__(kWriteThreads) void k_gather_write(
   const int t1 = min(N, t0 + kGatherBlockTokens);
   const bool k0 = keep[c0] != 0;
   for (int t = t0 + tid; t < t1; t += kWriteThreads) {
+    // All three reads at once (every index is valid): one round trip.
     const int c = t / C;
+    const bool kc = keep[c0 + c] != 0;
+    const int32_t slot = chunk_out[c0 + c];
+    const int32_t id = ids[tok0 + t];
     int64_t out;
     if (t == 0 && !k0) out = base;
-    else if (keep[c0 + c]) out = base + (k0 ? 0 : 1) + chunk_out[c0 + c] + (t - c * C);
+    else if (kc) out = base + (k0 ? 0 : 1) + slot + (t - c * C);
     else continue;
-    kept_ids[out] = ids[tok0 + t];
+    kept_ids[out] = id;
     kept_pos[out] = t;
   }
 }

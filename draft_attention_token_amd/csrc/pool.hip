@@ -8,8 +8,8 @@
 // Improvements item 2 (first 64 tokens x1.5, last 128 x1.3), and Chunk
 // Selection (a chunk's score is the mean over the tokens it holds).
 //
-// Work is split into blocks of whole chunks, TB = C * floor(1024 / C) <= 1024
-// tokens of one prompt. A block stages its importance values plus a halo of
+// Work is split into blocks of whole chunks, TB = C * max(1, floor(256 / C))
+// <= 1024 tokens of one prompt (one token per thread for C <= 256). A block stages its importance values plus a halo of
 // (W-1)/2 on each side (clamped to the prompt) in LDS and pools them there.
 // k_pool_stats: each block's min and max of the pooled values (only when
 //   normalising: the scale needs the prompt's min and max).
@@ -28,6 +28,11 @@ namespace {
 constexpr int kPoolThreads = 256;
 constexpr int kMaxHalo = (kMaxPoolWindow - 1) / 2;
 constexpr int kMaxTB = 1024;
+constexpr int kTargetTB = 256;
+// Prompts with more blocks than this get their min and max reduced once
+// (k_pool_minmax) instead of by every block of k_pool_finish.
+constexpr int kFinishReduceMax = 2048;
+constexpr int kDefaultRadius = 6;   // W = 13, the pages' window
 
 struct BlockSpan {
   int b;           // prompt
@@ -51,6 +56,26 @@ __device__ __forceinline__ BlockSpan block_span(const PoolTable &pt, int blk, in
   return s;
 }
 
+// Mean of buf over the window of token t clipped to the prompt, summed in
+// token order. R >= 0: the radius at compile time (the loads issue together);
+// R < 0: radius r at run time.
+template <int R>
+__device__ __forceinline__ float window_mean(const float *buf, int lo, int N, int t, int r) {
+  const int a = max(0, t - r), e = min(N - 1, t + r);
+  float sum = 0.f;
+  if constexpr (R >= 0) {
+#pragma unroll
+    for (int k = -R; k <= R; ++k) {
+      const int i = t + k;
+      const float v = buf[min(max(i, a), e) - lo];   // always inside the staged span
+      sum += (i >= a && i <= e) ? v : 0.f;
+    }
+  } else {
+    for (int i = a; i <= e; ++i) sum += buf[i - lo];
+  }
+  return sum / (float)(e - a + 1);
+}
+
 // Pooled values of the block's tokens into out[0 .. t1 - t0) (LDS), from the
 // halo-extended importance staged in buf.
 __device__ __forceinline__ void pool_block(const PoolParams &p, const BlockSpan &s,
@@ -59,11 +84,12 @@ __device__ __forceinline__ void pool_block(const PoolParams &p, const BlockSpan 
   const int lo = max(0, s.t0 - r), hi = min(s.N, s.t1 + r);
   for (int i = threadIdx.x; i < hi - lo; i += kPoolThreads) buf[i] = imp[s.base + lo + i];
   __syncthreads();
-  for (int t = s.t0 + threadIdx.x; t < s.t1; t += kPoolThreads) {
-    const int a = max(0, t - r), e = min(s.N - 1, t + r);
-    float sum = 0.f;
-    for (int i = a; i <= e; ++i) sum += buf[i - lo];
-    out[t - s.t0] = sum / (float)(e - a + 1);
+  if (r == kDefaultRadius) {
+    for (int t = s.t0 + threadIdx.x; t < s.t1; t += kPoolThreads)
+      out[t - s.t0] = window_mean<kDefaultRadius>(buf, lo, s.N, t, r);
+  } else {
+    for (int t = s.t0 + threadIdx.x; t < s.t1; t += kPoolThreads)
+      out[t - s.t0] = window_mean<-1>(buf, lo, s.N, t, r);
   }
   __syncthreads();
 }
@@ -169,7 +195,7 @@ __global__ __launch_bounds__(kPoolThreads) void k_pool_finish(
 
 }  // namespace
 
-int pool_block_tokens(int C) { return C * (kMaxTB / C); }
+int pool_block_tokens(int C) { return C * std::max(1, kTargetTB / C); }
 
 size_t pool_ws(int B, int total_blocks) {
   return align_up((size_t)total_blocks * sizeof(float2)) + align_up((size_t)B * sizeof(float2));
@@ -188,7 +214,7 @@ hipError_t launch_pool_chunk(const PoolParams &p, const PoolTable &blocks, const
                        imp, block_mm);
     int most = 0;
     for (int b = 0; b < blocks.B; ++b) most = std::max(most, blocks.blk_off[b + 1] - blocks.blk_off[b]);
-    if (most > kPoolThreads) {
+    if (most > kFinishReduceMax) {
       hipLaunchKernelGGL(k_pool_minmax, dim3(blocks.B), dim3(kPoolThreads), 0, st, blocks,
                          block_mm, prompt_mm);
       mm_arg = prompt_mm;

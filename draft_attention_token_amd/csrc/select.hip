@@ -92,13 +92,18 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectTable t, double param
   const int c0 = t.chunk_off[b], nc = t.chunk_off[b + 1] - c0, last = nc - 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // The prompt's scores, read once: chunk tid + kThreads * e in sc[e].
+  // The prompt's scores, read once: chunk tid + kThreads * e in sc[e]; with
+  // them (one round trip) the final chunk's and the lane's own chunk's.
   float sc[kPerThread];
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     const int j = tid + kThreads * e;
     sc[e] = j < nc ? cs[c0 + j] : 0.f;
   }
+  const int i = tile * kRankTile + (lane & (kRankTile - 1));
+  const bool mine = i < last;
+  const float c_last = cs[c0 + last];
+  const float c_i = mine ? cs[c0 + i] : 0.f;
   // The prompt's scale, and for mass mode the fixed-point sum the chunks
   // ahead of a kept one must stay below: ceil(mass * total) - final.
   float mx = 0.f;
@@ -112,15 +117,13 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectTable t, double param
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) tot += to_fixed(sc[e], shift);
     tot = block_reduce(tot, redl, [](long long a, long long c) { return a + c; });
-    need = (long long)ceil(param * (double)tot) - to_fixed(cs[c0 + last], shift);
+    need = (long long)ceil(param * (double)tot) - to_fixed(c_last, shift);
   } else {
     need = t.kc[b] - 1;   // chunks ahead of a kept one
   }
 
-  const int i = tile * kRankTile + (lane & (kRankTile - 1));
   const int grp = wave * (64 / kRankTile) + (lane / kRankTile);
-  const bool mine = i < last;
-  const long long fxi = mine ? to_fixed(cs[c0 + i], shift) : 0ll;
+  const long long fxi = mine ? to_fixed(c_i, shift) : 0ll;
   const uint32_t ki = order_key(fxi);
   uint32_t n = 0;
   long long sum = 0;
