@@ -451,3 +451,49 @@ def test_select_legacy_edge_batch(C, keep, min_tok, max_keep):
         want = oracle.thin(oracle.select_legacy_from_means(means[b], n, C, keep, min_tok), max_keep)
         np.testing.assert_array_equal(kpos[koff[b]:koff[b + 1]], want, err_msg=f"prompt {b} n={n}")
         np.testing.assert_array_equal(kid[koff[b]:koff[b + 1]], ids[batch.offsets[b] + want])
+
+
+# ----------------------------------------------------------------------------
+# Gather on random keep flags: batches small enough for the one-launch kernel
+# (<= 16384 chunks) and one past it (scan + write), every chunk size class.
+# ----------------------------------------------------------------------------
+
+GATHER_CASES = [
+    # (lengths, C, p_keep, chunk 0 of every prompt dropped)
+    ((1,), 32, 0.5, False),
+    ((5000,), 1, 0.5, True),
+    ((3, 1030, 2047, 64), 3, 0.4, True),
+    ((131072,), 32, 0.8, True),
+    ((70000, 1500, 33), 1000, 0.5, True),
+    ((100, 4096, 999, 2049) * 8, 32, 0.3, False),
+    ((300000, 250000), 32, 0.6, True),          # 17188 chunks: the two-kernel form
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("lengths,C,p_keep,drop0", GATHER_CASES)
+def test_gather_random_keep(lengths, C, p_keep, drop0):
+    """Kept ids, positions and offsets against the oracle's gather, prompt by prompt."""
+    rng = np.random.default_rng(len(lengths) * 1000 + C)
+    lengths = list(lengths)
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    ncs = [(n + C - 1) // C for n in lengths]
+    keep = []
+    for nc in ncs:
+        k = (rng.random(nc) < p_keep).astype(np.uint8)
+        k[-1] = 1
+        if drop0 and nc > 1:
+            k[0] = 0
+        keep.append(k)
+    keep_all = np.concatenate(keep)
+    ids = rng.integers(0, 1 << 30, size=int(off[-1]), dtype=np.int32)
+    kid, kpos, koff = sp.sp_gather_kept(torch.from_numpy(keep_all).to(DEV),
+                                        torch.from_numpy(ids).to(DEV), torch.from_numpy(off), C)
+    torch.cuda.synchronize()
+    kid, kpos, koff = kid.cpu().numpy(), kpos.cpu().numpy(), koff.cpu().numpy()
+    assert koff[0] == 0
+    for b, n in enumerate(lengths):
+        want_ids, want_pos = oracle.gather(keep[b], ids[off[b]:off[b + 1]], C)
+        assert koff[b + 1] - koff[b] == want_ids.size, (b, koff[b + 1] - koff[b], want_ids.size)
+        assert np.array_equal(kid[koff[b]:koff[b + 1]], want_ids), b
+        assert np.array_equal(kpos[koff[b]:koff[b + 1]], want_pos), b
