@@ -23,10 +23,14 @@ template <typename T, int D> struct Frag;
 template <int D> struct Frag<__bf16, D> {
   static constexpr int kSteps = D / 16;
   u32x4 v[kSteps];
+  // Ordinary cached loads: one instruction reads 32 bytes of each of 32 key
+  // rows, so four consecutive instructions share every 128-byte line; a
+  // non-temporal hint lets the line go between them and costs a refetch each
+  // time (K at ~3.3 instead of ~6 TB/s).
   __device__ __forceinline__ void load(const __bf16 *row, int half) {
     const u32x4 *p = reinterpret_cast<const u32x4 *>(row) + half;
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) v[s] = __builtin_nontemporal_load(p + 2 * s);
+    for (int s = 0; s < kSteps; ++s) v[s] = p[2 * s];
   }
   __device__ __forceinline__ void load_cached(const __bf16 *row, int half) {
     const u32x4 *p = reinterpret_cast<const u32x4 *>(row) + half;
