@@ -497,3 +497,44 @@ def test_gather_random_keep(lengths, C, p_keep, drop0):
         assert koff[b + 1] - koff[b] == want_ids.size, (b, koff[b + 1] - koff[b], want_ids.size)
         assert np.array_equal(kid[koff[b]:koff[b + 1]], want_ids), b
         assert np.array_equal(kpos[koff[b]:koff[b + 1]], want_pos), b
+
+
+# ----------------------------------------------------------------------------
+# Pooling on random importance: block shapes (one token per thread up to
+# C = 256, one chunk per block beyond), the compile-time 13-token window and
+# the run-time one, prompt edges, with and without normalisation.
+# ----------------------------------------------------------------------------
+
+POOL_CASES = [
+    # (lengths, W, C, normalize)
+    ((5000, 7, 300), 13, 32, True),
+    ((5000, 7, 300), 13, 32, False),
+    ((4099,), 5, 7, True),
+    ((3000, 257), 33, 256, True),
+    ((3000, 600), 13, 257, True),
+    ((2500,), 129, 1000, True),
+    ((12, 13, 14), 13, 1, True),
+    ((70000,), 1, 300, False),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("lengths,W,C,normalize", POOL_CASES)
+def test_pool_chunk_random(lengths, W, C, normalize):
+    """Token and chunk scores against the oracle's pooling, prompt by prompt."""
+    rng = np.random.default_rng(W * 1000 + C)
+    lengths = list(lengths)
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    imp = (rng.random(int(off[-1])) ** 4).astype(np.float32)
+    ts, cs = sp.sp_pool_chunk(torch.from_numpy(imp).to(DEV), torch.from_numpy(off), W=W, C=C,
+                              normalize=normalize)
+    torch.cuda.synchronize()
+    ts, cs = ts.cpu().numpy(), cs.cpu().numpy()
+    c0 = 0
+    for b, n in enumerate(lengths):
+        nc = (n + C - 1) // C
+        want_ts, want_cs = oracle.pool_chunk(imp[off[b]:off[b + 1]].astype(np.float64), W=W, C=C,
+                                             normalize=normalize)
+        assert_scores_close(ts[off[b]:off[b + 1]], want_ts, f"token scores {b}")
+        assert_scores_close(cs[c0:c0 + nc], want_cs, f"chunk scores {b}")
+        c0 += nc
