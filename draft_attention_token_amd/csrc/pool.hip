@@ -9,8 +9,9 @@
 // Selection (a chunk's score is the mean over the tokens it holds).
 //
 // Work is split into blocks of whole chunks, TB = C * max(1, floor(256 / C))
-// <= 1024 tokens of one prompt (one token per thread for C <= 256). A block stages its importance values plus a halo of
-// (W-1)/2 on each side (clamped to the prompt) in LDS and pools them there.
+// <= 1024 tokens of one prompt (one token per thread for C <= 256). A block
+// stages its importance values plus a halo of (W-1)/2 on each side (clamped
+// to the prompt) in LDS and pools them there.
 // k_pool_stats: each block's min and max of the pooled values (only when
 //   normalising: the scale needs the prompt's min and max).
 // k_pool_minmax: per prompt, when a prompt has too many blocks for every
@@ -32,7 +33,7 @@ constexpr int kTargetTB = 256;
 // Prompts with more blocks than this get their min and max reduced once
 // (k_pool_minmax) instead of by every block of k_pool_finish.
 constexpr int kFinishReduceMax = 2048;
-constexpr int kDefaultRadius = 6;   // W = 13, the pages' window
+constexpr int kDefaultRadius = 6;   // W = 13, the width of Approach step 3 (above)
 
 struct BlockSpan {
   int b;           // prompt

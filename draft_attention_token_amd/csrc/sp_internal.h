@@ -21,7 +21,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kPoolHalo = 16;
 constexpr int kPoolSpan = 64;                     // kTile + 2 * kPoolHalo
 constexpr int kMaxRowPool = 2 * kPoolHalo + 1;
-constexpr int kDefaultPoolRadius = 6;             // W = 13, the pages' width
+constexpr int kDefaultPoolRadius = 6;   // W = 13 ("Speculative prefill", Approach step 3)
 
 // Per-prompt prefix table passed to kernels by value (about 1 KB). unit_off
 // holds a host-computed prefix of per-prompt unit counts (tiles, chunks or
