@@ -26,6 +26,10 @@ using namespace sp;
 
 namespace {
 
+// Largest batch (keys: prompt tokens plus lookahead) that AUTO scores with the
+// two-pass kernels.
+constexpr int64_t kAutoTwoPassKeys = 14336;
+
 constexpr int64_t kMaxTotalTokens = (int64_t)1 << 30;   // keeps int32 token offsets safe
 
 // Checks a batch; on success fills N (per prompt) and the token total.
@@ -212,7 +216,14 @@ sp_status sp_score_attention(const sp_attn_desc *desc, const sp_batch *batch, co
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if ((desc->algo == SP_SCORE_STREAM || f8) && !score_stream_supported(s))
     return SP_ERR_UNSUPPORTED;
-  if (desc->algo != SP_SCORE_TWO_PASS) {
+  // AUTO: the two-pass kernels for short batches. There the single pass is
+  // bound by its per-problem hand-offs, while the two passes run every
+  // (tile, problem) pair at once (MI355X, 6 layers x 4 KV groups: 39 against
+  // 65 us at 3212 tokens, even near 16K tokens, single pass ahead beyond).
+  const int64_t total_keys = (int64_t)tiles.tok_off[tiles.B] + (int64_t)tiles.B * s.La;
+  const bool short_batch = total_keys <= kAutoTwoPassKeys;
+  if (desc->algo == SP_SCORE_STREAM || f8 ||
+      (desc->algo == SP_SCORE_AUTO && !short_batch)) {
     bool supported = false;
     const hipError_t e = launch_score_stream(s, tiles, q, k, ks, importance, ws, hs, &supported);
     if (supported) return launched(e);

@@ -143,23 +143,29 @@ __global__ __launch_bounds__(kLseParts * kRows) void k_lse(SegTable tiles, int n
   }
 }
 
-// Pass 2: per tile, loop over all layers and groups; p = 2^(x - lse2); the
-// step-max over (layer, head) lives in LDS as ordered uint (p >= 0, so the
-// float bits order like the values); then the mean over steps.
+// Pass 2: per tile, all layers and groups, dealt to the block's waves; p =
+// 2^(x - lse2); the step-max over (layer, head) lives in LDS as ordered uint
+// (p >= 0, so the float bits order like the values); then the mean over
+// steps. Several waves per tile keep short prompts (few tiles) from running
+// every problem of a tile one after another.
+constexpr int kScoreWaves = 4;
 template <typename T, int D>
-__global__ __launch_bounds__(64) void k_score(AttnShape s, SegTable tiles, int64_t total_keys,
-                                              const T *__restrict__ q, const T *__restrict__ k,
-                                              const float *__restrict__ lse,
-                                              float *__restrict__ imp) {
+__global__ __launch_bounds__(64 * kScoreWaves) void k_score(AttnShape s, SegTable tiles,
+                                                            int64_t total_keys,
+                                                            const T *__restrict__ q,
+                                                            const T *__restrict__ k,
+                                                            const float *__restrict__ lse,
+                                                            float *__restrict__ imp) {
   __shared__ unsigned smax[kRows][kTile];
   const int t = blockIdx.x;
-  const int lane = threadIdx.x, half = lane >> 5, col = lane & 31;
-  for (int i = lane; i < kRows * kTile; i += 64) (&smax[0][0])[i] = 0u;
+  const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  for (int i = threadIdx.x; i < kRows * kTile; i += 64 * kScoreWaves) (&smax[0][0])[i] = 0u;
   __syncthreads();
   const TileCtx c = tile_ctx(tiles, t, col);
   const int n_prob = s.n_layers * s.Hkv, rows = s.L * s.G;
   const bool prompt_key = c.kl < c.N;
-  for (int prob = 0; prob < n_prob; ++prob) {
+  for (int prob = wave; prob < n_prob; prob += kScoreWaves) {
     const int l = prob / s.Hkv, g = prob - l * s.Hkv;
     const f32x16 acc = tile_logits<T, D>(s, c, total_keys, q, k, l, g, lane);
     const float *lrow = lse + ((int64_t)c.b * n_prob + prob) * kRows;
@@ -173,7 +179,7 @@ __global__ __launch_bounds__(64) void k_score(AttnShape s, SegTable tiles, int64
     }
   }
   __syncthreads();
-  if (lane < 32 && prompt_key) {
+  if (threadIdx.x < 32 && prompt_key) {
     float acc = 0.f;
     for (int j = 0; j < s.L; ++j) acc += __uint_as_float(smax[j][col]);
     imp[tiles.tok_off[c.b] + c.kl] = acc / (float)s.L;
@@ -299,7 +305,7 @@ hipError_t run(const AttnShape &s, const SegTable &tiles, int total_tiles, const
     hipLaunchKernelGGL((k_score_pooled<T, D>), dim3((total_tiles + 7) / 8 * 8), dim3(64), 0, st, s,
                        tiles, total_keys, total_tiles, (const T *)q, (const T *)k, lse, imp);
   else
-    hipLaunchKernelGGL((k_score<T, D>), dim3(total_tiles), dim3(64), 0, st, s, tiles, total_keys,
+    hipLaunchKernelGGL((k_score<T, D>), dim3(total_tiles), dim3(64 * kScoreWaves), 0, st, s, tiles, total_keys,
                        (const T *)q, (const T *)k, lse, imp);
   return hipGetLastError();
 }

@@ -77,7 +77,10 @@ typedef enum { SP_DTYPE_F32 = 0, SP_DTYPE_BF16 = 1, SP_DTYPE_BF16_FP8K = 2 } sp_
 
 typedef enum { SP_SELECT_TOP_P = 0, SP_SELECT_MASS = 1 } sp_select_mode;
 
-/* Scoring kernel choice: AUTO picks the fastest one that supports the shape. */
+/* Scoring kernel choice: AUTO picks the fastest one that supports the shape:
+ * the two-pass kernels for batches of at most 14336 keys (prompt tokens plus
+ * lookahead) and wherever the single pass does not apply, else the single
+ * pass. */
 typedef enum {
   SP_SCORE_AUTO = 0,
   SP_SCORE_TWO_PASS = 1,   /* stats pass, then a recompute pass: K read twice */
