@@ -198,15 +198,16 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(AttnShape s, SegTabl
 // large probability).
 // Blocks take tiles die by die (block i runs on die i % 8 and gets the i / 8-th
 // tile of that die's contiguous share), so neighbouring tiles, which read each
-// other's halo keys, meet in the same L2.
-template <typename T, int D>
-__global__ __launch_bounds__(64) void k_score_pooled(AttnShape s, SegTable tiles,
-                                                     int64_t total_keys, int total_tiles,
-                                                     const T *__restrict__ q,
-                                                     const T *__restrict__ k,
-                                                     const float *__restrict__ lse,
-                                                     float *__restrict__ imp) {
-  __shared__ float pv[kPoolSpan][kRows + 1];   // [key - (k0 - kPoolHalo)][row], padded
+// other's halo keys, meet in the same L2. The tile's problems are dealt to
+// the block's kW waves, each with its own probability buffer: four for
+// short batches (few tiles, whose problems would otherwise run one after
+// another), one for long ones (more blocks per CU in flight instead).
+constexpr int kPooledManyTiles = 2048;   // batches this long take one wave per tile
+template <typename T, int D, int kW>
+__global__ __launch_bounds__(64 * kW) void k_score_pooled(
+    AttnShape s, SegTable tiles, int64_t total_keys, int total_tiles, const T *__restrict__ q,
+    const T *__restrict__ k, const float *__restrict__ lse, float *__restrict__ imp) {
+  __shared__ float pvs[kW][kPoolSpan][kRows + 1];   // [key - (k0 - kPoolHalo)][row]
   __shared__ unsigned smax[kRows][kTile];
   const int per = (total_tiles + 7) / 8;
   const int t = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
@@ -216,17 +217,24 @@ __global__ __launch_bounds__(64) void k_score_pooled(AttnShape s, SegTable tiles
   const int k0 = (t - tiles.unit_off[b]) * kTile;   // first output key (prompt-local)
   if (k0 >= N) return;                               // a tile of lookahead keys only
   const int64_t key0 = tiles.tok_off[b] + (int64_t)b * tiles.L;
-  const int lane = threadIdx.x, half = lane >> 5, col = lane & 31;
-  for (int i = lane; i < kRows * kTile; i += 64) (&smax[0][0])[i] = 0u;
+  const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  float(*pv)[kRows + 1] = pvs[wave];
+  for (int i = threadIdx.x; i < kRows * kTile; i += 64 * kW) (&smax[0][0])[i] = 0u;
   const int n_prob = s.n_layers * s.Hkv, rows = s.L * s.G;
   const int r = (s.row_pool - 1) / 2;
   // The lane's 16 output keys for row `col` in the pooling step.
   const int c0 = 16 * half;
-  for (int prob = 0; prob < n_prob; ++prob) {
-    const int l = prob / s.Hkv, g = prob - l * s.Hkv;
+  // Every wave runs the same number of rounds (the block barriers below);
+  // a wave without a problem in a round only takes part in them.
+  const int rounds = (n_prob + kW - 1) / kW;
+  for (int round = 0; round < rounds; ++round) {
+    const int prob = round * kW + wave;
+    const bool active = prob < n_prob;
+    const int l = active ? prob / s.Hkv : 0, g = active ? prob - l * s.Hkv : 0;
     Frag<T, D> a;
     if (col < rows) a.load_cached(q_row_ptr(q, s, b, l, g, col), half); else a.zero();
-    const float *lrow = lse + ((int64_t)b * n_prob + prob) * kRows;
+    const float *lrow = lse + ((int64_t)b * n_prob + (active ? prob : 0)) * kRows;
     float lr[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -236,7 +244,7 @@ __global__ __launch_bounds__(64) void k_score_pooled(AttnShape s, SegTable tiles
 #pragma unroll
     for (int u = 0; u < kPoolSpan / kTile; ++u) {
       const int kl = k0 - kPoolHalo + kTile * u + col;   // this lane's key column
-      const bool need = kl >= 0 && kl < N && kl >= k0 - r && kl < k0 + kTile + r;
+      const bool need = active && kl >= 0 && kl < N && kl >= k0 - r && kl < k0 + kTile + r;
       Frag<T, D> bk;
       if (need) bk.load(k_row_ptr(k, s, total_keys, l, key0 + kl, g), half); else bk.zero();
       const f32x16 acc = mfma_tile<D>(a, bk);
@@ -247,7 +255,7 @@ __global__ __launch_bounds__(64) void k_score_pooled(AttnShape s, SegTable tiles
       }
     }
     __syncthreads();
-    if (col < rows) {
+    if (active && col < rows) {
       // The row's probabilities of keys k0 + c0 - 16 .. k0 + c0 + 31 (pv rows
       // c0 .. c0 + 47), all read up front; each window sum then adds its
       // terms in key order, zeros outside the window.
@@ -281,7 +289,7 @@ __global__ __launch_bounds__(64) void k_score_pooled(AttnShape s, SegTable tiles
     }
     __syncthreads();
   }
-  if (lane < kTile && k0 + lane < N) {
+  if (threadIdx.x < kTile && k0 + lane < N) {
     float acc = 0.f;
     for (int j = 0; j < s.L; ++j) acc += __uint_as_float(smax[j][lane]);
     imp[tiles.tok_off[b] + k0 + lane] = acc / (float)s.L;
@@ -301,12 +309,18 @@ hipError_t run(const AttnShape &s, const SegTable &tiles, int total_tiles, const
                      (const T *)q, (const T *)k, part);
   hipLaunchKernelGGL(k_lse, dim3(tiles.B, n_prob), dim3(kLseParts * kRows), 0, st, tiles, n_prob,
                      total_tiles, part, lse, hdr, reserve_tags(1));
-  if (s.row_pool > 1)
-    hipLaunchKernelGGL((k_score_pooled<T, D>), dim3((total_tiles + 7) / 8 * 8), dim3(64), 0, st, s,
-                       tiles, total_keys, total_tiles, (const T *)q, (const T *)k, lse, imp);
-  else
-    hipLaunchKernelGGL((k_score<T, D>), dim3(total_tiles), dim3(64 * kScoreWaves), 0, st, s, tiles, total_keys,
-                       (const T *)q, (const T *)k, lse, imp);
+  if (s.row_pool > 1) {
+    const dim3 grid((total_tiles + 7) / 8 * 8);
+    if (total_tiles < kPooledManyTiles)
+      hipLaunchKernelGGL((k_score_pooled<T, D, 4>), grid, dim3(64 * 4), 0, st, s, tiles, total_keys,
+                         total_tiles, (const T *)q, (const T *)k, lse, imp);
+    else
+      hipLaunchKernelGGL((k_score_pooled<T, D, 1>), grid, dim3(64), 0, st, s, tiles, total_keys,
+                         total_tiles, (const T *)q, (const T *)k, lse, imp);
+  } else {
+    hipLaunchKernelGGL((k_score<T, D>), dim3(total_tiles), dim3(64 * kScoreWaves), 0, st, s, tiles,
+                       total_keys, (const T *)q, (const T *)k, lse, imp);
+  }
   return hipGetLastError();
 }
 
