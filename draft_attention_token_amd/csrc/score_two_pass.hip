@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kLseParts * kRows) void k_lse(SegTable tiles, int n
 // (p >= 0, so the float bits order like the values); then the mean over
 // steps. Several waves per tile keep short prompts (few tiles) from running
 // every problem of a tile one after another.
-constexpr int kScoreWaves = 4;
+constexpr int kScoreWaves = 8;
 template <typename T, int D>
 __global__ __launch_bounds__(64 * kScoreWaves) void k_score(AttnShape s, SegTable tiles,
                                                             int64_t total_keys,
