@@ -108,6 +108,11 @@ SMALL = [
     ("poolmax_bf16_ragged", "n3212_poolmax_bf16", dict(lengths=(65, 1, 640, 129, 7, 13))),
     ("poolmax_fp32_d64_w33", "n800_fp32", dict(lengths=(333, 40), pool_before_max=True,
                                                 pool_window=33)),
+    # Fewer problems than waves per tile (idle waves in a round).
+    ("poolmax_bf16_one_problem", "n3212_poolmax_bf16", dict(lengths=(700, 33), n_layers=1,
+                                                            n_q_heads=4, n_kv_heads=1)),
+    ("poolmax_bf16_three_problems", "n3212_poolmax_bf16", dict(lengths=(300,), n_layers=3,
+                                                               n_q_heads=4, n_kv_heads=1)),
     ("poolmax_bf16_d64_g8_w3_prerow", "n3212_bf16", dict(lengths=(500, 31), head_dim=64,
                                                          n_q_heads=16, n_kv_heads=2, n_lookahead=3,
                                                          prefill_row=True, pool_before_max=True,
