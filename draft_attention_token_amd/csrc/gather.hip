@@ -24,19 +24,22 @@ constexpr int kScanThreads = 1024;
 constexpr int kWriteThreads = 1024;
 constexpr int kFusedPerThread = 16;
 constexpr int kFusedMaxChunks = kWriteThreads * kFusedPerThread;
+static_assert(SP_MAX_PROMPTS <= kWriteThreads, "one thread per earlier prompt");
 
-// Block-wide sums of two ints (all threads get them).
-__device__ __forceinline__ int2 block_sum2(int a, int b, int2 *red) {
+// Block-wide sums of three ints (all threads get them).
+__device__ __forceinline__ int3 block_sum3(int a, int b, int c, int3 *red) {
   for (int off = 32; off > 0; off >>= 1) {
     a += __shfl_xor(a, off, 64);
     b += __shfl_xor(b, off, 64);
+    c += __shfl_xor(c, off, 64);
   }
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_int2(a, b);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_int3(a, b, c);
   __syncthreads();
-  int2 v = make_int2(0, 0);
+  int3 v = make_int3(0, 0, 0);
   for (int w = 0; w < kWriteThreads / 64; ++w) {
     v.x += red[w].x;
     v.y += red[w].y;
+    v.z += red[w].z;
   }
   __syncthreads();
   return v;
@@ -126,10 +129,9 @@ __global__ __launch_bounds__(kWriteThreads) void k_gather_fused(
     SegTable chunks, SegTable blocks, int C, const uint8_t *__restrict__ keep,
     const int32_t *__restrict__ ids, int32_t *__restrict__ kept_ids,
     int32_t *__restrict__ kept_pos, int64_t *__restrict__ kept_offsets) {
-  __shared__ int2 red[kWriteThreads / 64];
+  __shared__ int3 red[kWriteThreads / 64];
   __shared__ int wave_tot[kWriteThreads / 64];
   __shared__ int pre[kWriteThreads];
-  __shared__ int64_t corr_s;
   const int blk = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = seg_of(blocks, blk);
   const int c0 = chunks.unit_off[b];
@@ -158,21 +160,18 @@ __global__ __launch_bounds__(kWriteThreads) void k_gather_fused(
     before += (k && g < c0) ? 1 : 0;
     inside += (k && g >= c0) ? 1 : 0;
   }
-  if (tid == 0) {
-    // Earlier prompts: a kept final chunk holds its real size; a dropped
-    // chunk 0 still emits BOS.
-    int64_t corr = 0;
-    for (int bp = 0; bp < b; ++bp) {
-      const int cs = chunks.unit_off[bp], ce = chunks.unit_off[bp + 1];
-      const int np = chunks.tok_off[bp + 1] - chunks.tok_off[bp];
-      if (keep[ce - 1]) corr -= C - (np - (ce - cs - 1) * C);
-      if (!keep[cs]) corr += 1;
-    }
-    corr_s = corr;
+  // Earlier prompts, one per thread (b <= SP_MAX_PROMPTS < kWriteThreads): a
+  // kept final chunk holds its real size; a dropped chunk 0 still emits BOS.
+  int corr = 0;
+  if (tid < b) {
+    const int cs = chunks.unit_off[tid], ce = chunks.unit_off[tid + 1];
+    const int np = chunks.tok_off[tid + 1] - chunks.tok_off[tid];
+    if (keep[ce - 1]) corr -= C - (np - (ce - cs - 1) * C);
+    if (!keep[cs]) corr += 1;
   }
-  const int2 tot = block_sum2(before, inside, red);
+  const int3 tot = block_sum3(before, inside, corr, red);
   const bool k0 = keep[c0] != 0;
-  const int64_t base_prompt = (int64_t)C * tot.x + corr_s;
+  const int64_t base_prompt = (int64_t)C * tot.x + tot.z;
   const int64_t base_blk = base_prompt + (k0 ? 0 : 1) + (int64_t)C * tot.y;
   // Exclusive scan of the kept sizes of the block's chunks.
   const int sz = kc ? min(C, N - c * C) : 0;
