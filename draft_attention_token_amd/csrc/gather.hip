@@ -89,18 +89,9 @@ __global__ __launch_bounds__(kWriteThreads) void k_gather_write(
   __shared__ int64_t base_s;
   const int blk = blockIdx.x, tid = threadIdx.x;
   const int b = seg_of(blocks, blk);
-  if (tid == 0) {
-    int64_t acc = 0;
-    for (int i = 0; i < b; ++i) acc += counts[i];
-    base_s = acc;
-    if (blk == 0) {
-      int64_t o = 0;
-      kept_offsets[0] = 0;
-      for (int i = 0; i < blocks.B; ++i) {
-        o += counts[i];
-        kept_offsets[i + 1] = o;
-      }
-    }
+  if (tid < 64) {
+    const int64_t o = wave_prompt_offsets(counts, blocks.B, b, blk == 0 ? kept_offsets : nullptr);
+    if (tid == 0) base_s = o;
   }
   __syncthreads();
   const int64_t base = base_s;

@@ -46,6 +46,33 @@ __device__ __forceinline__ int seg_of(const SegTable &t, int32_t u) {
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Output offsets of a batch's prompts from their kept counts, on one wave
+// (lane l takes prompts 2 l and 2 l + 1; B <= SP_MAX_PROMPTS = 128): returns
+// the offset of prompt b to every lane, and when `offsets` is not null
+// writes offsets[0 .. B] (offsets[B] = the total). Counts sum below 2^31.
+__device__ __forceinline__ int64_t wave_prompt_offsets(const int32_t *counts, int B, int b,
+                                                       int64_t *offsets) {
+  const int lane = threadIdx.x & 63, i0 = 2 * lane, i1 = i0 + 1;
+  const int c0 = i0 < B ? counts[i0] : 0, c1 = i1 < B ? counts[i1] : 0;
+  const int pair = c0 + c1;
+  int incl = pair;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  const int e0 = incl - pair, e1 = e0 + c0;   // offsets of prompts i0 and i1
+  if (offsets) {
+    if (i0 <= B) offsets[i0] = e0;
+    if (i1 <= B) offsets[i1] = e1;
+    if (lane == 63) offsets[B] = incl;   // the total (B = 128 has no lane of its own)
+  }
+  const int mine = i0 == b ? e0 : (i1 == b ? e1 : 0);
+  int v = (i0 == b || i1 == b) ? mine : 0;
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+static_assert(SP_MAX_PROMPTS <= 128, "two prompts per lane of one wave");
+
 struct AttnShape {
   int n_layers, Hq, Hkv, d;
   int L;                            // query steps per (layer, head): La + pre

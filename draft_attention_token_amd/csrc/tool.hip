@@ -170,13 +170,14 @@ __global__ __launch_bounds__(kListThreads) void k_legacy_write(
   const int b = table_prompt(t.wblk_off, t.B, blockIdx.x);
   const int n = t.tok_off[b + 1] - t.tok_off[b], C = t.C, c0 = t.chunk_off[b];
   const int x = (blockIdx.x - t.wblk_off[b]) * kListThreads + threadIdx.x;
-  if (threadIdx.x == 0) {
-    int64_t s = 0;
-    for (int p = 0; p < b; ++p) s += counts[p];
-    s_off = s;
-    if (blockIdx.x == t.wblk_off[b]) {
-      kept_offsets[b] = s;
-      if (b == t.B - 1) kept_offsets[t.B] = s + counts[b];
+  if (threadIdx.x < 64) {
+    const int64_t s = wave_prompt_offsets(counts, t.B, b, nullptr);
+    if (threadIdx.x == 0) {
+      s_off = s;
+      if (blockIdx.x == t.wblk_off[b]) {
+        kept_offsets[b] = s;
+        if (b == t.B - 1) kept_offsets[t.B] = s + counts[b];
+      }
     }
   }
   __syncthreads();

@@ -487,6 +487,7 @@ GATHER_CASES = [
     ((100, 4096, 999, 2049) * 8, 32, 0.3, False),
     ((33, 64, 97, 1, 500) * 25 + (40, 41, 2), 32, 0.5, True),   # 128 prompts
     ((300000, 250000), 32, 0.6, True),          # 17188 chunks: the two-kernel form
+    ((4160,) * 127 + (77,), 32, 0.5, True),    # 128 prompts, 16513 chunks: two kernels
 ]
 
 
