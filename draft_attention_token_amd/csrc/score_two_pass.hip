@@ -208,7 +208,7 @@ __global__ __launch_bounds__(64 * kW) void k_score_pooled(
     AttnShape s, SegTable tiles, int64_t total_keys, int total_tiles, const T *__restrict__ q,
     const T *__restrict__ k, const float *__restrict__ lse, float *__restrict__ imp) {
   __shared__ float pvs[kW][kPoolSpan][kRows + 1];   // [key - (k0 - kPoolHalo)][row]
-  __shared__ unsigned smax[kRows][kTile];
+  __shared__ unsigned smax[kRows][kTile + 1];   // padded: rows fall in different banks
   const int per = (total_tiles + 7) / 8;
   const int t = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   if (t >= total_tiles) return;
@@ -225,6 +225,13 @@ __global__ __launch_bounds__(64 * kW) void k_score_pooled(
   const int r = (s.row_pool - 1) / 2;
   // The lane's 16 output keys for row `col` in the pooling step.
   const int c0 = 16 * half;
+  // With 2^k heads per group, the max over a step's heads is taken across its
+  // G lanes and kept in registers (per lane: its step, its 16 keys) until the
+  // end; other group sizes take it in LDS with atomics.
+  const bool pow2 = (s.G & (s.G - 1)) == 0;
+  float run[kTile / 2];
+#pragma unroll
+  for (int c = 0; c < kTile / 2; ++c) run[c] = 0.f;
   // Every wave runs the same number of rounds (the block barriers below);
   // a wave without a problem in a round only takes part in them.
   const int rounds = (n_prob + kW - 1) / kW;
@@ -255,6 +262,9 @@ __global__ __launch_bounds__(64 * kW) void k_score_pooled(
       }
     }
     __syncthreads();
+    float pc[kTile / 2];   // pooled probabilities of the lane's row and 16 keys
+#pragma unroll
+    for (int c = 0; c < kTile / 2; ++c) pc[c] = 0.f;
     if (active && col < rows) {
       // The row's probabilities of keys k0 + c0 - 16 .. k0 + c0 + 31 (pv rows
       // c0 .. c0 + 47), all read up front; each window sum then adds its
@@ -265,7 +275,7 @@ __global__ __launch_bounds__(64 * kW) void k_score_pooled(
       auto emit = [&](int c, float w) {
         const int kk = k0 + c0 + c;
         const int lo = max(0, kk - r), hi = min(N - 1, kk + r);
-        if (kk < N) atomicMax(&smax[col / s.G][c0 + c], __float_as_uint(w / (float)(hi - lo + 1)));
+        pc[c] = kk < N ? w / (float)(hi - lo + 1) : 0.f;
       };
       if (r == kDefaultPoolRadius) {
         // The default width: the window is known at compile time.
@@ -287,8 +297,25 @@ __global__ __launch_bounds__(64 * kW) void k_score_pooled(
         }
       }
     }
+    if (pow2) {
+      for (int m = 1; m < s.G; m <<= 1)
+#pragma unroll
+        for (int c = 0; c < kTile / 2; ++c) pc[c] = fmaxf(pc[c], __shfl_xor(pc[c], m, 64));
+#pragma unroll
+      for (int c = 0; c < kTile / 2; ++c) run[c] = fmaxf(run[c], pc[c]);
+    } else if (active && col < rows) {
+#pragma unroll
+      for (int c = 0; c < kTile / 2; ++c)
+        if (k0 + c0 + c < N) atomicMax(&smax[col / s.G][c0 + c], __float_as_uint(pc[c]));
+    }
     __syncthreads();
   }
+  if (pow2 && col < rows && col % s.G == 0) {
+    // One lane per step and half; the block's waves meet here.
+#pragma unroll
+    for (int c = 0; c < kTile / 2; ++c) atomicMax(&smax[col / s.G][c0 + c], __float_as_uint(run[c]));
+  }
+  __syncthreads();
   if (threadIdx.x < kTile && k0 + lane < N) {
     float acc = 0.f;
     for (int j = 0; j < s.L; ++j) acc += __uint_as_float(smax[j][lane]);

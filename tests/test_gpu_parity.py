@@ -113,6 +113,11 @@ SMALL = [
                                                             n_q_heads=4, n_kv_heads=1)),
     ("poolmax_bf16_three_problems", "n3212_poolmax_bf16", dict(lengths=(300,), n_layers=3,
                                                                n_q_heads=4, n_kv_heads=1)),
+    # Three heads per group: the head max through LDS atomics, not lane shuffles.
+    ("poolmax_bf16_g3", "n3212_poolmax_bf16", dict(lengths=(400, 21), n_q_heads=6, n_kv_heads=2,
+                                                   n_lookahead=4)),
+    ("bf16_g3_two_pass", "n3212_bf16", dict(lengths=(400, 21), n_q_heads=6, n_kv_heads=2,
+                                            n_lookahead=4)),
     ("poolmax_bf16_d64_g8_w3_prerow", "n3212_bf16", dict(lengths=(500, 31), head_dim=64,
                                                          n_q_heads=16, n_kv_heads=2, n_lookahead=3,
                                                          prefill_row=True, pool_before_max=True,
@@ -121,9 +126,10 @@ SMALL = [
 
 
 def stream_runs(w):
-    """Whether the single-pass kernel takes the workload's shape (bf16 Q and
-    no pooling before the max; every shape here has 2^k heads per group)."""
-    return w.dtype == torch.bfloat16 and not w.pool_before_max
+    """Whether the single-pass kernel takes the workload's shape: bf16 Q, no
+    pooling before the max, 2^k heads per group."""
+    g = w.n_q_heads // w.n_kv_heads
+    return w.dtype == torch.bfloat16 and not w.pool_before_max and g & (g - 1) == 0
 
 
 # AUTO scores batches this short with the two-pass kernels, so the single-pass
