@@ -157,6 +157,25 @@ def cpu_baseline_tool(win_inp):
             "seconds": dt, "host_threads": threads}
 
 
+# AUTO takes the two-pass kernels up to this many keys (the library's rule).
+AUTO_TWO_PASS_KEYS = 14336
+
+
+def scoring_kernels(w, algo, fp8k, n_keys):
+    """The scoring kernels a call runs, by the library's choice rule."""
+    import torch
+    g = w.n_q_heads // w.n_kv_heads
+    steps = w.n_lookahead + (1 if w.prefill_row else 0)
+    stream_ok = (w.dtype == torch.bfloat16 and not w.pool_before_max and g & (g - 1) == 0
+                 and steps * g <= 32)
+    stream = fp8k or (stream_ok and (algo == "stream" or
+                                     (algo == "auto" and n_keys > AUTO_TWO_PASS_KEYS)))
+    if stream:
+        return f"k_stream<{w.head_dim}, fp8 K={fp8k}> (sp_score_attention)"
+    last = "k_score_pooled" if w.pool_before_max else "k_score"
+    return f"k_stats + k_lse + {last} (sp_score_attention)"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,12 +282,10 @@ def main():
     log(f"plain 1 GiB streaming read: {read_gbs:.0f} GB/s ({read_shape} blocks per CU)")
 
     kept = int(pipe.kept_offsets[-1])
+    n_keys = int(inp.offsets[-1]) + (len(inp.offsets) - 1) * w.n_lookahead
+    kernel_name = scoring_kernels(w, args.algo, fp8k, n_keys)
     if tool:
-        kernel_name = "k_stream (sp_score_attention on the window batch)"
-    elif w.pool_before_max:
-        kernel_name = "k_stats + k_lse + k_score_pooled (sp_score_attention)"
-    else:
-        kernel_name = f"k_stream<{w.head_dim}, fp8 K={fp8k}> (sp_score_attention)"
+        kernel_name += " on the window batch"
     result = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
