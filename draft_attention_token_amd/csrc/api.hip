@@ -159,6 +159,23 @@ size_t score_ws_bytes(const AttnShape &s, const SegTable &tiles) {
 
 sp_status launched(hipError_t e) { return e == hipSuccess ? SP_OK : SP_ERR_DEVICE; }
 
+// The scoring kernel a call runs: the single pass for SP_SCORE_STREAM, fp8 K,
+// and AUTO on batches of more than kAutoTwoPassKeys keys, when it takes the
+// shape; else the two-pass kernels. AUTO gives short batches to the two-pass
+// kernels: there the single pass is bound by its per-problem hand-offs,
+// while the two passes run every (tile, problem) pair at once.
+sp_status choose_kernel(const sp_attn_desc *desc, const AttnShape &s, const SegTable &tiles,
+                        bool *stream) {
+  const bool f8 = s.dtype == SP_DTYPE_BF16_FP8K;
+  if ((desc->algo == SP_SCORE_STREAM || f8) && !score_stream_supported(s))
+    return SP_ERR_UNSUPPORTED;
+  const int64_t total_keys = (int64_t)tiles.tok_off[tiles.B] + (int64_t)tiles.B * s.La;
+  const bool short_batch = total_keys <= kAutoTwoPassKeys;
+  *stream = desc->algo == SP_SCORE_STREAM || f8 || (desc->algo == SP_SCORE_AUTO && !short_batch);
+  if (*stream && !score_stream_supported(s)) *stream = false;   // AUTO on another shape
+  return SP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -189,6 +206,34 @@ sp_status sp_score_workspace_bytes(const sp_attn_desc *desc, const sp_batch *bat
   return SP_OK;
 }
 
+
+sp_status sp_score_plan(const sp_attn_desc *desc, const sp_batch *batch, int32_t *kernel,
+                        int32_t *n_launches, int32_t *prompt_launch) {
+  if (!kernel || !n_launches) return SP_ERR_INVALID_ARGUMENT;
+  AttnShape s;
+  int64_t total;
+  sp_status st = check_attn(desc, &s);
+  if (st != SP_OK) return st;
+  if ((st = check_batch(batch, &total)) != SP_OK) return st;
+  const SegTable tiles = make_table(batch, s.La, kTile, s.La);
+  bool stream = false;
+  if ((st = choose_kernel(desc, s, tiles, &stream)) != SP_OK) return st;
+  if (stream) {
+    int launches = 0;
+    if (score_stream_plan(s, tiles, &launches, prompt_launch)) {
+      *kernel = SP_SCORE_STREAM;
+      *n_launches = launches;
+      return SP_OK;
+    }
+    if (desc->algo == SP_SCORE_STREAM || s.dtype == SP_DTYPE_BF16_FP8K) return SP_ERR_UNSUPPORTED;
+  }
+  *kernel = SP_SCORE_TWO_PASS;
+  *n_launches = 1;
+  if (prompt_launch)
+    for (int b = 0; b < batch->n_prompts; ++b) prompt_launch[b] = 0;
+  return SP_OK;
+}
+
 sp_status sp_score_attention(const sp_attn_desc *desc, const sp_batch *batch, const void *q,
                              const void *k, float *importance, void *ws, size_t ws_bytes,
                              void *stream) {
@@ -214,16 +259,9 @@ sp_status sp_score_attention(const sp_attn_desc *desc, const sp_batch *batch, co
   const int total_tiles = tiles.unit_off[tiles.B];
   if (!ws || ws_bytes < score_ws_bytes(s, tiles)) return SP_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  if ((desc->algo == SP_SCORE_STREAM || f8) && !score_stream_supported(s))
-    return SP_ERR_UNSUPPORTED;
-  // AUTO: the two-pass kernels for short batches. There the single pass is
-  // bound by its per-problem hand-offs, while the two passes run every
-  // (tile, problem) pair at once (MI355X, 6 layers x 4 KV groups: 39 against
-  // 65 us at 3212 tokens, even near 16K tokens, single pass ahead beyond).
-  const int64_t total_keys = (int64_t)tiles.tok_off[tiles.B] + (int64_t)tiles.B * s.La;
-  const bool short_batch = total_keys <= kAutoTwoPassKeys;
-  if (desc->algo == SP_SCORE_STREAM || f8 ||
-      (desc->algo == SP_SCORE_AUTO && !short_batch)) {
+  bool use_stream = false;
+  if ((st = choose_kernel(desc, s, tiles, &use_stream)) != SP_OK) return st;
+  if (use_stream) {
     bool supported = false;
     const hipError_t e = launch_score_stream(s, tiles, q, k, ks, importance, ws, hs, &supported);
     if (supported) return launched(e);

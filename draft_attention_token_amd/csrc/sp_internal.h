@@ -108,13 +108,17 @@ struct KScales {
 hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const void *q,
                                const void *k, const KScales &ks, float *imp, void *ws,
                                hipStream_t st, bool *supported);
+// Whether the single pass takes the batch on the current device, and if so
+// its number of launches and each prompt's launch (prompt_launch may be null).
+bool score_stream_plan(const AttnShape &s, const SegTable &tiles, int *n_launches,
+                       int32_t *prompt_launch);
 
 struct PoolParams {
   int W, C, normalize, first_n, last_n;
   float first_mult, last_mult;
 };
 // Pooling works on blocks of whole chunks of one prompt,
-// pool_block_tokens(C) = C * floor(1024 / C) tokens each.
+// pool_block_tokens(C) = C * max(1, floor(256 / C)) tokens each.
 struct PoolTable {
   int32_t B;
   int32_t blk_off[SP_MAX_PROMPTS + 1];     // block prefix per prompt

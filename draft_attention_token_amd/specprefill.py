@@ -19,7 +19,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
-from typing import Optional, Sequence
+from typing import NamedTuple, Optional, Sequence
 
 import numpy as np
 import torch
@@ -38,6 +38,7 @@ EXPORTED = [
     "sp_select_workspace_bytes", "sp_gather_workspace_bytes", "sp_score_attention",
     "sp_pool_chunk", "sp_select_chunks", "sp_gather_kept", "sp_score_status", "sp_break_even",
     "sp_window_plan", "sp_stitch_windows", "sp_select_legacy_workspace_bytes", "sp_select_legacy",
+    "sp_score_plan",
 ]
 
 _ALGOS = {"auto": SP_SCORE_AUTO, "two_pass": SP_SCORE_TWO_PASS, "stream": SP_SCORE_STREAM}
@@ -96,6 +97,8 @@ def lib():
                                        vp, vp, sz, vp]
         L.sp_gather_kept.argtypes = [bp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sp_score_status.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
+        L.sp_score_plan.argtypes = [ctypes.POINTER(sp_attn_desc), bp, ctypes.POINTER(ctypes.c_int32),
+                                    ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
         L.sp_break_even.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
                                     ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_int32)]
         i32p, i64p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
@@ -311,6 +314,23 @@ def select_legacy(batch: Batch, C: int, keep_pct: float, min_tokens: int, max_ke
                                   _ptr(kept_pos), _ptr(kept_off), _ptr(ws), ws.numel(),
                                   _stream(dev)), "sp_select_legacy")
     return kept_ids, kept_pos, kept_off
+
+
+class ScorePlan(NamedTuple):
+    kernel: str              # "stream" (single pass) or "two_pass"
+    n_launches: int
+    prompt_launch: list      # launch index of each prompt
+
+
+def score_plan(desc: sp_attn_desc, batch: Batch) -> ScorePlan:
+    """What sp_score_attention runs for this descriptor and batch on the
+    current device (sp_score_plan)."""
+    kernel, n = ctypes.c_int32(), ctypes.c_int32()
+    per = (ctypes.c_int32 * batch.B)()
+    _check(lib().sp_score_plan(ctypes.byref(desc), batch.ref(), ctypes.byref(kernel),
+                               ctypes.byref(n), per), "sp_score_plan")
+    name = {SP_SCORE_STREAM: "stream", SP_SCORE_TWO_PASS: "two_pass"}[kernel.value]
+    return ScorePlan(name, n.value, list(per))
 
 
 def score_status(ws: torch.Tensor) -> int:

@@ -185,6 +185,19 @@ sp_status sp_score_attention(const sp_attn_desc *desc, const sp_batch *batch, co
                              const void *k, float *importance, void *ws, size_t ws_bytes,
                              void *stream);
 
+/* What sp_score_attention would run for this descriptor and batch on the
+ * current device, without running it: *kernel = SP_SCORE_STREAM (the
+ * single pass) or SP_SCORE_TWO_PASS, by the same rule the call applies;
+ * *n_launches = the single pass's kernel launches (a batch is split where
+ * its prompts need more streaming blocks than the device has compute
+ * units), 1 for the two-pass kernels; prompt_launch (HOST, [n_prompts], or
+ * NULL) receives each prompt's launch. Returns the status the call would
+ * return for these arguments (SP_ERR_UNSUPPORTED where the single pass is
+ * demanded and does not take the shape). Host arithmetic and device
+ * attribute queries only; nothing is enqueued. */
+sp_status sp_score_plan(const sp_attn_desc *desc, const sp_batch *batch, int32_t *kernel,
+                        int32_t *n_launches, int32_t *prompt_launch);
+
 /* Whether the latest sp_score_attention call on this workspace completed:
  * *status_host = 0 if so (or if there was none), 1 if a wait timed out and
  * the importance it wrote is not valid. Synchronises `stream`. */
