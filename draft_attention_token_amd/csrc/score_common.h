@@ -10,6 +10,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x16 __attribute__((ext_vector_type(16)));
 
 // One lane's share of a 32 x d operand for the 32x32 MFMA contraction over d.
 //  bf16 (v_mfma_f32_32x32x16_bf16): d/16 k-steps; at step s the lane in half h

@@ -14,8 +14,8 @@
 // than read K twice, each block keeps the exponentiated logits of its keys on
 // chip until the row lse arrives from the other blocks:
 //
-//  * Persistent grid, one block per CU, all blocks resident at once
-//    (cooperative launch). Streaming blocks share a prompt's 32-key tiles
+//  * Persistent grid, one block per CU, all blocks resident at once (the
+//    host checks that the grid fits). Streaming blocks share a prompt's 32-key tiles
 //    round-robin (block i of n takes tiles i, i + n, ...), at most 21 each.
 //    Eight more blocks, one per chip die (XCD), read no K: they merge the
 //    partial results of the streaming blocks on their die.
@@ -117,9 +117,19 @@ __host__ __device__ constexpr int64_t die_slot(int x, int bb, int die) {
   return (((int64_t)x * SP_MAX_PROMPTS + bb) * kDies + die) * kRows;
 }
 
+// Shared memory: the K ring and the Q slots (written by direct loads) and
+// the control block are separate objects. Loads into shared memory are
+// counted as outstanding vector-memory operations; the compiler makes an
+// access wait for all of them unless it can tell the access cannot touch
+// their destination, which it can only across distinct objects. The ring and
+// Q reads wait for exactly their own loads by explicit counts.
+struct Ring {
+  alignas(16) uint8_t unit[kCompute][kRing][kUnitBytes];   // K units, by wave
+};
+struct QSlots {
+  alignas(16) uint8_t q[kQSlots][kQSlotBytes];             // Q of three problems
+};
 struct Smem {
-  alignas(16) uint8_t ring[kCompute][kRing][kUnitBytes];   // K units, by wave
-  alignas(16) uint8_t qbuf[kQSlots][kQSlotBytes];          // Q of three problems
   float2 red[kRedSlots][kCompute][kRows];                  // per-wave (m, z), by problem % 4
   float lse[kLseSlots][kRows];                             // staged row lse, by problem % 8
   // Hand-offs between the compute waves and the control wave, without a
@@ -260,6 +270,15 @@ constexpr int kCoherent = 16;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
+// The same from wave-uniform values, placed in scalar registers (an inline
+// assembly operand that must live there).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_uniform(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return rsrc(reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo),
+              __builtin_amdgcn_readfirstlane(bytes));
+}
 
 __device__ __forceinline__ Quad load_quad(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
   Quad q;
@@ -342,23 +361,6 @@ __device__ void merge_block(const AttnShape &s, const StreamTable &tb, int d, in
   }
 }
 
-// One level of the final butterfly on every value of the wave's tiles:
-// Ctrl >= 0 is a DPP control (within rows of 16 lanes), -1 the swizzle that
-// exchanges lane bit 4 (within groups of 32 lanes). Max or sum.
-template <int Ctrl, int kTPW>
-__device__ __forceinline__ void butterfly_level(f32x16 (&run)[kTPW], bool use_max) {
-#pragma unroll
-  for (int t = 0; t < kTPW; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int v = __float_as_int(run[t][i]);
-      const float o = __int_as_float(Ctrl >= 0 ? __builtin_amdgcn_update_dpp(0, v, Ctrl & 0x1ff, 0xf,
-                                                                             0xf, false)
-                                               : __builtin_amdgcn_ds_swizzle(v, 0x401f));
-      run[t][i] = use_max ? fmaxf(run[t][i], o) : run[t][i] + o;
-    }
-}
-
 // LDS layout of a unit (32 rows x UB bytes, UB = 128 or 64): one 1 KB block
 // per load instruction holding KPI = 1024 / UB consecutive rows; row r's
 // 16-byte chunk c sits at chunk position c ^ swz(r) inside the row. With
@@ -374,17 +376,25 @@ struct UnitLayout {
   __device__ static constexpr int row_base(int r) { return 1024 * (r / KPI) + UB * (r % KPI); }
 };
 
-// kF8: K holds fp8 e4m3 codes, key value = kscale[problem] * code; each code
-// becomes a bf16 exactly (v_cvt_scalef32_pk_bf16_fp8 with scale 1) and the
-// scale joins the logit scale of its problem.
-template <int D, bool kF8, int kLag>
-__global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable tb,
-                                                        int64_t total_keys,
-                                                        const __bf16 *__restrict__ q,
-                                                        const uint8_t *__restrict__ k,
-                                                        float *__restrict__ imp, StreamWs ws,
-                                                        KScales ks) {
-  constexpr int kTPW = tpw_for_lag(kLag);            // tiles per compute wave
+// Per-call constants a compute wave needs.
+struct WaveCtx {
+  AttnShape s;
+  StreamWs ws;
+  const KScales *ks;
+  const uint8_t *k;
+  float *imp;
+  int64_t total_keys, key0;
+  int P, N, NK, rows, cta, tok0;
+  int w_key0, t_stride, full_tiles;   // the wave's tiles: keys w_key0 + t * t_stride ..
+  int wave, lane;
+};
+
+// A compute wave that owns NT tiles (0 <= NT <= 3): the tile count is a
+// compile-time constant, so every e slot stays in fixed registers with no
+// branch around it.
+template <int D, bool kF8, int kLag, int CL, int NT>
+__device__ __forceinline__ void compute_wave(const WaveCtx &c, Ring &ring, QSlots &qsl, Smem &sm,
+                                             bool &dead) {
   constexpr int kES = kF8 ? 1 : 2;                   // bytes per K element
   constexpr int RBG = D * kES;                       // K bytes per key and KV group
   constexpr int UB = RBG < 128 ? RBG : 128;          // bytes per key in a unit
@@ -393,14 +403,378 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
   constexpr int kStepsPerUnit = kSteps / UPT;
   using KL = UnitLayout<UB>;
   using QL = UnitLayout<128>;
+  constexpr int NTA = NT > 0 ? NT : 1;               // array extent
+  const AttnShape &s = c.s;
+  const StreamWs &ws = c.ws;
+  const int lane = c.lane, half = lane >> 5, r = lane & 31, wave = c.wave;
+  const int P = c.P, N = c.N, NK = c.NK;
+  const int w_key0 = c.w_key0, t_stride = c.t_stride;
+  // Query row r of the group: head r / (32 / G), step r % (32 / G) (heads
+  // on the top lane bits, so the head max can start at fold time: below).
+  const int rs_h = 32 / s.G;
+  const int jr = r % rs_h;
+  const bool row_ok = jr < s.L;
+
+  // K of the prompt, by problem: a resource per (layer, group) whose range
+  // ends at the prompt's last key row; keys past it read as zeros.
+  const int64_t rowb = (int64_t)s.Hkv * RBG;          // bytes per key row (all groups)
+  const uint32_t k_bytes = (uint32_t)((NK - 1) * rowb + RBG);
+  const int64_t layer_step = c.total_keys * rowb - (int64_t)(s.Hkv - 1) * RBG;
+  // Per load instruction i of a unit: the lane's row (key within the tile)
+  // and byte offset of its 16-byte chunk.
+  const int lrow0 = lane / KL::SPK;            // + KPI i for instruction i
+  uint32_t loff[KL::IPU];
+#pragma unroll
+  for (int i = 0; i < KL::IPU; ++i) {
+    const int rr = KL::KPI * i + lrow0;
+    loff[i] = (uint32_t)(rr * rowb + 16 * ((lane % KL::SPK) ^ KL::swz(rr)));
+  }
+  // The ring: unit k of the wave's sequence (problem, tile, unit of the tile)
+  // goes to slot k % 4. Issue state, advanced without divisions.
+  const int total_units = P * NT * UPT;
+  const uint32_t tile_bytes = (uint32_t)(t_stride * rowb);   // between the wave's tiles
+  const uint32_t toff0 = (uint32_t)(w_key0 * rowb);
+  int ki = 0, kt = 0, ku = 0, kg = 0;            // next unit to issue: its tile, unit, group
+  const uint8_t *kbase = c.k + c.key0 * rowb;    // group slice of its problem
+  uint32_t ktoff = toff0;                        // its tile's offset
+  auto issue_next = [&]() {
+    if (ki >= total_units) return;
+    const __amdgpu_buffer_rsrc_t kr = rsrc_uniform(kbase, k_bytes);
+    const uint32_t tb_off = ktoff + ku * UB;
+    const int tk0 = w_key0 + kt * t_stride;    // the tile's first key
+    // The loads are issued by inline assembly: the compiler then does not
+    // track them, so it adds no waits for them before unrelated shared
+    // memory accesses (it would otherwise wait for every outstanding K load
+    // before each hand-off counter). wait_unit() waits for them explicitly.
+    const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+        (__attribute__((address_space(3))) uint8_t *)&ring.unit[wave][ki & (kRing - 1)][0]));
+    if (tk0 + kTile <= NK) {
+#pragma unroll
+      for (int i = 0; i < KL::IPU; ++i)
+        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                     :: "v"(tb_off + loff[i]), "s"(kr), "{m0}"(dst + 1024 * i) : "memory");
+    } else {
+#pragma unroll
+      for (int i = 0; i < KL::IPU; ++i) {
+        const uint32_t vo = tk0 + KL::KPI * i + lrow0 < NK ? tb_off + loff[i] : kOob;
+        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                     :: "v"(vo), "s"(kr), "{m0}"(dst + 1024 * i) : "memory");
+      }
+    }
+    ++ki;
+    if (++ku == UPT) {
+      ku = 0;
+      ktoff += tile_bytes;
+      if (++kt == NT) {
+        kt = 0;
+        ktoff = toff0;
+        if (++kg == s.Hkv) { kg = 0; kbase += layer_step; } else { kbase += RBG; }
+      }
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) issue_next();
+  int kc = 0;   // next unit to consume
+  // Wait until unit kc has landed: the (three) units issued after it may
+  // still fly; near the end of the stream wait for everything.
+  auto wait_unit = [&]() {
+    if (ki - kc >= kRing) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 1) * KL::IPU) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
+  // Operand reads. K: k-step st reads chunk 2 st + half of the row (bf16;
+  // unit st / 4) or 8 bytes at half of chunk st (fp8). Q: chunk 2 st + half
+  // (unit st / 4). For 128-byte units the two layouts coincide.
+  const int k_rb = KL::row_base(r), k_sw = KL::swz(r);
+  const int q_rb = QL::row_base(r), q_sw = QL::swz(r);
+  auto k_operand = [&](const uint8_t *unit, int st) -> bf16x8 {
+    if constexpr (!kF8) {
+      const int cc = (2 * st + half) % KL::SPK;
+      return *reinterpret_cast<const bf16x8 *>(unit + k_rb + 16 * (cc ^ k_sw));
+    } else {
+      const int cc = st % KL::SPK;
+      const uint2 w = *reinterpret_cast<const uint2 *>(unit + k_rb + 16 * (cc ^ k_sw) + 8 * half);
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, false);
+      const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, true);
+      const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, false);
+      const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, true);
+      return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+    }
+  };
+  auto q_operand = [&](const uint8_t *qs, int st) -> bf16x8 {
+    const int kq = 2 * st + half;
+    return *reinterpret_cast<const bf16x8 *>(qs + (kq / 8) * kUnitBytes + q_rb +
+                                             16 * ((kq % 8) ^ q_sw));
+  };
+  // MFMAs of k-steps [st0, st0 + 2) of a tile into acc, both operands of
+  // both read first (two reads in flight per wait).
+  // The first starts from init: 0, or -inf where a key is past the prompt's
+  // keys or hidden from the row (causality), so the logit is -inf there.
+  auto mfma2 = [&](f32x16 &acc, const uint8_t *unit, const uint8_t *qs, int st0, bool first,
+                   const f32x16 &init) {
+    bf16x8 ko[2], qo[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      ko[j] = k_operand(unit, st0 + j);
+      qo[j] = q_operand(qs, st0 + j);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ko[j], qo[j], (first && j == 0) ? init : acc,
+                                                    0, 0, 0);
+  };
+  // Accumulator start of tile t: all 0 unless the tile reaches past the
+  // prompt's keys (lookahead keys and the rest of the prompt's last tile).
+  // The lane's 16 visible keys of each tile as a bit mask, expanded at use
+  // (an opaque step keeps the compiler from hoisting 16 registers per tile
+  // out of the problem loop).
+  uint32_t vis[NTA];
+  bool partial[NTA];
+#pragma unroll
+  for (int t = 0; t < NTA; ++t) {
+    const int tk0 = w_key0 + t * t_stride;
+    partial[t] = tk0 + kTile > N;
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = tk0 + acc_row(i, half);
+      m |= (key < NK && key <= N - s.pre + jr) ? 1u << i : 0u;
+    }
+    vis[t] = m;
+  }
+  auto tile_init = [&](int t) -> f32x16 {
+    f32x16 v = {};
+    if (partial[t]) {
+      uint32_t m = vis[t];
+      asm volatile("" : "+v"(m));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = (m >> i) & 1u ? 0.f : -INFINITY;
+    }
+    return v;
+  };
+
+  // e slots: the accumulators of the problem in flight, then its e until
+  // folded. run: the running max over folded problems, kept as the bits of
+  // non-negative floats (they order like the values). The fold also takes
+  // the max over the heads on lane bits 4 (and 3): CL levels, after which a
+  // lane keeps 16 >> CL of its 16 keys (acc index 8 b4 + 4 b3 + k).
+  constexpr int RV = 16 >> CL;
+  f32x16 e[kLag][NTA];
+  uint32_t run[NTA][RV];
+  float mref[kLag];          // row max of the problem in each slot (base 2)
+#pragma unroll
+  for (int t = 0; t < NTA; ++t) {
+#pragma unroll
+    for (int k = 0; k < RV; ++k) run[t][k] = 0u;
+#pragma unroll
+    for (int a = 0; a < kLag; ++a) e[a][t] = f32x16{};
+  }
+  const bool b3 = (lane >> 3) & 1;
+#pragma unroll
+  for (int a = 0; a < kLag; ++a) mref[a] = -INFINITY;
+  // Fold slot a into run with factor f (0 before the first lag problems: a
+  // no-op, since run >= 0).
+  auto fold_tile = [&](int a, int t, float f) {
+    uint32_t p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = __float_as_uint(e[a][t][i] * f);
+    if constexpr (CL >= 1) {
+      // Lane bit 4 (lanes l, l ^ 16): one swap of register pairs (i, i + 8)
+      // gives the lane with bit 4 clear both values of key i, the other
+      // both values of key i + 8.
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(p[i], p[i + 8], false, false);
+        p[i] = __builtin_elementwise_max(sw[0], sw[1]);
+      }
+    }
+    if constexpr (CL >= 2) {
+      // Lane bit 3 (lanes l, l ^ 8: a rotation by 8 within rows of 16).
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t keep = b3 ? p[k + 4] : p[k], send = b3 ? p[k] : p[k + 4];
+        p[k] = __builtin_elementwise_max(
+            keep, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0x128, 0xf, 0xf, false));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < RV; ++k) run[t][k] = __builtin_elementwise_max(run[t][k], p[k]);
+  };
+
+  for (int x0 = 0; x0 < P + kLag; x0 += kLag) {
+#pragma unroll
+    for (int a = 0; a < kLag; ++a) {
+      const int x = x0 + a;            // problem computed now; x - kLag is folded
+      if (x >= P + kLag) break;
+      float fold_f = 0.f;
+      if (x >= kLag) {
+        const int xf = x - kLag;
+        lds_wait_ge(&sm.lse_ready[xf % kLseSlots], xf + 1, ws, dead);
+        const float l2 = sm.lse[xf % kLseSlots][r];
+        fold_f = (row_ok && mref[a] != -INFINITY) ? __builtin_amdgcn_exp2f(mref[a] - l2) : 0.f;
+        if (lane == 0) lds_inc(&sm.lse_used[xf % kLseSlots]);
+      }
+      if (x >= P) {
+        // Past the last problem: fold only.
+#pragma unroll
+        for (int t = 0; t < NT; ++t) fold_tile(a, t, fold_f);
+        continue;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      lds_wait_ge(&sm.q_ready, x + 1, ws, dead);
+      const uint8_t *qs = &qsl.q[x % kQSlots][0];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        fold_tile(a, t, fold_f);
+        __builtin_amdgcn_sched_barrier(0);
+        const f32x16 init = tile_init(t);
+#pragma unroll
+        for (int u = 0; u < UPT; ++u) {
+          wait_unit();
+          const uint8_t *unit = &ring.unit[wave][kc & (kRing - 1)][0];
+#pragma unroll
+          for (int g2 = 0; g2 < kStepsPerUnit; g2 += 2)
+            mfma2(e[a][t], unit, qs, u * kStepsPerUnit + g2, u == 0 && g2 == 0, init);
+          // The MFMAs above have read the unit (their operands were waited
+          // for): refill its slot.
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          ++kc;
+          issue_next();
+          __builtin_amdgcn_sched_barrier(0);   // keep the next unit's reads after the refill
+        }
+      }
+      if (lane == 0) lds_inc(&sm.q_used[x % kQSlots]);
+      // Row max over the wave's keys (both halves), then e = 2^(x - m) in
+      // place and the row sum (masked logits are -inf and give 0). The
+      // lookahead keys keep their e: they are never stored.
+      const float sl2 = kF8 ? s.scale_log2 * c.ks->v[x] : s.scale_log2;
+      float mt = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, e[a][t][i]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m = mt * sl2;      // -inf when the wave has no key this row sees
+      const float mz = m == -INFINITY ? 0.f : m;
+      float z = 0.f;
+      // (One tile at a time: left free, the scheduler computes every tile's
+      // exponent arguments first and runs out of registers.)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float ev = __builtin_amdgcn_exp2f(__builtin_fmaf(e[a][t][i], sl2, -mz));
+          z += ev;
+          e[a][t][i] = ev;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      z += __shfl_xor(z, 32, 64);
+      mref[a] = m;
+      const int rs = x % kRedSlots;
+      if (lane < 32) sm.red[rs][wave][r] = make_float2(m, z);
+      // The last wave to finish the problem posts the block's partials.
+      const int arrived = __builtin_amdgcn_readfirstlane(lane == 0 ? lds_inc(&sm.stats_cnt[rs]) : 0);
+      if (arrived == kCompute * (x / kRedSlots + 1) - 1 && lane < kRows) {
+        float M = -INFINITY, Z = 0.f;
+#pragma unroll
+        for (int w = 0; w < kCompute; ++w)
+          stats_merge(M, Z, sm.red[rs][w][lane].x, sm.red[rs][w][lane].y);
+        // Twice: an ordinary store that the merge block of this die reads
+        // from the die's L2, and a device-coherent one for a merge block
+        // elsewhere.
+        const int64_t at = cta_slot(x, c.cta) + lane;
+        const uint64_t word = slot_word(lse_of(M, Z), ws.call_tag);
+        ws.lslot[at] = word;
+        __hip_atomic_store(ws.slot + at, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+
+  // The rest of the reduction over the lane bits of the row (head r /
+  // (32 / G) on the top bits, step r % (32 / G) on the bottom ones): first a
+  // max over the head bits the fold left (G >= 8), then a sum over the step
+  // bits (padding steps hold 0). Each level exchanges across one lane bit
+  // (a swizzle within 32 lanes); it runs once per kernel.
+  if constexpr (NT > 0) {
+    float runf[NT][RV];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int k = 0; k < RV; ++k) runf[t][k] = __uint_as_float(run[t][k]);
+    const int hb = __builtin_ctz(rs_h);          // lowest head bit
+    constexpr int top = 4 - CL;                  // highest bit not reduced at fold time
+    auto level = [&](auto bit_tag, bool use_max) {
+      constexpr int B = decltype(bit_tag)::value;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int k = 0; k < RV; ++k) {
+          const float o = __int_as_float(
+              __builtin_amdgcn_ds_swizzle(__float_as_int(runf[t][k]), ((1 << B) << 10) | 0x1f));
+          runf[t][k] = use_max ? fmaxf(runf[t][k], o) : runf[t][k] + o;
+        }
+    };
+    auto both = [&](auto bit_tag) {
+      constexpr int B = decltype(bit_tag)::value;
+      if constexpr (B <= top) {
+        if (B >= hb) level(bit_tag, true);
+      }
+    };
+    auto steps = [&](auto bit_tag) {
+      constexpr int B = decltype(bit_tag)::value;
+      if constexpr (B <= top) {
+        if (B < hb) level(bit_tag, false);
+      }
+    };
+    both(std::integral_constant<int, 0>{});
+    both(std::integral_constant<int, 1>{});
+    both(std::integral_constant<int, 2>{});
+    both(std::integral_constant<int, 3>{});
+    both(std::integral_constant<int, 4>{});
+    steps(std::integral_constant<int, 0>{});
+    steps(std::integral_constant<int, 1>{});
+    steps(std::integral_constant<int, 2>{});
+    steps(std::integral_constant<int, 3>{});
+    steps(std::integral_constant<int, 4>{});
+    // Lanes whose reduced bits are all 0 hold the results of their keys:
+    // acc index 8 b4 + 4 b3 + k for the compacted bits.
+    const float inv_l = 1.f / (float)s.L;
+    float *out = c.imp + c.tok0;
+    const int low = r & ((1 << (5 - CL)) - 1);
+    const int ibase = (CL >= 1 ? 8 * ((r >> 4) & 1) : 0) + (CL >= 2 ? 4 * ((r >> 3) & 1) : 0);
+    if (low == 0) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int k = 0; k < RV; ++k) {
+          const int key = w_key0 + t * t_stride + acc_row(ibase + k, half);
+          if (key < N) out[key] = runf[t][k] * inv_l;
+        }
+    }
+  }
+}
+
+template <int D, bool kF8, int kLag, int CL>
+__global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable tb,
+                                                        int64_t total_keys,
+                                                        const __bf16 *__restrict__ q,
+                                                        const uint8_t *__restrict__ k,
+                                                        float *__restrict__ imp, StreamWs ws,
+                                                        KScales ks) {
+  constexpr int kTPW = tpw_for_lag(kLag);            // tiles per compute wave
+  using QL = UnitLayout<128>;
   constexpr int QU = D * 2 / 128;                    // Q units per problem (1 or 2)
   static_assert(QU * kUnitBytes <= kQSlotBytes, "Q slot too small");
 
+  __shared__ Ring ring;
+  __shared__ QSlots qsl;
   __shared__ Smem sm;
   const int cta = blockIdx.x;
   // The wave index is uniform across a wave; saying so keeps every value
   // derived from it in scalar registers and every branch on it scalar.
-  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, r = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = s.n_layers * s.Hkv;
   if (cta >= tb.n_stream) {
@@ -436,25 +810,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
     const __amdgpu_buffer_rsrc_t qr = rsrc(q + (int64_t)b * q_elems, (uint32_t)(q_elems * 2));
     uint32_t qoff[QL::IPU];   // per instruction: the lane's row and chunk within a problem's Q
     int qrow_j[QL::IPU], qrow_h[QL::IPU];
+    const int rs_h = 32 / s.G;   // query row rr: head rr / (32 / G), step rr % (32 / G)
 #pragma unroll
     for (int i = 0; i < QL::IPU; ++i) {
       const int rr = QL::KPI * i + lane / QL::SPK;
       const int c = (lane % QL::SPK) ^ QL::swz(rr);
-      qrow_j[i] = rr / s.G;
-      qrow_h[i] = rr - qrow_j[i] * s.G;
+      qrow_j[i] = rr % rs_h;
+      qrow_h[i] = rr / rs_h;
       qoff[i] = (uint32_t)(16 * c);
     }
     auto issue_q = [&](int y) {
       const int l = y / s.Hkv, g = y - l * s.Hkv;
-      uint8_t *dst = &sm.qbuf[y % kQSlots][0];
+      uint8_t *dst = &qsl.q[y % kQSlots][0];
 #pragma unroll
       for (int u = 0; u < QU; ++u)
 #pragma unroll
         for (int i = 0; i < QL::IPU; ++i) {
-          const int rr = QL::KPI * i + lane / QL::SPK;
           const uint32_t row_off =
               (uint32_t)((((int64_t)l * s.L + qrow_j[i]) * s.Hq + g * s.G + qrow_h[i]) * D * 2);
-          const uint32_t vo = rr < rows ? row_off + u * 128 + qoff[i] : kOob;
+          const uint32_t vo = qrow_j[i] < s.L ? row_off + u * 128 + qoff[i] : kOob;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               qr, (__attribute__((address_space(3))) void *)(dst + u * kUnitBytes + 1024 * i), 16,
               vo, 0, 0, 0);
@@ -520,259 +894,60 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
   const int nt_blk = (ntiles - ci + n_c - 1) / n_c;
   const int w_t0 = (nt_blk * wave) / kCompute;
   const int nt = (nt_blk * (wave + 1)) / kCompute - w_t0;   // this wave's tiles (<= kTPW)
-  const int t_stride = n_c * kTile;
-  const int w_key0 = (ci + n_c * w_t0) * kTile;             // first key of the wave's tile 0
-  const bool row_ok = r < rows;
-  const int jr = row_ok ? r / s.G : 0;
+  WaveCtx c;
+  c.s = s;
+  c.ws = ws;
+  c.ks = &ks;
+  c.k = k;
+  c.imp = imp;
+  c.total_keys = total_keys;
+  c.key0 = key0;
+  c.P = P;
+  c.N = N;
+  c.NK = NK;
+  c.rows = rows;
+  c.cta = cta;
+  c.tok0 = tb.tok_off[bb];
+  c.t_stride = n_c * kTile;
+  c.w_key0 = (ci + n_c * w_t0) * kTile;
+  c.wave = wave;
+  c.lane = lane;
   // A tile is "full" (all keys are prompt keys, seen by every row) when it
   // ends by N; the wave's full tiles come first.
   int full_tiles = 0;
-  while (full_tiles < nt && w_key0 + full_tiles * t_stride + kTile <= N) ++full_tiles;
-
-  // K of the prompt, by problem: a resource per (layer, group) whose range
-  // ends at the prompt's last key row; keys past it read as zeros.
-  const int64_t rowb = (int64_t)s.Hkv * RBG;          // bytes per key row (all groups)
-  const uint8_t *kprompt = k + key0 * rowb;
-  const uint32_t k_bytes = (uint32_t)((NK - 1) * rowb + RBG);
-  // Per load instruction i of a unit: the lane's row (key within the tile)
-  // and byte offset of its 16-byte chunk.
-  const int lrow0 = lane / KL::SPK;            // + KPI i for instruction i
-  uint32_t loff[KL::IPU];
-#pragma unroll
-  for (int i = 0; i < KL::IPU; ++i) {
-    const int rr = KL::KPI * i + lrow0;
-    loff[i] = (uint32_t)(rr * rowb + 16 * ((lane % KL::SPK) ^ KL::swz(rr)));
-  }
-  // The ring: unit k of the wave's sequence (problem, tile, unit of the tile)
-  // goes to slot k % 4. Issue state:
-  const int per_x = nt * UPT;                  // units per problem
-  const int total_units = P * per_x;
-  int ki = 0, kx = 0, kt = 0, ku = 0;          // next unit to issue and its (x, t, u)
-  auto issue_next = [&]() {
-    if (ki >= total_units) return;
-    const int l = kx / s.Hkv, g = kx - l * s.Hkv;
-    const __amdgpu_buffer_rsrc_t kr = rsrc(kprompt + l * total_keys * rowb + g * RBG, k_bytes);
-    const int tk0 = w_key0 + kt * t_stride;    // the tile's first key
-    const uint32_t tb_off = (uint32_t)(tk0 * rowb) + ku * UB;
-    uint8_t *dst = &sm.ring[wave][ki & (kRing - 1)][0];
-#pragma unroll
-    for (int i = 0; i < KL::IPU; ++i) {
-      const uint32_t vo = tk0 + KL::KPI * i + lrow0 < NK ? tb_off + loff[i] : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          kr, (__attribute__((address_space(3))) void *)(dst + 1024 * i), 16, vo, 0, 0, 2);
-    }
-    ++ki;
-    if (++ku == UPT) {
-      ku = 0;
-      if (++kt == nt) { kt = 0; ++kx; }
-    }
-  };
-#pragma unroll
-  for (int i = 0; i < kRing; ++i) issue_next();
-  int kc = 0;   // next unit to consume
-  // Wait until unit kc has landed: the units issued after it may still fly.
-  auto wait_unit = [&]() {
-    const int after = ki - 1 - kc;
-    if (after >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * KL::IPU) : "memory");
-    else if (after == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * KL::IPU) : "memory");
-    else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KL::IPU) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  };
-
-  // Operand reads. K: k-step st reads chunk 2 st + half of the row (bf16;
-  // unit st / 4) or 8 bytes at half of chunk st (fp8). Q: chunk 2 st + half
-  // (unit st / 4). For 128-byte units the two layouts coincide.
-  const int k_rb = KL::row_base(r), k_sw = KL::swz(r);
-  const int q_rb = QL::row_base(r), q_sw = QL::swz(r);
-  auto k_operand = [&](const uint8_t *unit, int st) -> bf16x8 {
-    if constexpr (!kF8) {
-      const int c = (2 * st + half) % KL::SPK;
-      return *reinterpret_cast<const bf16x8 *>(unit + k_rb + 16 * (c ^ k_sw));
-    } else {
-      const int c = st % KL::SPK;
-      const uint2 w = *reinterpret_cast<const uint2 *>(unit + k_rb + 16 * (c ^ k_sw) + 8 * half);
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, false);
-      const bf16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, true);
-      const bf16x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, false);
-      const bf16x2 d2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, true);
-      return bf16x8{a[0], a[1], b2[0], b2[1], c2[0], c2[1], d2[0], d2[1]};
-    }
-  };
-  auto q_operand = [&](const uint8_t *qs, int st) -> bf16x8 {
-    const int kq = 2 * st + half;
-    return *reinterpret_cast<const bf16x8 *>(qs + (kq / 8) * kUnitBytes + q_rb +
-                                             16 * ((kq % 8) ^ q_sw));
-  };
-
-  f32x16 e[kLag][kTPW];      // e slots (accumulators of the problem in flight)
-  f32x16 run[kTPW];          // running max over folded problems, per (row, key)
-  float mref[kLag];          // row max of the problem in each slot (base 2)
-#pragma unroll
-  for (int t = 0; t < kTPW; ++t) run[t] = f32x16{};
-#pragma unroll
-  for (int a = 0; a < kLag; ++a) mref[a] = -INFINITY;
-
-  for (int x0 = 0; x0 < P + kLag; x0 += kLag) {
-#pragma unroll
-    for (int a = 0; a < kLag; ++a) {
-      const int x = x0 + a;            // problem computed now; x - kLag is folded
-      if (x >= P + kLag) break;
-      float fold_f = 0.f;
-      const bool fold = x >= kLag;
-      if (fold) {
-        const int xf = x - kLag;
-        lds_wait_ge(&sm.lse_ready[xf % kLseSlots], xf + 1, ws, dead);
-        const float l2 = sm.lse[xf % kLseSlots][r];
-        fold_f = (row_ok && mref[a] != -INFINITY) ? __builtin_amdgcn_exp2f(mref[a] - l2) : 0.f;
-        if (lane == 0) lds_inc(&sm.lse_used[xf % kLseSlots]);
-      }
-      if (x < P) {
-        lds_wait_ge(&sm.q_ready, x + 1, ws, dead);
-        const uint8_t *qs = &sm.qbuf[x % kQSlots][0];
-#pragma unroll
-        for (int t = 0; t < kTPW; ++t) {
-          if (t < nt) {
-            if (fold) {
-#pragma unroll
-              for (int i = 0; i < 16; ++i) run[t][i] = fmaxf(run[t][i], e[a][t][i] * fold_f);
-            }
-            f32x16 acc = {};
-#pragma unroll
-            for (int u = 0; u < UPT; ++u) {
-              wait_unit();
-              const uint8_t *unit = &sm.ring[wave][kc & (kRing - 1)][0];
-#pragma unroll
-              for (int j = 0; j < kStepsPerUnit; ++j) {
-                const int st = u * kStepsPerUnit + j;
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(unit, st),
-                                                              q_operand(qs, st), acc, 0, 0, 0);
-              }
-              // The MFMAs above have read the unit (their operands were
-              // waited for): refill its slot.
-              asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-              ++kc;
-              issue_next();
-            }
-            e[a][t] = acc;
-          }
-        }
-        if (lane == 0) lds_inc(&sm.q_used[x % kQSlots]);
-        // Row max over the wave's keys (both halves), then e = 2^(x - m) in
-        // place and the row sum.
-        const float sl2 = kF8 ? s.scale_log2 * ks.v[x] : s.scale_log2;
-        float mt = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < kTPW; ++t) {
-          if (t < full_tiles) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, e[a][t][i]);
-          } else if (t < nt) {
-            // Tail tile: keys past the prompt's keys, causal lookahead keys.
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = w_key0 + t * t_stride + acc_row(i, half);
-              const bool ok = key < NK && key <= N - s.pre + jr;
-              e[a][t][i] = ok ? e[a][t][i] : -INFINITY;
-              mt = fmaxf(mt, e[a][t][i]);
-            }
-          }
-        }
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float m = mt * sl2;      // -inf when the wave has no key this row sees
-        float z = 0.f;
-#pragma unroll
-        for (int t = 0; t < kTPW; ++t) {
-          if (t < full_tiles) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const float ev = __builtin_amdgcn_exp2f(__builtin_fmaf(e[a][t][i], sl2, -m));
-              z += ev;
-              e[a][t][i] = ev;
-            }
-          } else if (t < nt) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const float xv = e[a][t][i];
-              const float ev = xv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(xv, sl2, -m));
-              z += ev;
-              const int key = w_key0 + t * t_stride + acc_row(i, half);
-              e[a][t][i] = key < N ? ev : 0.f;    // lookahead keys get no importance
-            }
-          }
-        }
-        z += __shfl_xor(z, 32, 64);
-        mref[a] = m;
-        const int rs = x % kRedSlots;
-        if (lane < 32) sm.red[rs][wave][r] = make_float2(m, z);
-        // The last wave to finish the problem posts the block's partials.
-        const int arrived = __builtin_amdgcn_readfirstlane(lane == 0 ? lds_inc(&sm.stats_cnt[rs]) : 0);
-        if (arrived == kCompute * (x / kRedSlots + 1) - 1 && lane < kRows) {
-          float M = -INFINITY, Z = 0.f;
-#pragma unroll
-          for (int w = 0; w < kCompute; ++w)
-            stats_merge(M, Z, sm.red[rs][w][lane].x, sm.red[rs][w][lane].y);
-          // Twice: an ordinary store that the merge block of this die reads
-          // from the die's L2, and a device-coherent one for a merge block
-          // elsewhere.
-          const int64_t at = cta_slot(x, cta) + lane;
-          const uint64_t word = slot_word(lse_of(M, Z), ws.call_tag);
-          ws.lslot[at] = word;
-          __hip_atomic_store(ws.slot + at, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      } else if (fold) {
-        // Past the last problem: fold only.
-#pragma unroll
-        for (int t = 0; t < kTPW; ++t)
-          if (t < nt) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) run[t][i] = fmaxf(run[t][i], e[a][t][i] * fold_f);
-          }
-      }
-    }
-  }
-
-  // Max over the G heads of each step (lanes j*G .. j*G+G-1), then the sum
-  // over the steps (the other lane bits; padding rows hold 0): one butterfly
-  // over the five lane bits of the row, each level a max or a sum. After
-  // level k every aligned group of 2^k lanes holds one value, so a mirror
-  // inside the next group pairs the same partial results as an exchange
-  // across lane bit k: levels 1, 2 are quad permutations, 4 and 8 the
-  // half-row and row mirrors (all DPP), 16 a swizzle within 32 lanes.
-  butterfly_level<0xB1>(run, 1 < s.G);
-  butterfly_level<0x4E>(run, 2 < s.G);
-  butterfly_level<0x141>(run, 4 < s.G);
-  butterfly_level<0x140>(run, 8 < s.G);
-  butterfly_level<-1>(run, 16 < s.G);
-  // Every lane of a half now holds the 16 results of its half's keys; lane
-  // r < 16 stores result r, so each tile is one store instruction.
-  const float inv_l = 1.f / (float)s.L;
-  float *out = imp + tb.tok_off[bb];
-#pragma unroll
-  for (int t = 0; t < kTPW; ++t) {
-    float v = run[t][0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) v = r == i ? run[t][i] : v;
-    const int key = w_key0 + t * t_stride + acc_row(r & 15, half);
-    if (r < 16 && t < nt && key < N) out[key] = v * inv_l;
+  while (full_tiles < nt && c.w_key0 + full_tiles * c.t_stride + kTile <= N) ++full_tiles;
+  c.full_tiles = full_tiles;
+  switch (nt) {
+    case 0: compute_wave<D, kF8, kLag, CL, 0>(c, ring, qsl, sm, dead); break;
+    case 1: compute_wave<D, kF8, kLag, CL, 1>(c, ring, qsl, sm, dead); break;
+    case 2:
+      if constexpr (kTPW >= 2) compute_wave<D, kF8, kLag, CL, 2>(c, ring, qsl, sm, dead);
+      break;
+    default:
+      if constexpr (kTPW >= 3) compute_wave<D, kF8, kLag, CL, 3>(c, ring, qsl, sm, dead);
+      break;
   }
 }
 
 struct DeviceInfo {
   int cus = 0;
-  int coop = 0;       // cooperative launches supported
   int occ = 0;        // blocks per CU of every kernel form (the least of them)
 };
 
-template <int D, bool F8>
-bool occupancy(int *occ) {
+// Blocks per CU of every form of the kernel (the least of them).
+template <int D, bool F8, int CL>
+bool occupancy_cl(int *occ) {
   int a = 0, b = 0, c = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, k_stream<D, F8, 2>, kThreads, 0) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_stream<D, F8, 4>, kThreads, 0) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, k_stream<D, F8, 8>, kThreads, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, k_stream<D, F8, 2, CL>, kThreads, 0) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_stream<D, F8, 4, CL>, kThreads, 0) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, k_stream<D, F8, 8, CL>, kThreads, 0) != hipSuccess)
     return false;
   *occ = std::min(*occ, std::min(a, std::min(b, c)));
   return true;
+}
+template <int D, bool F8>
+bool occupancy(int *occ) {
+  return occupancy_cl<D, F8, 0>(occ) && occupancy_cl<D, F8, 1>(occ) && occupancy_cl<D, F8, 2>(occ);
 }
 
 const DeviceInfo &device_info() {
@@ -786,7 +961,6 @@ const DeviceInfo &device_info() {
     DeviceInfo d;
     d.occ = 1 << 20;
     if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipDeviceGetAttribute(&d.coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
         !occupancy<128, false>(&d.occ) || !occupancy<64, false>(&d.occ) ||
         !occupancy<128, true>(&d.occ) || !occupancy<64, true>(&d.occ))
       d = DeviceInfo();
@@ -865,7 +1039,7 @@ bool make_plan(const SegTable &tok, int L, int n_stream, Plan &plan) {
 // blocks, so that every block of a launch is resident at once.
 int stream_ctas() {
   const DeviceInfo &d = device_info();
-  if (d.occ < 1 || d.cus < 2 * kDies || !d.coop) return 0;
+  if (d.occ < 1 || d.cus < 2 * kDies) return 0;
   return std::min(d.cus / kDies * kDies, kMaxCtas) - kDies;
 }
 
@@ -941,10 +1115,20 @@ hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const 
     // compute wave.
     const int tpw = (plan.max_tiles[li] + kCompute - 1) / kCompute;
     const int lag = lag_for_tpw(tpw);
+    // Head-max levels taken at fold time: lane bits 4 and 3 are head bits
+    // for G >= 4, bit 4 for G = 2.
+    const int cl = s.G >= 4 ? 2 : s.G == 2 ? 1 : 0;
     auto pick = [&](auto d_tag, auto f8_tag) {
       constexpr int Dv = decltype(d_tag)::value;
       constexpr bool F8v = decltype(f8_tag)::value;
-      return lag == 8 ? k_stream<Dv, F8v, 8> : lag == 4 ? k_stream<Dv, F8v, 4> : k_stream<Dv, F8v, 2>;
+      auto by_lag = [&](auto cl_tag) {
+        constexpr int C = decltype(cl_tag)::value;
+        return lag == 8 ? k_stream<Dv, F8v, 8, C> : lag == 4 ? k_stream<Dv, F8v, 4, C>
+                                                             : k_stream<Dv, F8v, 2, C>;
+      };
+      return cl == 2 ? by_lag(std::integral_constant<int, 2>{})
+                     : cl == 1 ? by_lag(std::integral_constant<int, 1>{})
+                               : by_lag(std::integral_constant<int, 0>{});
     };
     using D64 = std::integral_constant<int, 64>;
     using D128 = std::integral_constant<int, 128>;
@@ -954,8 +1138,12 @@ hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const 
     int64_t tk = total_keys;
     KScales kss = ks;
     void *args[] = {&sa, &tbl, &tk, &qp, &kp, &imp, &w, &kss};
-    const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(kern),
-                                                    dim3(plan.grid[li]), dim3(kThreads), args, 0, st);
+    // An ordinary launch: the host has checked that the grid fits the device
+    // with every block resident (one per CU). A cooperative launch would
+    // guarantee it against other work on the device too, but costs ~11 us
+    // more per call here; the bounded waits cover that case instead.
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(plan.grid[li]),
+                                         dim3(kThreads), args, 0, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
