@@ -185,6 +185,16 @@ __device__ __forceinline__ int cta_prompt(const StreamTable &t, int c) {
   return lo;
 }
 
+// stats_merge without branches, on the hardware exp2 (terms below 2^-126 of
+// the total flush to 0): for the partials of one block.
+__device__ __forceinline__ void stats_merge_lean(float &M, float &Z, float m, float z) {
+  const float nm = fmaxf(M, m);
+  const float a = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - nm);
+  const float b = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - nm);
+  Z = Z * a + z * b;
+  M = nm;
+}
+
 // Base-2 lse of a set given by its max and its sum of 2^(x - max).
 __device__ __forceinline__ float lse_of(float m, float z) {
   return (m == -INFINITY || !(z > 0.f)) ? -INFINITY : m + log2f(z);
@@ -211,8 +221,10 @@ __device__ __forceinline__ Group group_of(int d, int c_lo, int n_c) {
 
 // Kernel forms: the lag (problems folded behind) and the tiles per compute
 // wave it allows, 6 to 8 e slots of 16 registers each.
-__host__ __device__ constexpr int tpw_for_lag(int lag) { return lag == 2 ? 3 : lag == 4 ? 2 : 1; }
-constexpr int lag_for_tpw(int tpw) { return tpw <= 1 ? 8 : tpw == 2 ? 4 : 2; }
+// Problems a compute wave keeps parked (kPk) for the tiles it owns, and
+// back: the most that fit its registers.
+__host__ __device__ constexpr int tpw_for_pk(int pk) { return pk == 2 ? 3 : pk == 4 ? 2 : 1; }
+constexpr int pk_for_tpw(int tpw) { return tpw <= 1 ? 7 : tpw == 2 ? 4 : 2; }
 
 // A lane's four rows of a partial: two 16-byte loads of two slots each.
 struct Quad {
@@ -392,7 +404,7 @@ struct WaveCtx {
 // A compute wave that owns NT tiles (0 <= NT <= 3): the tile count is a
 // compile-time constant, so every e slot stays in fixed registers with no
 // branch around it.
-template <int D, bool kF8, int kLag, int CL, int NT>
+template <int D, bool kF8, int kPk, int CL, int NT>
 __device__ __forceinline__ void compute_wave(const WaveCtx &c, Ring &ring, QSlots &qsl, Smem &sm,
                                              bool &dead) {
   constexpr int kES = kF8 ? 1 : 2;                   // bytes per K element
@@ -507,22 +519,20 @@ __device__ __forceinline__ void compute_wave(const WaveCtx &c, Ring &ring, QSlot
     return *reinterpret_cast<const bf16x8 *>(qs + (kq / 8) * kUnitBytes + q_rb +
                                              16 * ((kq % 8) ^ q_sw));
   };
-  // MFMAs of k-steps [st0, st0 + 2) of a tile into acc, both operands of
-  // both read first (two reads in flight per wait).
-  // The first starts from init: 0, or -inf where a key is past the prompt's
-  // keys or hidden from the row (causality), so the logit is -inf there.
-  auto mfma2 = [&](f32x16 &acc, const uint8_t *unit, const uint8_t *qs, int st0, bool first,
-                   const f32x16 &init) {
-    bf16x8 ko[2], qo[2];
+  // MFMAs of unit u of a tile into acc: the unit's K operands are all read
+  // first (one wait for shared memory per unit); Q comes from registers. The
+  // unit 0 MFMAs start from init: 0, or -inf where a key is past the
+  // prompt's keys or hidden from the row (causality), so the logit is -inf
+  // there.
+  auto mfma_unit = [&](f32x16 &acc, const uint8_t *unit, const bf16x8 (&qreg)[kSteps], int u,
+                       const f32x16 &init) {
+    bf16x8 ko[kStepsPerUnit];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      ko[j] = k_operand(unit, st0 + j);
-      qo[j] = q_operand(qs, st0 + j);
-    }
+    for (int j = 0; j < kStepsPerUnit; ++j) ko[j] = k_operand(unit, u * kStepsPerUnit + j);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ko[j], qo[j], (first && j == 0) ? init : acc,
-                                                    0, 0, 0);
+    for (int j = 0; j < kStepsPerUnit; ++j)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ko[j], qreg[u * kStepsPerUnit + j],
+                                                    (u == 0 && j == 0) ? init : acc, 0, 0, 0);
   };
   // Accumulator start of tile t: all 0 unless the tile reaches past the
   // prompt's keys (lookahead keys and the rest of the prompt's last tile).
@@ -554,31 +564,62 @@ __device__ __forceinline__ void compute_wave(const WaveCtx &c, Ring &ring, QSlot
     return v;
   };
 
-  // e slots: the accumulators of the problem in flight, then its e until
-  // folded. run: the running max over folded problems, kept as the bits of
-  // non-negative floats (they order like the values). The fold also takes
-  // the max over the heads on lane bits 4 (and 3): CL levels, after which a
-  // lane keeps 16 >> CL of its 16 keys (acc index 8 b4 + 4 b3 + k).
+  // The problem in flight accumulates its logits in ec (16 floats per lane
+  // and tile), which the statistics turn into e = 2^(x - m) <= 1. Then e is
+  // parked until the row lse of the problem is known, in 24-bit form: the
+  // top three bytes of the float after rounding to nearest (15 mantissa
+  // bits, relative error <= 2^-16), in slot x % kPk. At the end of problem x
+  // the wave folds the slot's previous occupant, problem x - kPk: p =
+  // e * 2^(m - lse), max into run, a running max per (row, key) kept as the
+  // bits of non-negative floats (they order like the values). The fold also
+  // takes the max over the heads on lane bits 4 (and 3): CL levels, after
+  // which a lane keeps 16 >> CL of its 16 keys (acc index 8 b4 + 4 b3 + k).
   constexpr int RV = 16 >> CL;
-  f32x16 e[kLag][NTA];
+  f32x16 ec[NTA];
+  uint32_t pk[kPk][NTA][12];
+  float mref[kPk];           // row max of the problem in each slot (base 2)
   uint32_t run[NTA][RV];
-  float mref[kLag];          // row max of the problem in each slot (base 2)
 #pragma unroll
   for (int t = 0; t < NTA; ++t) {
 #pragma unroll
     for (int k = 0; k < RV; ++k) run[t][k] = 0u;
 #pragma unroll
-    for (int a = 0; a < kLag; ++a) e[a][t] = f32x16{};
-  }
-  const bool b3 = (lane >> 3) & 1;
+    for (int a = 0; a < kPk; ++a)
 #pragma unroll
-  for (int a = 0; a < kLag; ++a) mref[a] = -INFINITY;
-  // Fold slot a into run with factor f (0 before the first lag problems: a
+      for (int i = 0; i < 12; ++i) pk[a][t][i] = 0u;
+  }
+#pragma unroll
+  for (int a = 0; a < kPk; ++a) mref[a] = -INFINITY;
+  const bool b3 = (lane >> 3) & 1;
+  // Four floats (a, b, c, d) -> three words [a1 a2 a3 b1] [b2 b3 c1 c2]
+  // [c3 d1 d2 d3] (byte 0 of each float dropped after rounding), and back.
+  auto park = [&](const f32x16 &v, uint32_t (&o)[12]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t w0 = __float_as_uint(v[4 * g]) + 0x80u;
+      const uint32_t w1 = __float_as_uint(v[4 * g + 1]) + 0x80u;
+      const uint32_t w2 = __float_as_uint(v[4 * g + 2]) + 0x80u;
+      const uint32_t w3 = __float_as_uint(v[4 * g + 3]) + 0x80u;
+      o[3 * g] = __builtin_amdgcn_perm(w1, w0, 0x05030201u);
+      o[3 * g + 1] = __builtin_amdgcn_perm(w2, w1, 0x06050302u);
+      o[3 * g + 2] = __builtin_amdgcn_perm(w3, w2, 0x07060503u);
+    }
+  };
+  auto unpark = [&](const uint32_t (&o)[12], int i) -> float {
+    const int g = i / 4, j = i % 4;
+    uint32_t w;
+    if (j == 0) w = __builtin_amdgcn_perm(0u, o[3 * g], 0x0201000Cu);
+    else if (j == 1) w = __builtin_amdgcn_perm(o[3 * g + 1], o[3 * g], 0x0504030Cu);
+    else if (j == 2) w = __builtin_amdgcn_perm(o[3 * g + 2], o[3 * g + 1], 0x0403020Cu);
+    else w = __builtin_amdgcn_perm(0u, o[3 * g + 2], 0x0302010Cu);
+    return __uint_as_float(w);
+  };
+  // Fold tile t of slot a into run with factor f (0 for an empty slot: a
   // no-op, since run >= 0).
   auto fold_tile = [&](int a, int t, float f) {
     uint32_t p[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] = __float_as_uint(e[a][t][i] * f);
+    for (int i = 0; i < 16; ++i) p[i] = __float_as_uint(unpark(pk[a][t], i) * f);
     if constexpr (CL >= 1) {
       // Lane bit 4 (lanes l, l ^ 16): one swap of register pairs (i, i + 8)
       // gives the lane with bit 4 clear both values of key i, the other
@@ -602,92 +643,103 @@ __device__ __forceinline__ void compute_wave(const WaveCtx &c, Ring &ring, QSlot
     for (int k = 0; k < RV; ++k) run[t][k] = __builtin_elementwise_max(run[t][k], p[k]);
   };
 
-  for (int x0 = 0; x0 < P + kLag; x0 += kLag) {
+  for (int x0 = 0; x0 < P + kPk; x0 += kPk) {
 #pragma unroll
-    for (int a = 0; a < kLag; ++a) {
-      const int x = x0 + a;            // problem computed now; x - kLag is folded
-      if (x >= P + kLag) break;
-      float fold_f = 0.f;
-      if (x >= kLag) {
-        const int xf = x - kLag;
+    for (int a = 0; a < kPk; ++a) {
+      const int x = x0 + a;            // problem computed now; x - kPk is folded after it
+      if (x >= P + kPk) break;
+      float m = -INFINITY;
+      if (x < P) {
+        __builtin_amdgcn_sched_barrier(0);
+        lds_wait_ge(&sm.q_ready, x + 1, ws, dead);
+        // Q(x)'s operands stay in registers for the problem; its slot is
+        // free again once they are read.
+        bf16x8 qreg[kSteps];
+        {
+          const uint8_t *qs = &qsl.q[x % kQSlots][0];
+#pragma unroll
+          for (int st = 0; st < kSteps; ++st) qreg[st] = q_operand(qs, st);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          if (lane == 0) lds_inc(&sm.q_used[x % kQSlots]);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const f32x16 init = tile_init(t);
+#pragma unroll
+          for (int u = 0; u < UPT; ++u) {
+            wait_unit();
+            mfma_unit(ec[t], &ring.unit[wave][kc & (kRing - 1)][0], qreg, u, init);
+            // The MFMAs above have read the unit (their operands were
+            // waited for): refill its slot.
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            ++kc;
+            issue_next();
+            __builtin_amdgcn_sched_barrier(0);   // keep the next unit's reads after the refill
+          }
+        }
+        // Row max over the wave's keys (both halves), then e = 2^(x - m) in
+        // place and the row sum (masked logits are -inf and give 0). The
+        // lookahead keys keep their e: they are never stored.
+        const float sl2 = kF8 ? s.scale_log2 * c.ks->v[x] : s.scale_log2;
+        float mt = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mt = fmaxf(mt, ec[t][i]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        m = mt * sl2;      // -inf when the wave has no key this row sees
+        const float mz = m == -INFINITY ? 0.f : m;
+        float z = 0.f;
+        // (One tile at a time: left free, the scheduler computes every
+        // tile's exponent arguments first and runs out of registers.)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float ev = __builtin_amdgcn_exp2f(__builtin_fmaf(ec[t][i], sl2, -mz));
+            z += ev;
+            ec[t][i] = ev;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        z += __shfl_xor(z, 32, 64);
+        const int rs = x % kRedSlots;
+        if (lane < 32) sm.red[rs][wave][r] = make_float2(m, z);
+        // The last wave to finish the problem posts the block's partials.
+        const int arrived =
+            __builtin_amdgcn_readfirstlane(lane == 0 ? lds_inc(&sm.stats_cnt[rs]) : 0);
+        if (arrived == kCompute * (x / kRedSlots + 1) - 1 && lane < kRows) {
+          float M = -INFINITY, Z = 0.f;
+#pragma unroll
+          for (int w = 0; w < kCompute; ++w)
+            stats_merge_lean(M, Z, sm.red[rs][w][lane].x, sm.red[rs][w][lane].y);
+          // Twice: an ordinary store that the merge block of this die reads
+          // from the die's L2, and a device-coherent one for a merge block
+          // elsewhere.
+          const int64_t at = cta_slot(x, c.cta) + lane;
+          const uint64_t word = slot_word(lse_of(M, Z), ws.call_tag);
+          ws.lslot[at] = word;
+          __hip_atomic_store(ws.slot + at, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      // Fold problem x - kPk (its lse is needed only now), then park x in
+      // its slot.
+      if (x >= kPk) {
+        const int xf = x - kPk;
         lds_wait_ge(&sm.lse_ready[xf % kLseSlots], xf + 1, ws, dead);
         const float l2 = sm.lse[xf % kLseSlots][r];
-        fold_f = (row_ok && mref[a] != -INFINITY) ? __builtin_amdgcn_exp2f(mref[a] - l2) : 0.f;
+        const float f = (row_ok && mref[a] != -INFINITY) ? __builtin_amdgcn_exp2f(mref[a] - l2) : 0.f;
         if (lane == 0) lds_inc(&sm.lse_used[xf % kLseSlots]);
-      }
-      if (x >= P) {
-        // Past the last problem: fold only.
 #pragma unroll
-        for (int t = 0; t < NT; ++t) fold_tile(a, t, fold_f);
-        continue;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      lds_wait_ge(&sm.q_ready, x + 1, ws, dead);
-      const uint8_t *qs = &qsl.q[x % kQSlots][0];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        fold_tile(a, t, fold_f);
-        __builtin_amdgcn_sched_barrier(0);
-        const f32x16 init = tile_init(t);
-#pragma unroll
-        for (int u = 0; u < UPT; ++u) {
-          wait_unit();
-          const uint8_t *unit = &ring.unit[wave][kc & (kRing - 1)][0];
-#pragma unroll
-          for (int g2 = 0; g2 < kStepsPerUnit; g2 += 2)
-            mfma2(e[a][t], unit, qs, u * kStepsPerUnit + g2, u == 0 && g2 == 0, init);
-          // The MFMAs above have read the unit (their operands were waited
-          // for): refill its slot.
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          ++kc;
-          issue_next();
-          __builtin_amdgcn_sched_barrier(0);   // keep the next unit's reads after the refill
+        for (int t = 0; t < NT; ++t) {
+          fold_tile(a, t, f);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (lane == 0) lds_inc(&sm.q_used[x % kQSlots]);
-      // Row max over the wave's keys (both halves), then e = 2^(x - m) in
-      // place and the row sum (masked logits are -inf and give 0). The
-      // lookahead keys keep their e: they are never stored.
-      const float sl2 = kF8 ? s.scale_log2 * c.ks->v[x] : s.scale_log2;
-      float mt = -INFINITY;
+      if (x < P) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, e[a][t][i]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m = mt * sl2;      // -inf when the wave has no key this row sees
-      const float mz = m == -INFINITY ? 0.f : m;
-      float z = 0.f;
-      // (One tile at a time: left free, the scheduler computes every tile's
-      // exponent arguments first and runs out of registers.)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float ev = __builtin_amdgcn_exp2f(__builtin_fmaf(e[a][t][i], sl2, -mz));
-          z += ev;
-          e[a][t][i] = ev;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      z += __shfl_xor(z, 32, 64);
-      mref[a] = m;
-      const int rs = x % kRedSlots;
-      if (lane < 32) sm.red[rs][wave][r] = make_float2(m, z);
-      // The last wave to finish the problem posts the block's partials.
-      const int arrived = __builtin_amdgcn_readfirstlane(lane == 0 ? lds_inc(&sm.stats_cnt[rs]) : 0);
-      if (arrived == kCompute * (x / kRedSlots + 1) - 1 && lane < kRows) {
-        float M = -INFINITY, Z = 0.f;
-#pragma unroll
-        for (int w = 0; w < kCompute; ++w)
-          stats_merge(M, Z, sm.red[rs][w][lane].x, sm.red[rs][w][lane].y);
-        // Twice: an ordinary store that the merge block of this die reads
-        // from the die's L2, and a device-coherent one for a merge block
-        // elsewhere.
-        const int64_t at = cta_slot(x, c.cta) + lane;
-        const uint64_t word = slot_word(lse_of(M, Z), ws.call_tag);
-        ws.lslot[at] = word;
-        __hip_atomic_store(ws.slot + at, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int t = 0; t < NT; ++t) park(ec[t], pk[a][t]);
+        mref[a] = m;
       }
     }
   }
@@ -756,14 +808,14 @@ __device__ __forceinline__ void compute_wave(const WaveCtx &c, Ring &ring, QSlot
   }
 }
 
-template <int D, bool kF8, int kLag, int CL>
+template <int D, bool kF8, int kPk, int CL>
 __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable tb,
                                                         int64_t total_keys,
                                                         const __bf16 *__restrict__ q,
                                                         const uint8_t *__restrict__ k,
                                                         float *__restrict__ imp, StreamWs ws,
                                                         KScales ks) {
-  constexpr int kTPW = tpw_for_lag(kLag);            // tiles per compute wave
+  constexpr int kTPW = tpw_for_pk(kPk);              // tiles per compute wave
   using QL = UnitLayout<128>;
   constexpr int QU = D * 2 / 128;                    // Q units per problem (1 or 2)
   static_assert(QU * kUnitBytes <= kQSlotBytes, "Q slot too small");
@@ -834,9 +886,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
               vo, 0, 0, 0);
         }
     };
-    // Problem y goes into the slot of y - 3 as soon as every compute wave
-    // has read that one; checked before every poll, so Q never waits behind
-    // a slow exchange.
+    // Problem y goes into the slot of y - 3 once every compute wave has read
+    // that one. The wave's loads complete in order, and a Q load queues
+    // behind the block's K stream (about 1.5 us), so Q loads go out between
+    // problems, never between the polls of one: right after the lse of x is
+    // staged, when every wave has finished x and the slot of Q(x + 3) is
+    // free. Only when the compute waves may run further ahead than that
+    // (lag > 2) does the poll loop top up as well.
     int q_issued = 0, q_marked = 0;
     auto top_up = [&]() {
       while (q_issued < P &&
@@ -860,7 +916,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
       const uint32_t voff = dlane * kRows * (int)sizeof(uint64_t) + (lane & 7) * 32;
       Quad v[1];
       const bool in[1] = {din};
-      top_up();
       int q_round = q_issued;
       v[0] = load_quad(rs, voff, 0);
       const uint64_t t0 = wall_clock64();
@@ -873,8 +928,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
         if (__all(ok) || dead) break;
         if (wall_clock64() - t0 > kWaitTicks) { timeout(ws, dead); break; }
         asm volatile("" ::: "memory");
-        top_up();
-        q_round = q_issued;
+        if (q_issued <= x + kPk) {    // the compute waves may need Q(x + kPk) now
+          top_up();
+          q_round = q_issued;
+        }
         if (in[0] && !quad_full(v[0], ws.call_tag)) v[0] = load_quad(rs, voff, 0);
       }
       const f32x4 lq = merge_quads(v, in);
@@ -882,6 +939,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
       lds_wait_ge(&sm.lse_used[x % kLseSlots], kCompute * (x / kLseSlots), ws, dead);
       if (lane < 8) *reinterpret_cast<f32x4 *>(&sm.lse[x % kLseSlots][4 * lane]) = lq;
       if (lane == 0) lds_set(&sm.lse_ready[x % kLseSlots], x + 1);
+      top_up();
     }
     return;
   }
@@ -918,13 +976,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
   while (full_tiles < nt && c.w_key0 + full_tiles * c.t_stride + kTile <= N) ++full_tiles;
   c.full_tiles = full_tiles;
   switch (nt) {
-    case 0: compute_wave<D, kF8, kLag, CL, 0>(c, ring, qsl, sm, dead); break;
-    case 1: compute_wave<D, kF8, kLag, CL, 1>(c, ring, qsl, sm, dead); break;
+    case 0: compute_wave<D, kF8, kPk, CL, 0>(c, ring, qsl, sm, dead); break;
+    case 1: compute_wave<D, kF8, kPk, CL, 1>(c, ring, qsl, sm, dead); break;
     case 2:
-      if constexpr (kTPW >= 2) compute_wave<D, kF8, kLag, CL, 2>(c, ring, qsl, sm, dead);
+      if constexpr (kTPW >= 2) compute_wave<D, kF8, kPk, CL, 2>(c, ring, qsl, sm, dead);
       break;
     default:
-      if constexpr (kTPW >= 3) compute_wave<D, kF8, kLag, CL, 3>(c, ring, qsl, sm, dead);
+      if constexpr (kTPW >= 3) compute_wave<D, kF8, kPk, CL, 3>(c, ring, qsl, sm, dead);
       break;
   }
 }
@@ -940,7 +998,7 @@ bool occupancy_cl(int *occ) {
   int a = 0, b = 0, c = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, k_stream<D, F8, 2, CL>, kThreads, 0) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_stream<D, F8, 4, CL>, kThreads, 0) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, k_stream<D, F8, 8, CL>, kThreads, 0) != hipSuccess)
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, k_stream<D, F8, 7, CL>, kThreads, 0) != hipSuccess)
     return false;
   *occ = std::min(*occ, std::min(a, std::min(b, c)));
   return true;
@@ -1111,24 +1169,24 @@ hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const 
   AttnShape sa = s;
   for (int li = 0; li < plan.n_launch; ++li) {
     w.call_tag = reserve_tags(1);
-    // The deepest lag whose e slots hold the tiles of the launch's busiest
-    // compute wave.
+    // The most parked problems whose slots hold the tiles of the launch's
+    // busiest compute wave.
     const int tpw = (plan.max_tiles[li] + kCompute - 1) / kCompute;
-    const int lag = lag_for_tpw(tpw);
+    const int npk = pk_for_tpw(tpw);
     // Head-max levels taken at fold time: lane bits 4 and 3 are head bits
     // for G >= 4, bit 4 for G = 2.
     const int cl = s.G >= 4 ? 2 : s.G == 2 ? 1 : 0;
     auto pick = [&](auto d_tag, auto f8_tag) {
       constexpr int Dv = decltype(d_tag)::value;
       constexpr bool F8v = decltype(f8_tag)::value;
-      auto by_lag = [&](auto cl_tag) {
+      auto by_pk = [&](auto cl_tag) {
         constexpr int C = decltype(cl_tag)::value;
-        return lag == 8 ? k_stream<Dv, F8v, 8, C> : lag == 4 ? k_stream<Dv, F8v, 4, C>
+        return npk == 7 ? k_stream<Dv, F8v, 7, C> : npk == 4 ? k_stream<Dv, F8v, 4, C>
                                                              : k_stream<Dv, F8v, 2, C>;
       };
-      return cl == 2 ? by_lag(std::integral_constant<int, 2>{})
-                     : cl == 1 ? by_lag(std::integral_constant<int, 1>{})
-                               : by_lag(std::integral_constant<int, 0>{});
+      return cl == 2 ? by_pk(std::integral_constant<int, 2>{})
+                     : cl == 1 ? by_pk(std::integral_constant<int, 1>{})
+                               : by_pk(std::integral_constant<int, 0>{});
     };
     using D64 = std::integral_constant<int, 64>;
     using D128 = std::integral_constant<int, 128>;
