@@ -952,10 +952,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
   // The prompt's keys in tiles of 32 (the last may be partial), dealt to its
   // blocks round-robin: block ci takes tiles ci, ci + n_c, ci + 2 n_c, ...
   // (within one tile of an even share), then split over the compute waves.
+  // Wave w runs on SIMD w % 4, so waves w and w + 4 share one, and SIMD 3
+  // holds only wave 3 besides the control wave. The tiles left over after
+  // an even split go to waves 3, 0, 1, 2, 4, 5, 6 in that order, which
+  // keeps the busiest SIMD's share lowest.
   const int ntiles = (NK + kTile - 1) / kTile;
   const int nt_blk = (ntiles - ci + n_c - 1) / n_c;
-  const int w_t0 = (nt_blk * wave) / kCompute;
-  const int nt = (nt_blk * (wave + 1)) / kCompute - w_t0;   // this wave's tiles (<= kTPW)
+  const int base = nt_blk / kCompute, extra = nt_blk - base * kCompute;
+  auto rank_of = [](int w) { return w == 3 ? 0 : w < 3 ? w + 1 : w; };
+  auto tiles_of = [&](int w) { return base + (rank_of(w) < extra ? 1 : 0); };
+  int w_t0 = 0;
+  for (int w = 0; w < wave; ++w) w_t0 += tiles_of(w);
+  const int nt = tiles_of(wave);   // this wave's tiles (<= kTPW)
   WaveCtx c;
   c.s = s;
   c.ws = ws;
