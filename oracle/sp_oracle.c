@@ -134,8 +134,11 @@ static void box_mean(int64_t n, const double *in, int W, double *out) {
  *
  *   imp[tok_off[b] + k] = (1/S) * sum_j max_{l, h} p[b][l][j][h][k],  k < N_b
  *
- * Parallel over (prompt, step) pairs when built with OpenMP; each pair owns
- * its own step-max row, so the result does not depend on the thread count.
+ * Parallel over (prompt, step, layer) triples when built with OpenMP; each
+ * takes its heads' max in a row of its own and merges it into the (prompt,
+ * step) row under a lock. Maxima are exact in any order and the mean over
+ * steps runs afterwards in step order, so the result does not depend on the
+ * thread count.
  * nthreads <= 0 uses the OpenMP default. Returns 0, or -1 on bad args.
  */
 int oracle_importance(int B, const int64_t *tok_off, int n_layers, int Hq,
@@ -157,20 +160,28 @@ int oracle_importance(int B, const int64_t *tok_off, int n_layers, int Hq,
   /* stepmax[b][j][k] lives at stepmax[(tok_off[b] * S) + j * N_b + k]. */
   double *stepmax = (double *)malloc(sizeof(double) * (size_t)(total_tok * S));
   if (!stepmax) return -1;
+  for (int64_t i = 0; i < total_tok * S; i++) stepmax[i] = 0.0; /* probabilities are >= 0 */
   int err = 0;
+  /* One task per (prompt, step, layer): its Hq rows, max into a private row,
+   * then max into the (prompt, step) row under that row's lock. A max is
+   * exact in any order, so the result does not depend on the thread count. */
 #ifdef _OPENMP
   if (nthreads <= 0) nthreads = omp_get_max_threads();
-#pragma omp parallel for collapse(2) schedule(dynamic) num_threads(nthreads) reduction(| : err)
+  omp_lock_t *locks = (omp_lock_t *)malloc(sizeof(omp_lock_t) * (size_t)(B * S));
+  if (!locks) { free(stepmax); return -1; }
+  for (int i = 0; i < B * S; i++) omp_init_lock(&locks[i]);
+#pragma omp parallel for collapse(3) schedule(dynamic) num_threads(nthreads) reduction(| : err)
 #endif
   for (int b = 0; b < B; b++) {
     for (int j = 0; j < S; j++) {
-      const int64_t N = tok_off[b + 1] - tok_off[b];
-      double *sm = stepmax + tok_off[b] * S + (int64_t)j * N;
-      double *p = (double *)malloc(sizeof(double) * (size_t)(N + L));
-      double *pooled = (double *)malloc(sizeof(double) * (size_t)N);
-      if (!p || !pooled) { free(p); free(pooled); err |= 1; continue; }
-      for (int64_t kk = 0; kk < N; kk++) sm[kk] = 0.0; /* probabilities are >= 0 */
       for (int l = 0; l < n_layers; l++) {
+        const int64_t N = tok_off[b + 1] - tok_off[b];
+        double *sm = stepmax + tok_off[b] * S + (int64_t)j * N;
+        double *p = (double *)malloc(sizeof(double) * (size_t)(N + L));
+        double *pooled = (double *)malloc(sizeof(double) * (size_t)N);
+        double *mine = (double *)malloc(sizeof(double) * (size_t)N);
+        if (!p || !pooled || !mine) { free(p); free(pooled); free(mine); err |= 1; continue; }
+        for (int64_t kk = 0; kk < N; kk++) mine[kk] = 0.0;
         for (int h = 0; h < Hq; h++) {
           oracle_softmax_row(B, tok_off, n_layers, Hq, Hkv, d, L, pre, scale, q, k,
                              b, l, j, h, p, k_scales);
@@ -180,13 +191,26 @@ int oracle_importance(int B, const int64_t *tok_off, int n_layers, int Hq,
             row = pooled;
           }
           for (int64_t kk = 0; kk < N; kk++)  /* prompt columns only */
-            if (row[kk] > sm[kk]) sm[kk] = row[kk];
+            if (row[kk] > mine[kk]) mine[kk] = row[kk];
         }
+#ifdef _OPENMP
+        omp_set_lock(&locks[b * S + j]);
+#endif
+        for (int64_t kk = 0; kk < N; kk++)
+          if (mine[kk] > sm[kk]) sm[kk] = mine[kk];
+#ifdef _OPENMP
+        omp_unset_lock(&locks[b * S + j]);
+#endif
+        free(p);
+        free(pooled);
+        free(mine);
       }
-      free(p);
-      free(pooled);
     }
   }
+#ifdef _OPENMP
+  for (int i = 0; i < B * S; i++) omp_destroy_lock(&locks[i]);
+  free(locks);
+#endif
   if (!err) {
     for (int b = 0; b < B; b++) {
       const int64_t N = tok_off[b + 1] - tok_off[b];

@@ -169,6 +169,16 @@ def test_importance_prompts_are_independent():
     np.testing.assert_allclose(both[12:], one, rtol=1e-15)
 
 
+def test_importance_does_not_depend_on_the_thread_count():
+    """The max over layers and heads is merged from parallel tasks; maxima
+    are exact in any order, so every thread count gives the same bits."""
+    rng = np.random.default_rng(41)
+    off, q, k = _rand_problem(rng, [40, 7, 65], 3, 4, 2, 8, 4)
+    one = oracle.importance(off, q, k, 3, 4, 2, 8, 4, 0.35, nthreads=1)
+    for n in (2, 3, 8):
+        assert np.array_equal(oracle.importance(off, q, k, 3, 4, 2, 8, 4, 0.35, nthreads=n), one)
+
+
 # ----------------------------------------------------------------------------
 # Pool-before-max: each probability row pooled before the head/layer max
 # ----------------------------------------------------------------------------
