@@ -4,10 +4,10 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "sp_internal.h"
-
-#include <atomic>
 
 namespace sp {
 
@@ -176,6 +176,62 @@ sp_status choose_kernel(const sp_attn_desc *desc, const AttnShape &s, const SegT
   return SP_OK;
 }
 
+// A validated sp_score_attention call: its shape, key tiles, fp8 scales
+// and the kernel it takes.
+struct ScoreCall {
+  AttnShape s;
+  SegTable tiles;
+  KScales ks;
+  bool use_stream = false;   // the single pass, if the plan takes the batch
+  bool must_stream = false;  // no two-pass fallback (SP_SCORE_STREAM or fp8 K)
+};
+
+sp_status prepare_score(const sp_attn_desc *desc, const sp_batch *batch, const void *q,
+                        const void *k, float *importance, ScoreCall *c) {
+  int64_t total;
+  sp_status st = check_attn(desc, &c->s);
+  if (st != SP_OK) return st;
+  if ((st = check_batch(batch, &total)) != SP_OK) return st;
+  if (!q || !k || !importance) return SP_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k)) return SP_ERR_INVALID_ARGUMENT;
+  const bool f8 = c->s.dtype == SP_DTYPE_BF16_FP8K;
+  if (f8) {
+    if (!desc->k_scales) return SP_ERR_INVALID_ARGUMENT;
+    const int P = c->s.n_layers * c->s.Hkv;
+    for (int x = 0; x < P; ++x) {
+      const float v = desc->k_scales[x];
+      if (!(v > 0.f) || !isfinite(v)) return SP_ERR_INVALID_ARGUMENT;
+      c->ks.v[x] = v;
+    }
+  }
+  c->tiles = make_table(batch, c->s.La, kTile, c->s.La);
+  c->must_stream = desc->algo == SP_SCORE_STREAM || f8;
+  return choose_kernel(desc, c->s, c->tiles, &c->use_stream);
+}
+
+// Scratch of sp_score_attention_noalloc: the scoring workspace of calls that
+// may not allocate, one copy per GPU, held until the process ends. Host code
+// uses only the device addresses hipGetSymbolAddress returns for it.
+constexpr size_t kNoAllocBytes = size_t(48) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
+// The scratch's address on the current device, taken once per device with
+// that device current (each GPU holds its own copy at its own address).
+void *scratch_on_current_device() {
+  constexpr int kMaxDevices = 64;
+  static void *addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -237,39 +293,52 @@ sp_status sp_score_plan(const sp_attn_desc *desc, const sp_batch *batch, int32_t
 sp_status sp_score_attention(const sp_attn_desc *desc, const sp_batch *batch, const void *q,
                              const void *k, float *importance, void *ws, size_t ws_bytes,
                              void *stream) {
-  AttnShape s;
-  int64_t total;
-  sp_status st = check_attn(desc, &s);
+  ScoreCall c;
+  sp_status st = prepare_score(desc, batch, q, k, importance, &c);
   if (st != SP_OK) return st;
-  if ((st = check_batch(batch, &total)) != SP_OK) return st;
-  if (!q || !k || !importance) return SP_ERR_INVALID_ARGUMENT;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(ws)) return SP_ERR_INVALID_ARGUMENT;
-  KScales ks;
-  const bool f8 = s.dtype == SP_DTYPE_BF16_FP8K;
-  if (f8) {
-    if (!desc->k_scales) return SP_ERR_INVALID_ARGUMENT;
-    const int P = s.n_layers * s.Hkv;
-    for (int x = 0; x < P; ++x) {
-      const float v = desc->k_scales[x];
-      if (!(v > 0.f) || !isfinite(v)) return SP_ERR_INVALID_ARGUMENT;
-      ks.v[x] = v;
-    }
-  }
-  const SegTable tiles = make_table(batch, s.La, kTile, s.La);
-  const int total_tiles = tiles.unit_off[tiles.B];
-  if (!ws || ws_bytes < score_ws_bytes(s, tiles)) return SP_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(ws)) return SP_ERR_INVALID_ARGUMENT;
+  if (!ws || ws_bytes < score_ws_bytes(c.s, c.tiles)) return SP_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  bool use_stream = false;
-  if ((st = choose_kernel(desc, s, tiles, &use_stream)) != SP_OK) return st;
-  if (use_stream) {
+  if (c.use_stream) {
     bool supported = false;
-    const hipError_t e = launch_score_stream(s, tiles, q, k, ks, importance, ws, hs, &supported);
+    const hipError_t e = launch_score_stream(c.s, c.tiles, q, k, c.ks, importance, ws, hs, &supported);
     if (supported) return launched(e);
-    if (desc->algo == SP_SCORE_STREAM || f8) return SP_ERR_UNSUPPORTED;
+    if (c.must_stream) return SP_ERR_UNSUPPORTED;
   }
-  char *region = reinterpret_cast<char *>(ws) + kStatusBytes + score_stream_slot_bytes(s);
-  return launched(launch_score_two_pass(s, tiles, total_tiles, q, k, importance,
+  char *region = reinterpret_cast<char *>(ws) + kStatusBytes + score_stream_slot_bytes(c.s);
+  return launched(launch_score_two_pass(c.s, c.tiles, c.tiles.unit_off[c.tiles.B], q, k, importance,
                                         reinterpret_cast<uint32_t *>(ws), region, hs));
+}
+
+sp_status sp_score_attention_noalloc(const sp_attn_desc *desc, const sp_batch *batch,
+                                     const void *q, const void *k, float *importance,
+                                     void *stream) {
+  ScoreCall c;
+  sp_status st = prepare_score(desc, batch, q, k, importance, &c);
+  if (st != SP_OK) return st;
+  // The scratch takes sp_score_attention's workspace layout (header,
+  // single-pass slots, two-pass region), so neither kernel's data lands on
+  // the other's slots; the single pass needs only the first two parts.
+  int launches = 0;
+  const bool stream_plan = c.use_stream && score_stream_plan(c.s, c.tiles, &launches, nullptr);
+  if (c.use_stream && !stream_plan && c.must_stream) return SP_ERR_UNSUPPORTED;
+  const size_t need = stream_plan ? kStatusBytes + score_stream_slot_bytes(c.s)
+                                  : score_ws_bytes(c.s, c.tiles);
+  if (need > kNoAllocBytes) return SP_ERR_WORKSPACE_TOO_SMALL;
+  char *ws = reinterpret_cast<char *>(scratch_on_current_device());
+  if (!ws) return SP_ERR_DEVICE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (stream_plan) {
+    bool supported = false;
+    const hipError_t e = launch_score_stream(c.s, c.tiles, q, k, c.ks, importance, ws, hs, &supported);
+    if (supported) return launched(e);
+    // (The plan took the batch a moment ago; should it not now, the two
+    // passes run only if their region fits too.)
+    if (c.must_stream || score_ws_bytes(c.s, c.tiles) > kNoAllocBytes) return SP_ERR_UNSUPPORTED;
+  }
+  return launched(launch_score_two_pass(c.s, c.tiles, c.tiles.unit_off[c.tiles.B], q, k, importance,
+                                        reinterpret_cast<uint32_t *>(ws),
+                                        ws + kStatusBytes + score_stream_slot_bytes(c.s), hs));
 }
 
 sp_status sp_score_status(const void *ws, int32_t *status_host, void *stream) {

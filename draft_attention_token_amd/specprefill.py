@@ -38,7 +38,7 @@ EXPORTED = [
     "sp_select_workspace_bytes", "sp_gather_workspace_bytes", "sp_score_attention",
     "sp_pool_chunk", "sp_select_chunks", "sp_gather_kept", "sp_score_status", "sp_break_even",
     "sp_window_plan", "sp_stitch_windows", "sp_select_legacy_workspace_bytes", "sp_select_legacy",
-    "sp_score_plan",
+    "sp_score_plan", "sp_score_attention_noalloc",
 ]
 
 _ALGOS = {"auto": SP_SCORE_AUTO, "two_pass": SP_SCORE_TWO_PASS, "stream": SP_SCORE_STREAM}
@@ -97,6 +97,7 @@ def lib():
                                        vp, vp, sz, vp]
         L.sp_gather_kept.argtypes = [bp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sp_score_status.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
+        L.sp_score_attention_noalloc.argtypes = [ctypes.POINTER(sp_attn_desc), bp, vp, vp, vp, vp]
         L.sp_score_plan.argtypes = [ctypes.POINTER(sp_attn_desc), bp, ctypes.POINTER(ctypes.c_int32),
                                     ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
         L.sp_break_even.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
@@ -253,6 +254,21 @@ def sp_score_attention(q: torch.Tensor, k: torch.Tensor, offsets, n_layers: int,
         ws = _ws(score_workspace_bytes(desc, batch), dev)
     _check(lib().sp_score_attention(ctypes.byref(desc), batch.ref(), _ptr(q), _ptr(k), _ptr(out),
                                     _ptr(ws), ws.numel(), _stream(dev)), "sp_score_attention")
+    return out
+
+
+def sp_score_attention_noalloc(q: torch.Tensor, k: torch.Tensor, batch: "Batch",
+                               desc: sp_attn_desc, out: torch.Tensor) -> torch.Tensor:
+    """sp_score_attention_noalloc: the same call with the library's own
+    scratch as workspace; allocates nothing (out is the caller's [sum N_b]
+    fp32 tensor; desc from attn_desc)."""
+    if not (q.is_contiguous() and k.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q, k and out must be contiguous")
+    if out.dtype != torch.float32 or out.numel() != batch.total:
+        raise ValueError("out must be fp32 with one value per prompt token")
+    _check(lib().sp_score_attention_noalloc(ctypes.byref(desc), batch.ref(), _ptr(q), _ptr(k),
+                                            _ptr(out), _stream(q.device)),
+           "sp_score_attention_noalloc")
     return out
 
 

@@ -185,6 +185,25 @@ sp_status sp_score_attention(const sp_attn_desc *desc, const sp_batch *batch, co
                              const void *k, float *importance, void *ws, size_t ws_bytes,
                              void *stream);
 
+/* sp_score_attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, kernels and results; the
+ * workspace is instead a 48 MiB scratch array inside the library, one copy
+ * per GPU, held until the process ends. The call allocates nothing.
+ *   Returns SP_ERR_WORKSPACE_TOO_SMALL if the call needs more than 48 MiB:
+ *   the single pass needs 256 B + 384 KiB per (layer, KV head) pair (up to
+ *   127 pairs); the two-pass kernels (short batches under
+ *   SP_SCORE_AUTO, SP_SCORE_TWO_PASS, pool-before-max) need
+ *   sp_score_workspace_bytes(). SP_ERR_DEVICE if the scratch's address
+ *   cannot be read on the current device.
+ *   Every call on a GPU shares that GPU's scratch and finds it as the last
+ *   call left it (nothing in it needs clearing): calls that overlap in time
+ *   on one GPU, on any streams, race. Timed-out waits (see
+ *   sp_score_status) are not reported for this variant. */
+sp_status sp_score_attention_noalloc(const sp_attn_desc *desc, const sp_batch *batch,
+                                     const void *q, const void *k, float *importance,
+                                     void *stream);
+
 /* What sp_score_attention would run for this descriptor and batch on the
  * current device, without running it: *kernel = SP_SCORE_STREAM (the
  * single pass) or SP_SCORE_TWO_PASS, by the same rule the call applies;
