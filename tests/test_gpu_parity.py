@@ -175,6 +175,23 @@ def test_all_zero_queries_give_equal_chunk_scores():
 
 
 @pytest.mark.parametrize("algo", ["auto", "stream"])
+def test_flat_scores_normalise_to_one_then_boost(algo):
+    """All-zero queries give every prompt token the same importance: the
+    scores carry no signal, so normalisation makes each 1.0 before the boosts
+    (first 64 tokens x1.5, last 128 x1.3), as in the oracle."""
+    w = workloads.small_workload("n3212_bf16", lengths=(900,), normalize=True, boost=True)
+    inp = workloads.make_inputs(w)
+    inp.q.zero_()
+    want = np.ones(900)
+    want[:64] *= 1.5
+    want[-128:] *= 1.3
+    for mode, param in (("top_p", 0.3), ("mass", 0.85)):
+        pipe = run_gpu(inp, mode, param, algo)
+        np.testing.assert_allclose(pipe.token_scores.cpu().numpy(), want, rtol=1e-6)
+        compare(inp, pipe, mode, param, ora=oracle.pipeline(inp, mode, param))
+
+
+@pytest.mark.parametrize("algo", ["auto", "stream"])
 def test_results_are_bitwise_deterministic(algo):
     w = workloads.small_workload("n3212_bf16", lengths=(2000, 3000), seed=9)
     inp = workloads.make_inputs(w)
@@ -342,11 +359,37 @@ def test_full_size_single_prompt(name):
             assert keep[c] == 1 or st < floor, f"planted chunk {c} dropped"
 
 
+@pytest.mark.parametrize("name", ["n160k_bf16", "n160k_fp8k"])
+def test_single_pass_at_163840_tokens(name):
+    """The longest prompt one single-pass launch takes (5121 tiles over 248
+    blocks of at most 21): the plan must keep it in one launch of the single
+    pass, and its results must match the oracle's."""
+    w = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(w)
+    desc = sp.attn_desc(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_lookahead, w.dtype,
+                        k_dtype=inp.k.dtype, k_scales=inp.k_scales)
+    plan = sp.score_plan(desc, sp.Batch(inp.offsets))
+    assert plan.kernel == "stream" and plan.n_launches == 1, plan
+    imp = oracle.importance(inp.offsets.numpy(), inp.q, inp.k, w.n_layers, w.n_q_heads,
+                            w.n_kv_heads, w.head_dim, w.n_lookahead, inp.scale,
+                            k_scales=inp.k_scales)
+    for mode, param in (w.select,) + tuple(w.also_select):
+        pipe = run_gpu(inp, mode, param)
+        ora = oracle.pipeline(inp, mode, param, imp=imp)
+        excused, _ = compare(inp, pipe, mode, param, ora=ora)
+        print(f"[gpu] {name} {mode}: excused differing chunks = {excused}", flush=True)
+        keep = pipe.keep.cpu().numpy()
+        for c in inp.spans[0]:
+            assert keep[c] == 1, f"planted chunk {c} dropped"
+
+
 @pytest.mark.parametrize("n", [70000, 9000])
 def test_fold_lag_forms(n):
-    """The single-pass kernel folds 2, 3 or 6 problems behind, by how many
-    tiles its blocks own: 70000 tokens over 248 blocks give 9 tiles per block
-    (lag 3), 9000 tokens 2 (lag 6); the 128K prompts above run at lag 2."""
+    """The single-pass kernel keeps 3, 4 or 7 problems parked, by how many
+    tiles its compute waves own: 70000 tokens over 248 blocks give 9 tiles
+    per block, at most 2 per wave (4 parked), 9000 tokens 2 per block, at
+    most 1 per wave (7 parked); the 128K prompts above own up to 3 (3
+    parked)."""
     w = workloads.small_workload("n32k_bf16", lengths=(n,), n_spans=8)
     inp = workloads.make_inputs(w)
     mode, param = w.select

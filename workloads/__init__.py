@@ -103,6 +103,14 @@ WORKLOADS = {
     # Same prompt length with no planted spans (diffuse attention).
     "n128k_diffuse_bf16": Workload("n128k_diffuse_bf16", (131072,), 6, 16, 4,
                                    128, 8, torch.bfloat16, 1014, 0, None),
+    # A 163840-token prompt (the ~150K-token contexts the PR discussion runs),
+    # 80 spans of varied strength: the longest single prompt the single-pass
+    # kernel takes in one launch (248 blocks x 21 tiles of 32 keys).
+    "n160k_bf16": Workload("n160k_bf16", (163840,), 6, 16, 4, 128, 8,
+                           torch.bfloat16, 1016, 80, None,
+                           also_select=(("top_p", 0.15),)),
+    "n160k_fp8k": Workload("n160k_fp8k", (163840,), 6, 16, 4, 128, 8,
+                           torch.bfloat16, 1016, 80, None, k_fp8=True),
     # Ragged batch: 16 prompts, log-uniform lengths in [2048, 65536].
     "ragged16_bf16": Workload("ragged16_bf16", None, 8, 32, 8, 128, 8,
                               torch.bfloat16, 1500, None, None,
