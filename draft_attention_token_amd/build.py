@@ -74,5 +74,51 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer: every flag after
+# -Xarch_host, so only the host half of each HIP source is instrumented (the
+# device code is built as usual).
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+            "-Xarch_host", "-g"]
+
+
+def build_sanitized(out_dir: str) -> str:
+    """libspecprefill.so with its host code built under ASan + UBSan, into
+    out_dir (for the host-side checks; load it with the ASan runtime
+    preloaded, see sanitizer_runtime())."""
+    objdir = os.path.join(out_dir, "obj")
+    os.makedirs(objdir, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+    def one(src):
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        r = subprocess.run([_hipcc(), *FLAGS, *SANITIZE, "-c", src, "-o", obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}{r.stderr}")
+        return obj
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(one, srcs))
+    out = os.path.join(out_dir, "libspecprefill.so")
+    r = subprocess.run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libsan",
+                        "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                        *objs, "-o", out], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("sanitized link failed:\n" + r.stdout + r.stderr)
+    return out
+
+
+def sanitizer_runtime() -> str:
+    """Path of the ASan shared runtime of hipcc's clang (it carries UBSan's
+    handlers too)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(_hipcc())), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                       text=True, check=True)
+    return r.stdout.strip()
+
+
 if __name__ == "__main__":
     build(verbose=True)

@@ -240,19 +240,25 @@ hipError_t launch_legacy(const LegacyTable &t, const float *chunk_scores, const 
 int legacy_write_blocks(int n) { return (n + kListThreads - 1) / kListThreads; }
 
 LegacyWs legacy_ws(int B, int total_chunks, void *base) {
-  LegacyWs w;
-  char *p = reinterpret_cast<char *>(base);
-  w.in = reinterpret_cast<uint8_t *>(p);
-  p += align_up((size_t)total_chunks);
-  w.kept_before = reinterpret_cast<int32_t *>(p);
-  p += align_up(sizeof(int32_t) * (size_t)total_chunks);
-  w.rest_before = reinterpret_cast<int32_t *>(p);
-  p += align_up(sizeof(int32_t) * (size_t)total_chunks);
-  w.counts = reinterpret_cast<int32_t *>(p);
-  p += align_up(sizeof(int32_t) * (size_t)B);
-  w.stats = reinterpret_cast<int32_t *>(p);
-  p += align_up(2 * sizeof(int32_t) * (size_t)B);
-  w.bytes = (size_t)(p - reinterpret_cast<char *>(base));
+  // Offsets first, as integers; pointers only from a real base (a null base
+  // asks for the size alone).
+  size_t off[6];
+  off[0] = 0;
+  off[1] = off[0] + align_up((size_t)total_chunks);
+  off[2] = off[1] + align_up(sizeof(int32_t) * (size_t)total_chunks);
+  off[3] = off[2] + align_up(sizeof(int32_t) * (size_t)total_chunks);
+  off[4] = off[3] + align_up(sizeof(int32_t) * (size_t)B);
+  off[5] = off[4] + align_up(2 * sizeof(int32_t) * (size_t)B);
+  LegacyWs w = {};
+  w.bytes = off[5];
+  if (base) {
+    char *p = reinterpret_cast<char *>(base);
+    w.in = reinterpret_cast<uint8_t *>(p + off[0]);
+    w.kept_before = reinterpret_cast<int32_t *>(p + off[1]);
+    w.rest_before = reinterpret_cast<int32_t *>(p + off[2]);
+    w.counts = reinterpret_cast<int32_t *>(p + off[3]);
+    w.stats = reinterpret_cast<int32_t *>(p + off[4]);
+  }
   return w;
 }
 

@@ -25,7 +25,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libspecprefill.so")
+# SP_LIB_PATH names another build of the library (the host-sanitizer checks
+# load one); by default the in-tree build.
+LIB_PATH = os.environ.get("SP_LIB_PATH") or os.path.join(_HERE, "libspecprefill.so")
 
 SP_OK, SP_ERR_INVALID_ARGUMENT, SP_ERR_UNSUPPORTED, SP_ERR_WORKSPACE_TOO_SMALL, SP_ERR_DEVICE = range(5)
 SP_DTYPE_F32, SP_DTYPE_BF16, SP_DTYPE_BF16_FP8K = 0, 1, 2
