@@ -57,9 +57,10 @@
 // Slots carry the tag of the call that posted them, next to the value, so a
 // waiting block only takes values of its own call: nothing needs clearing
 // between calls, and a call that gave up leaves nothing that a later call
-// could mistake for its own. Every wait is bounded (about 2 s); on time-out
-// the kernel records it in the workspace header and runs to completion, so
-// the grid always drains.
+// could mistake for its own. Every wait is bounded (2 s unless the host sets
+// another budget); on time-out the kernel records it in the workspace header
+// and runs to completion, so the grid always drains.
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -82,7 +83,6 @@ constexpr int kLseSlots = 8;                      // staged row lse (>= the deep
 constexpr int kRedSlots = 4;                      // per-wave statistics of problems in flight
 constexpr int kMaxTPW = 3;                        // tiles per compute wave
 constexpr int kTilesPerCta = kCompute * kMaxTPW;  // 21
-constexpr uint64_t kWaitTicks = 200000000ull;     // wall clock runs at 100 MHz: 2 s
 constexpr int kDies = 8;                          // XCDs; block c runs on die c % 8
 constexpr int kMaxCtas = 256;                     // blocks per launch (one per CU)
 constexpr int kMaxStream = kMaxCtas - kDies;      // streaming blocks per launch
@@ -108,6 +108,7 @@ struct StreamWs {
   uint64_t *lslot;  // ordinary-store copy (kept in the die's L2)
   uint64_t *dslot;
   uint32_t call_tag;
+  uint64_t wait_ticks;   // budget of each cross-block wait (wall clock, 100 MHz)
 };
 
 __host__ __device__ constexpr int64_t cta_slot(int x, int cta) {
@@ -167,7 +168,7 @@ __device__ __forceinline__ void lds_wait_ge(const int *p, int v, const StreamWs 
   if (dead || lds_get(p) >= v) return;
   const uint64_t t0 = wall_clock64();
   while (lds_get(p) < v) {
-    if (wall_clock64() - t0 > kWaitTicks) {
+    if (wall_clock64() - t0 > ws.wait_ticks) {
       timeout(ws, dead);
       break;
     }
@@ -331,7 +332,7 @@ __device__ f32x4 gather_group(const StreamWs &ws, int x, const Group &g, int lan
 #pragma unroll
     for (int u = 0; u < kPer; ++u) ok &= !in[u] | quad_full(v[u], ws.call_tag);
     if (__all(ok) || dead) break;
-    if (wall_clock64() - t0 > kWaitTicks) { timeout(ws, dead); break; }
+    if (wall_clock64() - t0 > ws.wait_ticks) { timeout(ws, dead); break; }
     asm volatile("" ::: "memory");   // the slots change behind the compiler's back: reload
     const bool far = (round & 7) == 0;
 #pragma unroll
@@ -930,7 +931,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
           q_marked = q_round;
         }
         if (__all(ok) || dead) break;
-        if (wall_clock64() - t0 > kWaitTicks) { timeout(ws, dead); break; }
+        if (wall_clock64() - t0 > ws.wait_ticks) { timeout(ws, dead); break; }
         asm volatile("" ::: "memory");
         if (q_issued <= x + kPk) {    // the compute waves may need Q(x + kPk) now
           top_up();
@@ -1160,6 +1161,18 @@ bool score_stream_plan(const AttnShape &s, const SegTable &tiles, int *n_launche
   return true;
 }
 
+// Budget of each cross-block wait in wall-clock ticks (100 MHz): 2 s, or
+// SP_SCORE_WAIT_US microseconds when that is set (up to about 3 hours).
+uint64_t score_wait_ticks() {
+  const char *e = getenv("SP_SCORE_WAIT_US");
+  if (e && *e) {
+    char *end = nullptr;
+    const unsigned long long us = strtoull(e, &end, 10);
+    if (end && *end == '\0') return std::min(us, 10000000000ull) * 100ull;
+  }
+  return 200000000ull;
+}
+
 hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const void *q,
                                const void *k, const KScales &ks, float *imp, void *ws,
                                hipStream_t st, bool *supported) {
@@ -1174,6 +1187,7 @@ hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const 
   w.slot = reinterpret_cast<uint64_t *>(base);
   w.lslot = reinterpret_cast<uint64_t *>(base + cta_region(s));
   w.dslot = reinterpret_cast<uint64_t *>(base + 2 * cta_region(s));
+  w.wait_ticks = score_wait_ticks();
   const int64_t total_keys = (int64_t)tiles.tok_off[tiles.B] + (int64_t)tiles.B * tiles.L;
   const __bf16 *qp = reinterpret_cast<const __bf16 *>(q);
   const uint8_t *kp = reinterpret_cast<const uint8_t *>(k);

@@ -465,7 +465,10 @@ class Pipeline:
     def score_status(self) -> int:
         return score_status(self.ws_score)
 
-    def run(self, q: torch.Tensor, k: torch.Tensor, token_ids: torch.Tensor):
+    def run(self, q: torch.Tensor, k: torch.Tensor, token_ids: torch.Tensor, check: bool = False):
+        """The four calls on the pipeline's stream. check=True waits for them
+        and raises if a cross-block wait of the scoring kernel timed out (the
+        results are then invalid)."""
         L = lib()
         st = _stream(self.device)
         b = self.batch.ref()
@@ -483,6 +486,8 @@ class Pipeline:
                                 _ptr(self.kept_pos), _ptr(self.kept_offsets),
                                 _ptr(self.ws_gather), self.ws_gather.numel(), st),
                "sp_gather_kept")
+        if check and self.score_status() != 0:
+            raise SpError(SP_ERR_DEVICE, "sp_score_attention (a cross-block wait timed out)")
 
 
 class ToolPipeline:
@@ -521,8 +526,9 @@ class ToolPipeline:
     def score_status(self) -> int:
         return score_status(self.ws_score)
 
-    def run(self, q: torch.Tensor, k: torch.Tensor, token_ids: torch.Tensor):
-        """q, k: the window batch's Q and K; token_ids: [n_tokens] of the prompt."""
+    def run(self, q: torch.Tensor, k: torch.Tensor, token_ids: torch.Tensor, check: bool = False):
+        """q, k: the window batch's Q and K; token_ids: [n_tokens] of the prompt.
+        check=True waits and raises if a scoring wait timed out."""
         L = lib()
         st = _stream(self.device)
         _check(L.sp_score_attention(ctypes.byref(self.adesc), self.windows.ref(), _ptr(q), _ptr(k),
@@ -539,3 +545,5 @@ class ToolPipeline:
                                   _ptr(token_ids), _ptr(self.kept_ids), _ptr(self.kept_pos),
                                   _ptr(self.kept_offsets), _ptr(self.ws_legacy),
                                   self.ws_legacy.numel(), st), "sp_select_legacy")
+        if check and self.score_status() != 0:
+            raise SpError(SP_ERR_DEVICE, "sp_score_attention (a cross-block wait timed out)")

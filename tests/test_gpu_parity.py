@@ -2,9 +2,11 @@
 
 Small shapes cover several tiles, ragged tails, every supported dtype /
 head size / group size, both scoring kernels and the batch edge cases; the
-named workloads run at their full sizes (the ragged batch compares a sample
-of its prompts end to end, the rest through properties).
+named workloads run at their full sizes (the ragged batch compares every
+prompt of every scoring launch end to end).
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -189,6 +191,51 @@ def test_flat_scores_normalise_to_one_then_boost(algo):
         pipe = run_gpu(inp, mode, param, algo)
         np.testing.assert_allclose(pipe.token_scores.cpu().numpy(), want, rtol=1e-6)
         compare(inp, pipe, mode, param, ora=oracle.pipeline(inp, mode, param))
+
+
+def test_timed_out_call_leaves_the_workspace_usable(monkeypatch):
+    """A zero wait budget (SP_SCORE_WAIT_US=0, read by the host at launch)
+    makes every cross-block wait of the single pass give up at once: the
+    kernels still drain, the call reports the time-out and a checked
+    pipeline raises. The next call on the same workspace with the normal
+    budget succeeds and matches a call on a fresh workspace, bit for bit:
+    slots carry the tag of the call that wrote them, so nothing the failed
+    call left behind is taken for a result."""
+    w = workloads.small_workload("n32k_bf16", lengths=(20000,), n_spans=4)
+    inp = workloads.make_inputs(w)
+    q, k = inp.q.to(DEV), inp.k.to(DEV)
+    batch = sp.Batch(inp.offsets)
+    desc = sp.attn_desc(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_lookahead, w.dtype,
+                        algo="stream")
+    nbytes = sp.score_workspace_bytes(desc, batch)
+    ws, fresh = sp._ws(nbytes, DEV), sp._ws(nbytes, DEV)
+    st = ctypes.c_void_p(torch.cuda.current_stream(DEV).cuda_stream)
+
+    def call(wsx):
+        out = torch.full((batch.total,), float("nan"), dtype=torch.float32, device=DEV)
+        rc = sp.lib().sp_score_attention(ctypes.byref(desc), batch.ref(),
+                                         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                         ctypes.c_void_p(out.data_ptr()),
+                                         ctypes.c_void_p(wsx.data_ptr()), wsx.numel(), st)
+        assert rc == sp.SP_OK, sp.status_string(rc)
+        torch.cuda.synchronize()
+        return out
+
+    monkeypatch.setenv("SP_SCORE_WAIT_US", "0")
+    print("[gpu] scoring with a zero wait budget", flush=True)
+    call(ws)
+    assert sp.score_status(ws) == 1
+    pipe = sp.Pipeline(inp.offsets, w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                       w.n_lookahead, w.dtype, DEV, algo="stream")
+    with pytest.raises(sp.SpError):
+        pipe.run(q, k, inp.token_ids.to(DEV), check=True)
+    monkeypatch.delenv("SP_SCORE_WAIT_US")
+    again = call(ws)
+    assert sp.score_status(ws) == 0
+    ref = call(fresh)
+    assert sp.score_status(fresh) == 0
+    assert torch.equal(again, ref)
+    pipe.run(q, k, inp.token_ids.to(DEV), check=True)
 
 
 @pytest.mark.parametrize("algo", ["auto", "stream"])
