@@ -23,7 +23,8 @@
 // exact integer arithmetic, independent of the order of the additions, and
 // the sum ahead of a chunk grows along the order. The order compares the
 // top 32 bits of the fixed-point value (two scores closer than 2^-32 of the
-// largest tie and go by index; both then sit at the selection boundary).
+// largest tie and go by index; both then sit at the selection boundary),
+// as one 64-bit key with the chunk index below them.
 #include "sp_internal.h"
 
 namespace sp {
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectTable t, double param
                                                      const float *__restrict__ cs,
                                                      uint8_t *__restrict__ keep,
                                                      int32_t *__restrict__ n_kept) {
-  __shared__ __align__(16) uint32_t skey[kStage];
+  __shared__ __align__(16) unsigned long long skey[kStage];
   __shared__ __align__(16) long long sfx[kMass ? kStage : 2];
   __shared__ uint32_t rc[kWaves][kRankTile];
   __shared__ long long rs[kWaves][kRankTile];
@@ -124,7 +125,9 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectTable t, double param
 
   const int grp = wave * (64 / kRankTile) + (lane / kRankTile);
   const long long fxi = mine ? to_fixed(c_i, shift) : 0ll;
-  const uint32_t ki = order_key(fxi);
+  // The order as one 64-bit key: score key on top, chunk index below, so
+  // "ahead of i" is a single unsigned comparison (equal scores by index).
+  const unsigned long long ki = ((unsigned long long)order_key(fxi) << 32) | (uint32_t)i;
   uint32_t n = 0;
   long long sum = 0;
   // Every chunk except the final one, in LDS-sized stages; lane group g
@@ -142,15 +145,17 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectTable t, double param
       for (int r = 0; r < kPerThread; ++r) v = r == ej ? sc[r] : v;
       const bool in = j < len;
       const long long fx = in ? to_fixed(v, shift) : 0ll;
-      skey[j] = in ? order_key(fx) : 0xffffffffu;   // padding is never ahead
+      skey[j] = in ? ((unsigned long long)order_key(fx) << 32) | (uint32_t)(j0 + j)
+                   : ~0ull;   // padding is never ahead
       if (kMass) sfx[j] = fx;
     }
     __syncthreads();
     const int per = (len + 4 * kGroups - 1) / (4 * kGroups) * 4;
     const int a = grp * per;
     for (int j = a; j < a + per; j += 4) {
-      const uint4 k4 = *reinterpret_cast<const uint4 *>(&skey[j]);
-      const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
+      const ulonglong2 k01 = *reinterpret_cast<const ulonglong2 *>(&skey[j]);
+      const ulonglong2 k23 = *reinterpret_cast<const ulonglong2 *>(&skey[j + 2]);
+      const unsigned long long kk[4] = {k01.x, k01.y, k23.x, k23.y};
       long long f[4] = {0, 0, 0, 0};
       if (kMass) {
         const longlong2 f01 = *reinterpret_cast<const longlong2 *>(&sfx[j]);
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectTable t, double param
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bool ahead = kk[u] < ki || (kk[u] == ki && j0 + j + u < i);
+        const bool ahead = kk[u] < ki;
         n += ahead ? 1u : 0u;
         if (kMass) sum += ahead ? f[u] : 0ll;
       }
