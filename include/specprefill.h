@@ -166,20 +166,22 @@ sp_status sp_gather_workspace_bytes(const sp_batch *batch, int32_t chunk_size, s
  *       key rows start at token_offsets[b] + b * L: its N_b prompt keys, then
  *       its L lookahead keys.
  *   importance: [sum_b N_b] fp32 out.
- *   ws: device workspace of at least sp_score_workspace_bytes() bytes. It
- *       carries state from call to call: zero-fill all of it once before its
- *       first use (e.g. hipMemsetAsync) and leave it alone between calls.
- *       Each call leaves it ready for the next one with the same n_layers and
- *       n_kv_heads, whatever the batch or algorithm. Calls that share a
- *       workspace must not overlap in time.
+ *   ws: device workspace of at least sp_score_workspace_bytes() bytes. Zero-fill
+ *       it once before its first use (e.g. hipMemsetAsync) and leave it alone
+ *       between calls; it then serves any sequence of calls with the same
+ *       n_layers and n_kv_heads, whatever the batch or algorithm. Calls that
+ *       share a workspace must not overlap in time.
  *   The single-pass kernel runs one block per compute unit and needs all of
- *   them resident together. Blocks exchange partial results through the
- *   workspace; every launch empties again each slot it used, so nothing
- *   needs clearing between calls.
- *   A block waits at most about 2 s for another one, then finishes without
- *   hanging the device and marks the call as failed (importance is then not
- *   valid); sp_score_status() reports it. Only other work that keeps compute
- *   units busy that long can cause this.
+ *   them resident together; the call checks the device's compute units
+ *   before launching, and no other work should hold them meanwhile. Blocks
+ *   exchange partial results through the workspace in slots that carry the
+ *   posting call's tag, so nothing needs clearing between calls and a failed
+ *   call leaves nothing a later one could take for its own.
+ *   A block waits at most 2 s for another one (the SP_SCORE_WAIT_US
+ *   environment variable, read at each call, sets another budget in
+ *   microseconds), then finishes without hanging the device and marks the
+ *   call as failed (importance is then not valid); sp_score_status()
+ *   reports it. The workspace stays usable for the next call.
  */
 sp_status sp_score_attention(const sp_attn_desc *desc, const sp_batch *batch, const void *q,
                              const void *k, float *importance, void *ws, size_t ws_bytes,
