@@ -306,23 +306,30 @@ def main():
     # Scoring stage alone, same stream, same inputs: one pair of events around
     # each launch (the scoring call is one kernel launch per batch of up to
     # 256 blocks' worth of prompts), averaged.
-    import ctypes
-    L = sp.lib()
-    st = ctypes.c_void_p(stream.cuda_stream)
-    adesc = pipe.adesc
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     for a, b in ev:
         a.record(stream)
-        rc = L.sp_score_attention(ctypes.byref(adesc), pipe.batch.ref(), ctypes.c_void_p(q.data_ptr()),
-                                  ctypes.c_void_p(k.data_ptr()),
-                                  ctypes.c_void_p(pipe.importance.data_ptr()),
-                                  ctypes.c_void_p(pipe.ws_score.data_ptr()), pipe.ws_score.numel(), st)
-        assert rc == 0, sp.status_string(rc)
+        pipe.run_score(q, k)
         b.record(stream)
     torch.cuda.synchronize()
     assert pipe.score_status() == 0, "scoring kernel reported a timed-out wait"
     ms_score = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    # The stages after scoring alone, the same way.
+    for a, b in ev:
+        a.record(stream)
+        pipe.run_post(ids)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms_post = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    if tool:
+        post_form = "sp_stitch_windows + sp_pool_chunk + sp_select_legacy"
+    else:
+        assert pipe.post_status() == 0, "post-scoring launch reported a timed-out wait"
+        tb = sp.post_plan(pipe.pdesc, pipe.batch)
+        post_form = (f"sp_pool_select_gather: one launch, {tb}-token blocks" if tb
+                     else "sp_pool_select_gather: separate pool, select and gather kernels")
+    log(f"after scoring: {ms_post * 1e3:.1f} us ({post_form})")
     alg_bytes = score_algorithmic_bytes(inp)
     achieved = alg_bytes / (ms_score * 1e-3) / 1e9
     log(f"scoring {ms_score * 1e3:.1f} us per launch -> {achieved:.0f} GB/s algorithmic")
@@ -359,6 +366,7 @@ def main():
                    **({"window": w.window, "stride": w.stride, "windows": len(inp.lengths),
                        "window_tokens": int(inp.offsets[-1]), "max_keep": w.max_keep}
                       if tool else {})},
+        "stages": {"score_us": ms_score * 1e3, "post_us": ms_post * 1e3, "post": post_form},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": kernel_name,

@@ -150,6 +150,60 @@ sp_status check_chunks(const sp_batch *batch, int32_t C, int *max_nc) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+bool check_select_args(int32_t mode, double param) {
+  return (mode == SP_SELECT_TOP_P || mode == SP_SELECT_MASS) && param > 0.0 && param <= 1.0;
+}
+
+// Selection tables: chunk prefix, rank-kernel blocks and the top-p budget
+// kc = clamp(ceil(p * nc), 1, nc) of each prompt.
+SelectTable make_select_table(const SegTable &chunks, double param) {
+  SelectTable t;
+  memset(&t, 0, sizeof(t));
+  t.B = chunks.B;
+  for (int b = 0; b < chunks.B; ++b) {
+    const int nc = chunks.unit_off[b + 1] - chunks.unit_off[b];
+    t.chunk_off[b + 1] = chunks.unit_off[b + 1];
+    t.blk_off[b + 1] = t.blk_off[b] + select_rank_blocks(nc);
+    int64_t v = (int64_t)ceil(param * (double)nc - 1e-9);
+    if (v > nc) v = nc;
+    if (v < 1) v = 1;
+    t.kc[b] = (int32_t)v;
+  }
+  return t;
+}
+
+// Tokens per block of the fused post-scoring launch: the smallest multiple of
+// the pool group (pool_block_tokens(C); at most kPostMaxTB tokens and
+// kPostMaxChunks chunks) whose blocks number at most max_blocks, with at
+// most kPostMaxGroups groups in a prompt; 0 when there is none.
+int post_block_tokens(const sp_batch *batch, int C, int max_blocks) {
+  const int GT = pool_block_tokens(C);
+  for (int b = 0; b < batch->n_prompts; ++b)
+    if ((batch->token_offsets[b + 1] - batch->token_offsets[b] + GT - 1) / GT > kPostMaxGroups)
+      return 0;
+  const int64_t total = batch->token_offsets[batch->n_prompts];
+  int per = (int)std::max<int64_t>(1, total / ((int64_t)std::max(1, max_blocks) * GT));
+  for (; (int64_t)per * GT <= kPostMaxTB && (int64_t)per * GT / C <= kPostMaxChunks; ++per) {
+    const int64_t TB = (int64_t)per * GT;
+    int64_t G = 0;
+    for (int b = 0; b < batch->n_prompts; ++b)
+      G += (batch->token_offsets[b + 1] - batch->token_offsets[b] + TB - 1) / TB;
+    if (G <= max_blocks) return (int)TB;
+  }
+  return 0;
+}
+
+// Workspace of sp_pool_select_gather: the status header, then either the
+// fused launch's slots or the separate kernels' workspaces (pool, gather).
+size_t post_split_bytes(const PoolTable &pt, const SegTable &chunks) {
+  return align_up(pool_ws(pt.B, pt.blk_off[pt.B])) + gather_ws(chunks.B, chunks.unit_off[chunks.B]);
+}
+size_t post_ws_bytes(const PoolTable &pt, const SegTable &chunks) {
+  // The pool table's blocks are the pool groups.
+  return kStatusBytes + std::max(post_slot_bytes(chunks.unit_off[chunks.B], pt.blk_off[pt.B]),
+                                 post_split_bytes(pt, chunks));
+}
+
 // Scoring workspace: header, single-pass slots, two-pass region (one layout
 // for every algorithm, so calls with different algorithms can share it).
 size_t score_ws_bytes(const AttnShape &s, const SegTable &tiles) {
@@ -400,8 +454,7 @@ sp_status sp_select_chunks(int32_t mode, double param, const sp_batch *batch, in
                            void *ws, size_t ws_bytes, void *stream) {
   int64_t total;
   int max_nc;
-  if (mode != SP_SELECT_TOP_P && mode != SP_SELECT_MASS) return SP_ERR_INVALID_ARGUMENT;
-  if (!(param > 0.0) || !(param <= 1.0)) return SP_ERR_INVALID_ARGUMENT;
+  if (!check_select_args(mode, param)) return SP_ERR_INVALID_ARGUMENT;
   sp_status st = check_batch(batch, &total);
   if (st != SP_OK) return st;
   if ((st = check_chunks(batch, chunk_size, &max_nc)) != SP_OK) return st;
@@ -409,18 +462,7 @@ sp_status sp_select_chunks(int32_t mode, double param, const sp_batch *batch, in
   const SegTable chunks = make_table(batch, 0, chunk_size, 0);
   const size_t need = select_ws(chunks.B, chunks.unit_off[chunks.B]);
   if (need && (!ws || ws_bytes < need)) return SP_ERR_WORKSPACE_TOO_SMALL;
-  SelectTable t;
-  memset(&t, 0, sizeof(t));
-  t.B = chunks.B;
-  for (int b = 0; b < chunks.B; ++b) {
-    const int nc = chunks.unit_off[b + 1] - chunks.unit_off[b];
-    t.chunk_off[b + 1] = chunks.unit_off[b + 1];
-    t.blk_off[b + 1] = t.blk_off[b] + select_rank_blocks(nc);
-    int64_t v = (int64_t)ceil(param * (double)nc - 1e-9);
-    if (v > nc) v = nc;
-    if (v < 1) v = 1;
-    t.kc[b] = (int32_t)v;
-  }
+  const SelectTable t = make_select_table(chunks, param);
   return launched(launch_select(mode, param, t, chunk_scores, keep, n_kept_chunks, ws,
                                 reinterpret_cast<hipStream_t>(stream)));
 }
@@ -454,6 +496,92 @@ sp_status sp_gather_kept(const sp_batch *batch, int32_t chunk_size, const uint8_
   return launched(launch_gather(chunks, blocks, blocks.unit_off[blocks.B], chunk_size, keep,
                                 token_ids, kept_ids, kept_pos, kept_offsets, ws,
                                 reinterpret_cast<hipStream_t>(stream)));
+}
+
+sp_status sp_pool_select_gather_workspace_bytes(const sp_pool_desc *pool, const sp_batch *batch,
+                                                size_t *bytes) {
+  if (!bytes) return SP_ERR_INVALID_ARGUMENT;
+  PoolParams p;
+  int64_t total;
+  int max_nc;
+  sp_status st = check_pool(pool, &p);
+  if (st != SP_OK) return st;
+  if ((st = check_batch(batch, &total)) != SP_OK) return st;
+  if ((st = check_chunks(batch, p.C, &max_nc)) != SP_OK) return st;
+  *bytes = post_ws_bytes(make_pool_table(batch, p.C), make_table(batch, 0, p.C, 0));
+  return SP_OK;
+}
+
+sp_status sp_pool_select_gather(const sp_pool_desc *pool, int32_t mode, double param,
+                                const sp_batch *batch, const float *importance,
+                                const int32_t *token_ids, float *token_scores,
+                                float *chunk_scores, uint8_t *keep, int32_t *n_kept_chunks,
+                                int32_t *kept_ids, int32_t *kept_pos, int64_t *kept_offsets,
+                                void *ws, size_t ws_bytes, void *stream) {
+  PoolParams p;
+  int64_t total;
+  int max_nc;
+  if (!check_select_args(mode, param)) return SP_ERR_INVALID_ARGUMENT;
+  sp_status st = check_pool(pool, &p);
+  if (st != SP_OK) return st;
+  if ((st = check_batch(batch, &total)) != SP_OK) return st;
+  if ((st = check_chunks(batch, p.C, &max_nc)) != SP_OK) return st;
+  if (!importance || !token_ids || !chunk_scores || !keep || !n_kept_chunks || !kept_ids ||
+      !kept_pos || !kept_offsets)
+    return SP_ERR_INVALID_ARGUMENT;
+  if (!aligned16(ws)) return SP_ERR_INVALID_ARGUMENT;
+  const PoolTable pt = make_pool_table(batch, p.C);
+  const SegTable chunks = make_table(batch, 0, p.C, 0);
+  if (!ws || ws_bytes < post_ws_bytes(pt, chunks)) return SP_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const SelectTable sel = make_select_table(chunks, param);
+  const int TB = post_block_tokens(batch, p.C, post_max_blocks());
+  if (TB > 0) {
+    PostTable t;
+    memset(&t, 0, sizeof(t));
+    t.B = batch->n_prompts;
+    t.TB = TB;
+    t.GT = pool_block_tokens(p.C);
+    for (int b = 0; b < t.B; ++b) {
+      const int64_t n = batch->token_offsets[b + 1] - batch->token_offsets[b];
+      t.blk_off[b + 1] = t.blk_off[b] + (int32_t)((n + TB - 1) / TB);
+      t.chunk_off[b + 1] = chunks.unit_off[b + 1];
+      t.grp_off[b + 1] = pt.blk_off[b + 1];
+      t.tok_off[b] = chunks.tok_off[b];
+      t.kc[b] = sel.kc[b];
+    }
+    t.tok_off[t.B] = chunks.tok_off[t.B];
+    t.G = t.blk_off[t.B];
+    return launched(launch_post(mode, param, p, t, importance, token_ids, token_scores,
+                                chunk_scores, keep, n_kept_chunks, kept_ids, kept_pos,
+                                kept_offsets, ws, hs));
+  }
+  // The separate kernels, on the regions after the header.
+  char *pool_region = reinterpret_cast<char *>(ws) + kStatusBytes;
+  char *gather_region = pool_region + align_up(pool_ws(pt.B, pt.blk_off[pt.B]));
+  const SegTable blocks = make_table(batch, 0, kGatherBlockTokens, 0);
+  hipError_t e = launch_stamp(ws, hs);
+  if (e == hipSuccess)
+    e = launch_pool_chunk(p, pt, importance, token_scores, chunk_scores, pool_region, hs);
+  if (e == hipSuccess)
+    e = launch_select(mode, param, sel, chunk_scores, keep, n_kept_chunks, nullptr, hs);
+  if (e == hipSuccess)
+    e = launch_gather(chunks, blocks, blocks.unit_off[blocks.B], p.C, keep, token_ids, kept_ids,
+                      kept_pos, kept_offsets, gather_region, hs);
+  return launched(e);
+}
+
+sp_status sp_pool_select_gather_plan(const sp_pool_desc *pool, const sp_batch *batch, int32_t *block_tokens) {
+  PoolParams p;
+  int64_t total;
+  int max_nc;
+  if (!block_tokens) return SP_ERR_INVALID_ARGUMENT;
+  sp_status st = check_pool(pool, &p);
+  if (st != SP_OK) return st;
+  if ((st = check_batch(batch, &total)) != SP_OK) return st;
+  if ((st = check_chunks(batch, p.C, &max_nc)) != SP_OK) return st;
+  *block_tokens = post_block_tokens(batch, p.C, post_max_blocks());
+  return SP_OK;
 }
 
 sp_status sp_window_plan(int64_t n_tokens, int32_t window, int32_t stride, int32_t capacity,

@@ -17,8 +17,11 @@
 // k_pool_minmax: per prompt, when a prompt has too many blocks for every
 //   block to reduce them itself.
 // k_pool_finish: pools again (cheaper than a round trip of the pooled values
-//   through memory), normalises, boosts, writes the token scores and takes
-//   the chunk means from LDS.
+//   through memory), normalises, boosts and writes the token scores, and
+//   writes each chunk's mean of them as chunk_score() forms it: from the
+//   chunk's boosted pooled values relative to the block's min, so that a
+//   launch that does not know the prompt's min and max yet can form the
+//   same sums.
 #include <algorithm>
 
 #include "sp_internal.h"
@@ -33,7 +36,6 @@ constexpr int kTargetTB = 256;
 // Prompts with more blocks than this get their min and max reduced once
 // (k_pool_minmax) instead of by every block of k_pool_finish.
 constexpr int kFinishReduceMax = 2048;
-constexpr int kDefaultRadius = 6;   // W = 13, the width of Approach step 3 (above)
 
 struct BlockSpan {
   int b;           // prompt
@@ -57,26 +59,6 @@ __device__ __forceinline__ BlockSpan block_span(const PoolTable &pt, int blk, in
   return s;
 }
 
-// Mean of buf over the window of token t clipped to the prompt, summed in
-// token order. R >= 0: the radius at compile time (the loads issue together);
-// R < 0: radius r at run time.
-template <int R>
-__device__ __forceinline__ float window_mean(const float *buf, int lo, int N, int t, int r) {
-  const int a = max(0, t - r), e = min(N - 1, t + r);
-  float sum = 0.f;
-  if constexpr (R >= 0) {
-#pragma unroll
-    for (int k = -R; k <= R; ++k) {
-      const int i = t + k;
-      const float v = buf[min(max(i, a), e) - lo];   // always inside the staged span
-      sum += (i >= a && i <= e) ? v : 0.f;
-    }
-  } else {
-    for (int i = a; i <= e; ++i) sum += buf[i - lo];
-  }
-  return sum / (float)(e - a + 1);
-}
-
 // Pooled values of the block's tokens into out[0 .. t1 - t0) (LDS), from the
 // halo-extended importance staged in buf.
 __device__ __forceinline__ void pool_block(const PoolParams &p, const BlockSpan &s,
@@ -85,9 +67,9 @@ __device__ __forceinline__ void pool_block(const PoolParams &p, const BlockSpan 
   const int lo = max(0, s.t0 - r), hi = min(s.N, s.t1 + r);
   for (int i = threadIdx.x; i < hi - lo; i += kPoolThreads) buf[i] = imp[s.base + lo + i];
   __syncthreads();
-  if (r == kDefaultRadius) {
+  if (r == kDefaultPoolRadius) {
     for (int t = s.t0 + threadIdx.x; t < s.t1; t += kPoolThreads)
-      out[t - s.t0] = window_mean<kDefaultRadius>(buf, lo, s.N, t, r);
+      out[t - s.t0] = window_mean<kDefaultPoolRadius>(buf, lo, s.N, t, r);
   } else {
     for (int t = s.t0 + threadIdx.x; t < s.t1; t += kPoolThreads)
       out[t - s.t0] = window_mean<-1>(buf, lo, s.N, t, r);
@@ -96,19 +78,7 @@ __device__ __forceinline__ void pool_block(const PoolParams &p, const BlockSpan 
 }
 
 __device__ __forceinline__ float2 block_minmax(float mn, float mx, float2 *red) {
-  for (int off = 32; off > 0; off >>= 1) {
-    mn = fminf(mn, __shfl_xor(mn, off, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  }
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(mn, mx);
-  __syncthreads();
-  float2 v = red[0];
-  for (int w = 1; w < kPoolThreads / 64; ++w) {
-    v.x = fminf(v.x, red[w].x);
-    v.y = fmaxf(v.y, red[w].y);
-  }
-  __syncthreads();
-  return v;
+  return sp::block_minmax<kPoolThreads / 64>(mn, mx, red);
 }
 
 __global__ __launch_bounds__(kPoolThreads) void k_pool_stats(PoolParams p, PoolTable blocks, int TB,
@@ -174,23 +144,28 @@ __global__ __launch_bounds__(kPoolThreads) void k_pool_finish(
     flat = range <= 1e-6f * v.y;   // no signal: every score becomes 1
   }
   pool_block(p, s, imp, buf, xs);
+  // The block's chunks (it starts on a chunk boundary of its prompt; the
+  // block is the chunks' pool group, its min g from k_pool_stats or, without
+  // normalisation, reduced here).
+  float g;
+  if (p.normalize) {
+    g = block_mm[blockIdx.x].x;
+  } else {
+    float lo = INFINITY;
+    for (int i = threadIdx.x; i < s.t1 - s.t0; i += kPoolThreads) lo = fminf(lo, xs[i]);
+    g = block_minmax(lo, -INFINITY, red).x;
+  }
+  const int nchunk = (s.t1 - s.t0 + p.C - 1) / p.C;
+  for (int c = threadIdx.x; c < nchunk; c += kPoolThreads) {
+    const int a = s.t0 + c * p.C, e = min(s.t1, a + p.C);
+    const float rel = chunk_rel(p, s.N, xs, s.t0, a, e, g);
+    chunk_scores[blocks.chunk_off[s.b] + a / p.C] =
+        chunk_score(rel, boost_sum(p, s.N, a, e), g, e - a, p.normalize, flat, mn, range);
+  }
   for (int t = s.t0 + threadIdx.x; t < s.t1; t += kPoolThreads) {
     float x = xs[t - s.t0];
     if (p.normalize) x = flat ? 1.f : (x - mn) / range;
-    if (t < p.first_n) x *= p.first_mult;
-    if (t >= s.N - p.last_n) x *= p.last_mult;
-    xs[t - s.t0] = x;
-    if (token_scores) token_scores[s.base + t] = x;
-  }
-  __syncthreads();
-  // The block's chunks: it starts on a chunk boundary of its prompt.
-  const int nchunk = (s.t1 - s.t0 + p.C - 1) / p.C;
-  for (int c = threadIdx.x; c < nchunk; c += kPoolThreads) {
-    const int a = c * p.C, e = min(s.t1 - s.t0, a + p.C);
-    float sum = 0.f;
-    for (int i = a; i < e; ++i) sum += xs[i];
-    const int pc = (s.t0 + a) / p.C;   // chunk index within the prompt
-    chunk_scores[blocks.chunk_off[s.b] + pc] = sum / (float)(e - a);
+    if (token_scores) token_scores[s.base + t] = boosted(p, s.N, t, x);
   }
 }
 

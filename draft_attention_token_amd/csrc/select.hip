@@ -57,17 +57,6 @@ __device__ __forceinline__ uint32_t order_key(long long fx) {
   return 0xffffffffu - (uint32_t)((unsigned long long)fx >> 16);
 }
 
-template <typename T, typename Op>
-__device__ __forceinline__ T block_reduce(T v, T *red, Op op) {
-  for (int off = 32; off > 0; off >>= 1) v = op(v, __shfl_xor(v, off, 64));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  v = red[0];
-  for (int w = 1; w < kWaves; ++w) v = op(v, red[w]);
-  __syncthreads();
-  return v;
-}
-
 __device__ __forceinline__ int table_prompt(const int32_t *off, int B, int u) {
   int lo = 0, hi = B - 1;
   while (lo < hi) {
@@ -110,14 +99,14 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectTable t, double param
   float mx = 0.f;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) mx = fmaxf(mx, sc[e]);
-  mx = block_reduce(mx, redf, [](float a, float c) { return fmaxf(a, c); });
+  mx = block_max<kWaves>(mx, redf);
   const int shift = fixed_shift(mx);
   long long need;
   if (kMass) {
     long long tot = 0;
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) tot += to_fixed(sc[e], shift);
-    tot = block_reduce(tot, redl, [](long long a, long long c) { return a + c; });
+    tot = block_sum<kWaves>(tot, redl);
     need = (long long)ceil(param * (double)tot) - to_fixed(c_last, shift);
   } else {
     need = t.kc[b] - 1;   // chunks ahead of a kept one

@@ -46,6 +46,91 @@ __device__ __forceinline__ int seg_of(const SegTable &t, int32_t u) {
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Reduction with op over the 64 lanes of a wave, the result in every lane:
+// DPP within each row of 16 lanes (lane xor 1 and xor 2 by quad permutes,
+// then rotations by 4 and 8 gather the row's four quads), then the four row
+// values read as scalars. Few-cycle steps, where a lane shuffle is an LDS
+// crossbar round trip. op must be associative and commutative.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x, Op op) {
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false));   // xor 1
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xf, 0xf, false));   // xor 2
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xf, 0xf, false));  // ror 4
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false));  // ror 8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
+__device__ __forceinline__ float wave_min(float v) {
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+// Block-wide forms (kWaves waves; red: kWaves entries of LDS), the result
+// in every thread; they synchronise the block.
+template <int kWaves>
+__device__ __forceinline__ float block_max(float v, float *red) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) v = fmaxf(v, red[w]);
+  __syncthreads();
+  return v;
+}
+template <int kWaves>
+__device__ __forceinline__ float2 block_minmax(float lo, float hi, float2 *red) {
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(lo, hi);
+  __syncthreads();
+  float2 v = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    v.x = fminf(v.x, red[w].x);
+    v.y = fmaxf(v.y, red[w].y);
+  }
+  __syncthreads();
+  return v;
+}
+// Sum over the wave of a 64-bit integer (exact), in every lane.
+__device__ __forceinline__ long long wave_sum_i64(long long v) {
+  unsigned long long x = (unsigned long long)v;
+#define SP_DPP_ADD64(ctrl)                                                                        \
+  {                                                                                               \
+    const uint32_t l2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, ctrl, 0xf, 0xf, false); \
+    const uint32_t h2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), ctrl, 0xf, 0xf, false); \
+    x += ((unsigned long long)h2 << 32) | l2;                                                     \
+  }
+  SP_DPP_ADD64(0xB1) SP_DPP_ADD64(0x4E) SP_DPP_ADD64(0x124) SP_DPP_ADD64(0x128)
+#undef SP_DPP_ADD64
+  unsigned long long t = 0;
+#pragma unroll
+  for (int r = 0; r < 64; r += 16)
+    t += ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), r) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, r);
+  return (long long)t;
+}
+template <int kWaves>
+__device__ __forceinline__ long long block_sum(long long v, long long *red) {
+  v = wave_sum_i64(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) v += red[w];
+  __syncthreads();
+  return v;
+}
+
 // Output offsets of a batch's prompts from their kept counts, on one wave
 // (lane l takes prompts 2 l and 2 l + 1; B <= SP_MAX_PROMPTS = 128): returns
 // the offset of prompt b to every lane, and when `offsets` is not null
@@ -86,6 +171,9 @@ struct AttnShape {
 
 // n consecutive nonzero tags, unique within the process (until 2^32 calls).
 uint32_t reserve_tags(int n);
+// Budget of a cross-block wait in wall-clock ticks (100 MHz): 2 s, or
+// SP_SCORE_WAIT_US microseconds when that is set.
+uint64_t score_wait_ticks();
 
 // Launchers (return hipError_t of the launch).
 // Scoring workspace: header, then the single-pass kernel's slots (for shapes
@@ -113,12 +201,81 @@ hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const 
 bool score_stream_plan(const AttnShape &s, const SegTable &tiles, int *n_launches,
                        int32_t *prompt_launch);
 
+// Mean of buf over the window of token t clipped to the prompt, summed in
+// token order. R >= 0: the radius at compile time (the loads issue together);
+// R < 0: radius r at run time.
+template <int R>
+__device__ __forceinline__ float window_mean(const float *buf, int lo, int N, int t, int r) {
+  const int a = max(0, t - r), e = min(N - 1, t + r);
+  float sum = 0.f;
+  if constexpr (R >= 0) {
+#pragma unroll
+    for (int k = -R; k <= R; ++k) {
+      const int i = t + k;
+      const float v = buf[min(max(i, a), e) - lo];   // always inside the staged span
+      sum += (i >= a && i <= e) ? v : 0.f;
+    }
+  } else {
+    for (int i = a; i <= e; ++i) sum += buf[i - lo];
+  }
+  return sum / (float)(e - a + 1);
+}
+
 struct PoolParams {
   int W, C, normalize, first_n, last_n;
   float first_mult, last_mult;
 };
+
+// v times the boosts of token t of a prompt of N tokens (first, then last;
+// a factor of 1 where a boost does not apply leaves v as it is).
+__device__ __forceinline__ float boosted(const PoolParams &p, int N, int t, float v) {
+  v = __fmul_rn(v, t < p.first_n ? p.first_mult : 1.f);
+  return __fmul_rn(v, t >= N - p.last_n ? p.last_mult : 1.f);
+}
+// Sum of the boosts of tokens [a, e), in token order (e - a where none
+// applies: a sum of ones is exact).
+__device__ __forceinline__ float boost_sum(const PoolParams &p, int N, int a, int e) {
+  if (a >= p.first_n && e <= N - p.last_n) return (float)(e - a);
+  float s = 0.f;
+  for (int t = a; t < e; ++t) s = __fadd_rn(s, boosted(p, N, t, 1.f));
+  return s;
+}
+// Sum of b_t (x_t - g) over tokens [a, e), x_t at xs[t - base] (LDS), in a
+// fixed order: partial sums of consecutive runs of 8 tokens, each in token
+// order, then the partials in order (chunk_rel; chunk_part gives one run so
+// that lanes can take them in parallel). Additions stay uncontracted.
+__device__ __forceinline__ float chunk_part(const PoolParams &p, int N, const float *xs, int base,
+                                            int a, int e, float g) {
+  float v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) v[u] = xs[min(a + u, e - 1) - base];   // (clamped: unused past e)
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (a + u < e) s = __fadd_rn(s, boosted(p, N, a + u, v[u] - g));
+  return s;
+}
+__device__ __forceinline__ float chunk_rel(const PoolParams &p, int N, const float *xs, int base,
+                                           int a, int e, float g) {
+  float rel = 0.f;
+  for (int t = a; t < e; t += 8) rel = __fadd_rn(rel, chunk_part(p, N, xs, base, t, e, g));
+  return rel;
+}
+// A chunk's score, the mean over its n tokens of their normalised, boosted
+// scores b_t (x_t - mn) / range, from sums that do not need the prompt's
+// min and max: rel = sum of b_t (x_t - g) in token order, with g the min of
+// the chunk's pool group (so every term is >= 0), and bs = sum of b_t. The
+// mean is (rel + (g - mn) bs) / (range n); without normalisation (mn = 0,
+// range = 1) (rel + g bs) / n; a flat prompt (every score 1) bs / n.
+__device__ __forceinline__ float chunk_score(float rel, float bs, float g, int n, bool normalize,
+                                             bool flat, float mn, float range) {
+  if (!normalize) return __fmaf_rn(g, bs, rel) / (float)n;
+  if (flat) return bs / (float)n;
+  return __fmaf_rn(g - mn, bs, rel) / (range * (float)n);
+}
 // Pooling works on blocks of whole chunks of one prompt,
-// pool_block_tokens(C) = C * max(1, floor(256 / C)) tokens each.
+// pool_block_tokens(C) = C * max(1, floor(256 / C)) tokens each; these
+// blocks are also the pool groups whose min enters the chunk scores.
 struct PoolTable {
   int32_t B;
   int32_t blk_off[SP_MAX_PROMPTS + 1];     // block prefix per prompt
@@ -142,6 +299,35 @@ int select_rank_blocks(int nc);
 size_t select_ws(int B, int total_chunks);
 hipError_t launch_select(int mode, double param, const SelectTable &t, const float *chunk_scores,
                          uint8_t *keep, int32_t *n_kept, void *ws, hipStream_t st);
+
+// Pooling, selection and compaction in one launch (post.hip): blocks of TB
+// tokens (whole pool groups of one prompt, at most kPostMaxTB tokens and
+// kPostMaxChunks chunks), at most one per CU and kPostMaxBlocks in all, all
+// resident at once; at most kPostMaxGroups pool groups per prompt.
+constexpr int kPostMaxTB = 2048;
+constexpr int kPostMaxChunks = 64;
+constexpr int kPostMaxBlocks = 1024;
+constexpr int kPostMaxGroups = 2048;
+struct PostTable {
+  int32_t B, G, TB;
+  int32_t GT;                              // tokens per pool group: pool_block_tokens(C)
+  int32_t blk_off[SP_MAX_PROMPTS + 1];     // block prefix per prompt
+  int32_t chunk_off[SP_MAX_PROMPTS + 1];   // chunk prefix per prompt
+  int32_t grp_off[SP_MAX_PROMPTS + 1];     // pool-group prefix per prompt
+  int32_t tok_off[SP_MAX_PROMPTS + 1];     // token offsets
+  int32_t kc[SP_MAX_PROMPTS];              // top-p budget per prompt
+};
+// Blocks the fused launch may use on the current device (0: it cannot run).
+int post_max_blocks();
+// Bytes of its slots (after the status header) for a batch's chunks and
+// pool groups.
+size_t post_slot_bytes(int total_chunks, int total_groups);
+hipError_t launch_post(int mode, double param, const PoolParams &p, const PostTable &t,
+                       const float *imp, const int32_t *ids, float *token_scores,
+                       float *chunk_scores, uint8_t *keep, int32_t *n_kept, int32_t *kept_ids,
+                       int32_t *kept_pos, int64_t *kept_offsets, void *ws, hipStream_t st);
+// Marks the status header at ws as a call with no timed-out wait.
+hipError_t launch_stamp(void *ws, hipStream_t st);
 
 hipError_t launch_gather(const SegTable &chunks, const SegTable &blocks, int total_blocks, int C,
                          const uint8_t *keep, const int32_t *ids, int32_t *kept_ids,

@@ -11,6 +11,7 @@ Functions mirror the C ABI in ``include/specprefill.h``:
 * :func:`sp_pool_chunk` (importance -> token scores, chunk scores)
 * :func:`sp_select_chunks` (chunk scores -> keep flags, kept-chunk counts)
 * :func:`sp_gather_kept` (keep flags, token ids -> kept ids, positions, offsets)
+* :func:`sp_pool_select_gather` (the three calls above as one)
 
 ``offsets`` is always the host-side ``[B + 1]`` int64 prompt-token offsets.
 """
@@ -40,7 +41,8 @@ EXPORTED = [
     "sp_select_workspace_bytes", "sp_gather_workspace_bytes", "sp_score_attention",
     "sp_pool_chunk", "sp_select_chunks", "sp_gather_kept", "sp_score_status", "sp_break_even",
     "sp_window_plan", "sp_stitch_windows", "sp_select_legacy_workspace_bytes", "sp_select_legacy",
-    "sp_score_plan", "sp_score_attention_noalloc",
+    "sp_score_plan", "sp_score_attention_noalloc", "sp_pool_select_gather_workspace_bytes",
+    "sp_pool_select_gather", "sp_pool_select_gather_plan",
 ]
 
 _ALGOS = {"auto": SP_SCORE_AUTO, "two_pass": SP_SCORE_TWO_PASS, "stream": SP_SCORE_STREAM}
@@ -102,6 +104,12 @@ def lib():
         L.sp_score_attention_noalloc.argtypes = [ctypes.POINTER(sp_attn_desc), bp, vp, vp, vp, vp]
         L.sp_score_plan.argtypes = [ctypes.POINTER(sp_attn_desc), bp, ctypes.POINTER(ctypes.c_int32),
                                     ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+        L.sp_pool_select_gather_workspace_bytes.argtypes = [ctypes.POINTER(sp_pool_desc), bp, szp]
+        L.sp_pool_select_gather.argtypes = [ctypes.POINTER(sp_pool_desc), ctypes.c_int32,
+                                            ctypes.c_double, bp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                            vp, sz, vp]
+        L.sp_pool_select_gather_plan.argtypes = [ctypes.POINTER(sp_pool_desc), bp,
+                                                 ctypes.POINTER(ctypes.c_int32)]
         L.sp_break_even.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
                                     ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_int32)]
         i32p, i64p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
@@ -424,8 +432,58 @@ def sp_gather_kept(keep: torch.Tensor, token_ids: torch.Tensor, offsets, C: int,
     return out_ids, out_pos, out_offsets
 
 
+def post_workspace_bytes(desc: sp_pool_desc, batch: Batch) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().sp_pool_select_gather_workspace_bytes(ctypes.byref(desc), batch.ref(),
+                                                       ctypes.byref(n)),
+           "sp_pool_select_gather_workspace_bytes")
+    return n.value
+
+
+def post_plan(desc: sp_pool_desc, batch: Batch) -> int:
+    """Tokens per block of the one-launch form on the current device (0: the
+    call runs the separate kernels)."""
+    tb = ctypes.c_int32(-1)
+    _check(lib().sp_pool_select_gather_plan(ctypes.byref(desc), batch.ref(), ctypes.byref(tb)),
+           "sp_pool_select_gather_plan")
+    return tb.value
+
+
+def sp_pool_select_gather(importance: torch.Tensor, token_ids: torch.Tensor, offsets, mode: str,
+                          param: float, W=13, C=32, normalize=True, first_n=64, first_mult=1.5,
+                          last_n=128, last_mult=1.3, token_scores: bool = True, ws=None):
+    """sp_pool_chunk + sp_select_chunks + sp_gather_kept in one call: (token_scores
+    or None, chunk_scores, keep, n_kept_chunks, kept_ids, kept_pos, kept_offsets)."""
+    batch = offsets if isinstance(offsets, Batch) else Batch(offsets)
+    desc = pool_desc(W, C, normalize, first_n, first_mult, last_n, last_mult)
+    if importance.dtype != torch.float32 or importance.numel() != batch.total:
+        raise ValueError("importance must be fp32 [sum N_b]")
+    if token_ids.dtype != torch.int32 or token_ids.numel() != batch.total:
+        raise ValueError("token_ids must be int32 [sum N_b]")
+    dev = importance.device
+    T, nc = batch.total, batch.n_chunks(C) if C > 0 else 1
+    ts = torch.empty(T, dtype=torch.float32, device=dev) if token_scores else None
+    cs = torch.empty(nc, dtype=torch.float32, device=dev)
+    keep = torch.empty(nc, dtype=torch.uint8, device=dev)
+    counts = torch.empty(batch.B, dtype=torch.int32, device=dev)
+    ids = torch.empty(T, dtype=torch.int32, device=dev)
+    pos = torch.empty(T, dtype=torch.int32, device=dev)
+    offs = torch.empty(batch.B + 1, dtype=torch.int64, device=dev)
+    if ws is None:
+        ws = _ws(post_workspace_bytes(desc, batch), dev)
+    m = _MODES[mode] if isinstance(mode, str) else int(mode)
+    _check(lib().sp_pool_select_gather(ctypes.byref(desc), m, float(param), batch.ref(),
+                                       _ptr(importance), _ptr(token_ids), _ptr(ts), _ptr(cs),
+                                       _ptr(keep), _ptr(counts), _ptr(ids), _ptr(pos), _ptr(offs),
+                                       _ptr(ws), ws.numel(), _stream(dev)),
+           "sp_pool_select_gather")
+    return ts, cs, keep, counts, ids, pos, offs
+
+
 class Pipeline:
-    """All four calls on preallocated buffers (what the benchmark times).
+    """The whole path on preallocated buffers (what the benchmark times):
+    sp_score_attention, then sp_pool_select_gather (fused=True) or the three
+    calls it stands for.
 
     Holds device buffers for one batch shape; :meth:`run` enqueues the whole
     path on the current stream and returns nothing (results stay in the
@@ -436,8 +494,9 @@ class Pipeline:
     def __init__(self, offsets, n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype,
                  device, W=13, C=32, normalize=True, boost=True, mode="mass", param=0.85,
                  algo="auto", scale=None, token_scores=True, k_dtype=None, k_scales=None,
-                 prefill_row=False, pool_before_max=False):
+                 prefill_row=False, pool_before_max=False, fused=True):
         self.batch = offsets if isinstance(offsets, Batch) else Batch(offsets)
+        self.fused = fused
         fm, lm = (1.5, 1.3) if boost else (1.0, 1.0)
         self.adesc = attn_desc(n_layers, n_q_heads, n_kv_heads, head_dim, n_lookahead, dtype,
                                scale, algo, k_dtype=k_dtype, k_scales=k_scales,
@@ -460,21 +519,47 @@ class Pipeline:
         self.ws_pool = _ws(pool_workspace_bytes(self.pdesc, self.batch), device)
         self.ws_select = _ws(select_workspace_bytes(self.batch, C), device)
         self.ws_gather = _ws(gather_workspace_bytes(self.batch, C), device)
+        self.ws_post = _ws(post_workspace_bytes(self.pdesc, self.batch), device)
         self.device = device
 
     def score_status(self) -> int:
         return score_status(self.ws_score)
 
+    def post_status(self) -> int:
+        """Status of the latest sp_pool_select_gather on the pipeline's workspace."""
+        return score_status(self.ws_post)
+
     def run(self, q: torch.Tensor, k: torch.Tensor, token_ids: torch.Tensor, check: bool = False):
-        """The four calls on the pipeline's stream. check=True waits for them
-        and raises if a cross-block wait of the scoring kernel timed out (the
-        results are then invalid)."""
+        """The path on the pipeline's stream. check=True waits for it and
+        raises if a cross-block wait timed out (the results are then invalid)."""
+        self.run_score(q, k)
+        self.run_post(token_ids)
+        if check:
+            if self.score_status() != 0:
+                raise SpError(SP_ERR_DEVICE, "sp_score_attention (a cross-block wait timed out)")
+            if self.fused and self.post_status() != 0:
+                raise SpError(SP_ERR_DEVICE, "sp_pool_select_gather (a cross-block wait timed out)")
+
+    def run_score(self, q: torch.Tensor, k: torch.Tensor):
+        """The scoring call alone (importance from Q and K)."""
+        _check(lib().sp_score_attention(ctypes.byref(self.adesc), self.batch.ref(), _ptr(q), _ptr(k),
+                                        _ptr(self.importance), _ptr(self.ws_score),
+                                        self.ws_score.numel(), _stream(self.device)),
+               "sp_score_attention")
+
+    def run_post(self, token_ids: torch.Tensor):
+        """The stages after scoring, on the pipeline's importance."""
         L = lib()
         st = _stream(self.device)
         b = self.batch.ref()
-        _check(L.sp_score_attention(ctypes.byref(self.adesc), b, _ptr(q), _ptr(k),
-                                    _ptr(self.importance), _ptr(self.ws_score),
-                                    self.ws_score.numel(), st), "sp_score_attention")
+        if self.fused:
+            _check(L.sp_pool_select_gather(
+                ctypes.byref(self.pdesc), self.mode, self.param, b, _ptr(self.importance),
+                _ptr(token_ids), _ptr(self.token_scores), _ptr(self.chunk_scores), _ptr(self.keep),
+                _ptr(self.n_kept), _ptr(self.kept_ids), _ptr(self.kept_pos),
+                _ptr(self.kept_offsets), _ptr(self.ws_post), self.ws_post.numel(), st),
+                "sp_pool_select_gather")
+            return
         _check(L.sp_pool_chunk(ctypes.byref(self.pdesc), b, _ptr(self.importance),
                                _ptr(self.token_scores), _ptr(self.chunk_scores),
                                _ptr(self.ws_pool), self.ws_pool.numel(), st), "sp_pool_chunk")
@@ -486,8 +571,6 @@ class Pipeline:
                                 _ptr(self.kept_pos), _ptr(self.kept_offsets),
                                 _ptr(self.ws_gather), self.ws_gather.numel(), st),
                "sp_gather_kept")
-        if check and self.score_status() != 0:
-            raise SpError(SP_ERR_DEVICE, "sp_score_attention (a cross-block wait timed out)")
 
 
 class ToolPipeline:
@@ -529,11 +612,22 @@ class ToolPipeline:
     def run(self, q: torch.Tensor, k: torch.Tensor, token_ids: torch.Tensor, check: bool = False):
         """q, k: the window batch's Q and K; token_ids: [n_tokens] of the prompt.
         check=True waits and raises if a scoring wait timed out."""
+        self.run_score(q, k)
+        self.run_post(token_ids)
+        if check and self.score_status() != 0:
+            raise SpError(SP_ERR_DEVICE, "sp_score_attention (a cross-block wait timed out)")
+
+    def run_score(self, q: torch.Tensor, k: torch.Tensor):
+        """The scoring call on the window batch alone."""
+        _check(lib().sp_score_attention(ctypes.byref(self.adesc), self.windows.ref(), _ptr(q),
+                                        _ptr(k), _ptr(self.importance), _ptr(self.ws_score),
+                                        self.ws_score.numel(), _stream(self.device)),
+               "sp_score_attention")
+
+    def run_post(self, token_ids: torch.Tensor):
+        """Stitching, pooling and the legacy selection on the window scores."""
         L = lib()
         st = _stream(self.device)
-        _check(L.sp_score_attention(ctypes.byref(self.adesc), self.windows.ref(), _ptr(q), _ptr(k),
-                                    _ptr(self.importance), _ptr(self.ws_score),
-                                    self.ws_score.numel(), st), "sp_score_attention")
         _check(L.sp_stitch_windows(self.windows.ref(), self._starts, self._keeps, self.n,
                                    _ptr(self.importance), _ptr(self.scores), st),
                "sp_stitch_windows")
@@ -545,5 +639,3 @@ class ToolPipeline:
                                   _ptr(token_ids), _ptr(self.kept_ids), _ptr(self.kept_pos),
                                   _ptr(self.kept_offsets), _ptr(self.ws_legacy),
                                   self.ws_legacy.numel(), st), "sp_select_legacy")
-        if check and self.score_status() != 0:
-            raise SpError(SP_ERR_DEVICE, "sp_score_attention (a cross-block wait timed out)")

@@ -11,6 +11,7 @@
  *   sp_pool_chunk       importance      -> token_scores[token], chunk_scores[chunk]
  *   sp_select_chunks    chunk_scores    -> keep[chunk], n_kept_chunks[prompt]
  *   sp_gather_kept      keep, token ids -> kept ids + original positions
+ *   sp_pool_select_gather   the three calls above as one
  *   sp_break_even       host-side estimate: is sparse prefill worth running?
  * and the standalone tool's window and legacy-selection steps:
  *   sp_window_plan, sp_stitch_windows, sp_select_legacy
@@ -219,9 +220,10 @@ sp_status sp_score_attention_noalloc(const sp_attn_desc *desc, const sp_batch *b
 sp_status sp_score_plan(const sp_attn_desc *desc, const sp_batch *batch, int32_t *kernel,
                         int32_t *n_launches, int32_t *prompt_launch);
 
-/* Whether the latest sp_score_attention call on this workspace completed:
- * *status_host = 0 if so (or if there was none), 1 if a wait timed out and
- * the importance it wrote is not valid. Synchronises `stream`. */
+/* Whether the latest sp_score_attention (or sp_pool_select_gather) call on
+ * this workspace completed: *status_host = 0 if so (or if there was none), 1
+ * if a wait timed out and the results it wrote are not valid. Synchronises
+ * `stream`. */
 sp_status sp_score_status(const void *ws, int32_t *status_host, void *stream);
 
 /*
@@ -280,6 +282,47 @@ sp_status sp_select_chunks(int32_t mode, double param, const sp_batch *batch, in
 sp_status sp_gather_kept(const sp_batch *batch, int32_t chunk_size, const uint8_t *keep,
                          const int32_t *token_ids, int32_t *kept_ids, int32_t *kept_pos,
                          int64_t *kept_offsets, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * sp_pool_chunk, sp_select_chunks and sp_gather_kept in one call, with the
+ * same arguments and bit-identical results ([PR] Approach steps 3-4; [G]
+ * v3.1 item 5, v3 items 1-2, Chunk Selection, Sparse Prefill). On the device
+ * the three stages run as one launch of at most one block per compute unit
+ * (blocks of whole chunks of one prompt, up to 2048 tokens and 64 chunks
+ * each), the blocks handing each other min/max, chunk scores and kept
+ * counts through the workspace; a batch that needs more blocks than that
+ * runs the three stages' own kernels instead (sp_pool_select_gather_plan
+ * tells which).
+ *
+ *   pool:         as sp_pool_chunk (its chunk_size is C).
+ *   mode, param:  as sp_select_chunks.
+ *   importance:   [sum N_b] fp32 in.
+ *   token_ids:    [sum N_b] int32 in.
+ *   token_scores: [sum N_b] fp32 out, or NULL.
+ *   chunk_scores, keep, n_kept_chunks: out, as sp_pool_chunk and
+ *                 sp_select_chunks.
+ *   kept_ids, kept_pos, kept_offsets: out, as sp_gather_kept.
+ *   ws: device workspace (16-byte aligned) of at least
+ *       sp_pool_select_gather_workspace_bytes() bytes; it starts with the
+ *       same status header as the scoring workspace, and never needs
+ *       clearing.
+ * Waits between blocks are bounded like the scoring call's (2 s, or
+ * SP_SCORE_WAIT_US): a call whose wait ran out writes no kept ids or
+ * positions and sp_score_status() on its workspace reports 1.
+ */
+sp_status sp_pool_select_gather_workspace_bytes(const sp_pool_desc *pool, const sp_batch *batch,
+                                                size_t *bytes);
+sp_status sp_pool_select_gather(const sp_pool_desc *pool, int32_t mode, double param,
+                                const sp_batch *batch, const float *importance,
+                                const int32_t *token_ids, float *token_scores,
+                                float *chunk_scores, uint8_t *keep, int32_t *n_kept_chunks,
+                                int32_t *kept_ids, int32_t *kept_pos, int64_t *kept_offsets,
+                                void *ws, size_t ws_bytes, void *stream);
+/* The tokens per block of the one-launch form of sp_pool_select_gather for
+ * this batch on the current device, or 0 when the call runs the separate
+ * kernels. Host arithmetic and device attribute queries only. */
+sp_status sp_pool_select_gather_plan(const sp_pool_desc *pool, const sp_batch *batch,
+                                     int32_t *block_tokens);
 
 /*
  * Standalone-tool semantics ([G] Sliding Window and its worked example,

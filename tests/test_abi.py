@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 import torch
 
@@ -207,6 +208,57 @@ def test_select_and_gather_reject_null_pointers():
         sp.SP_ERR_INVALID_ARGUMENT
     assert L.sp_gather_kept(b.ref(), 32, *args, vp(4096), 4, None) == sp.SP_ERR_WORKSPACE_TOO_SMALL
     assert L.sp_gather_kept(b.ref(), 0, *args, vp(4096), 1 << 20, None) == sp.SP_ERR_INVALID_ARGUMENT
+
+
+def _post(batch, desc=None, mode=sp.SP_SELECT_MASS, param=0.85, null=(), ws_bytes=1 << 30,
+          ws=4096):
+    """sp_pool_select_gather with fake (never dereferenced) device pointers;
+    the arguments named in `null` are passed as NULL."""
+    names = ["importance", "token_ids", "token_scores", "chunk_scores", "keep", "n_kept",
+             "kept_ids", "kept_pos", "kept_offsets"]
+    ptrs = [ctypes.c_void_p(0 if n in null else 4096 * (i + 1)) for i, n in enumerate(names)]
+    d = desc if desc is not None else sp.pool_desc()
+    return sp.lib().sp_pool_select_gather(ctypes.byref(d), mode, param, batch.ref(), *ptrs,
+                                          ctypes.c_void_p(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw, want", [
+    (dict(mode=7), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(param=0.0), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(param=float("nan")), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(mode=sp.SP_SELECT_TOP_P, param=1.5), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(desc=sp.pool_desc(W=4)), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(desc=sp.pool_desc(C=0)), sp.SP_ERR_INVALID_ARGUMENT),
+    (dict(desc=sp.pool_desc(C=2048)), sp.SP_ERR_UNSUPPORTED),
+    (dict(desc=sp.pool_desc(C=1)), sp.SP_ERR_UNSUPPORTED),      # 100000 chunks in a prompt
+    (dict(ws=4100), sp.SP_ERR_INVALID_ARGUMENT),                  # misaligned workspace
+    (dict(ws_bytes=64), sp.SP_ERR_WORKSPACE_TOO_SMALL),
+    (dict(ws=0), sp.SP_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_pool_select_gather_rejects_bad_arguments(kw, want):
+    assert _post(sp.Batch([0, 100000]), **kw) == want
+
+
+@pytest.mark.parametrize("name", ["importance", "token_ids", "chunk_scores", "keep", "n_kept",
+                                  "kept_ids", "kept_pos", "kept_offsets"])
+def test_pool_select_gather_rejects_null_pointers(name):
+    assert _post(sp.Batch([0, 100]), null=(name,)) == sp.SP_ERR_INVALID_ARGUMENT
+
+
+def test_pool_select_gather_workspace_covers_both_forms():
+    pd = sp.pool_desc()
+    for offs in ([0, 100], [0, 5000, 5001], [0, 131072], [0] + [4096 * (i + 1) for i in range(64)]):
+        b = sp.Batch(offs)
+        nc = b.n_chunks(32)
+        need = sp.post_workspace_bytes(pd, b)
+        # status header + two 8-byte slots per pool group (256 tokens at C = 32),
+        # one per block (up to 1024) and one per chunk
+        groups = sum((n + 255) // 256 for n in np.diff(offs))
+        assert need >= 256 + groups * 16 + 1024 * 8 + nc * 8
+        # or the separate kernels' own workspaces
+        assert need >= 256 + sp.pool_workspace_bytes(pd, b) + sp.gather_workspace_bytes(b, 32)
+    # a plan query is host arithmetic (0 = separate kernels; no device here)
+    assert sp.post_plan(pd, sp.Batch([0, 131072])) in (0, 512)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
