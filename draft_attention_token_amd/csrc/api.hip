@@ -444,8 +444,7 @@ sp_status sp_select_workspace_bytes(const sp_batch *batch, int32_t chunk_size, s
   sp_status st = check_batch(batch, &total);
   if (st != SP_OK) return st;
   if ((st = check_chunks(batch, chunk_size, &max_nc)) != SP_OK) return st;
-  const SegTable chunks = make_table(batch, 0, chunk_size, 0);
-  *bytes = select_ws(chunks.B, chunks.unit_off[chunks.B]);
+  *bytes = 0;   // the selection needs no workspace
   return SP_OK;
 }
 
@@ -459,11 +458,11 @@ sp_status sp_select_chunks(int32_t mode, double param, const sp_batch *batch, in
   if (st != SP_OK) return st;
   if ((st = check_chunks(batch, chunk_size, &max_nc)) != SP_OK) return st;
   if (!chunk_scores || !keep || !n_kept_chunks) return SP_ERR_INVALID_ARGUMENT;
+  (void)ws;   // none needed (see sp_select_workspace_bytes)
+  (void)ws_bytes;
   const SegTable chunks = make_table(batch, 0, chunk_size, 0);
-  const size_t need = select_ws(chunks.B, chunks.unit_off[chunks.B]);
-  if (need && (!ws || ws_bytes < need)) return SP_ERR_WORKSPACE_TOO_SMALL;
   const SelectTable t = make_select_table(chunks, param);
-  return launched(launch_select(mode, param, t, chunk_scores, keep, n_kept_chunks, ws,
+  return launched(launch_select(mode, param, t, chunk_scores, keep, n_kept_chunks,
                                 reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -564,7 +563,7 @@ sp_status sp_pool_select_gather(const sp_pool_desc *pool, int32_t mode, double p
   if (e == hipSuccess)
     e = launch_pool_chunk(p, pt, importance, token_scores, chunk_scores, pool_region, hs);
   if (e == hipSuccess)
-    e = launch_select(mode, param, sel, chunk_scores, keep, n_kept_chunks, nullptr, hs);
+    e = launch_select(mode, param, sel, chunk_scores, keep, n_kept_chunks, hs);
   if (e == hipSuccess)
     e = launch_gather(chunks, blocks, blocks.unit_off[blocks.B], p.C, keep, token_ids, kept_ids,
                       kept_pos, kept_offsets, gather_region, hs);

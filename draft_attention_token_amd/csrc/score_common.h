@@ -33,11 +33,6 @@ template <int D> struct Frag<__bf16, D> {
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) v[s] = p[2 * s];
   }
-  __device__ __forceinline__ void load_cached(const __bf16 *row, int half) {
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(row) + half;
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) v[s] = p[2 * s];
-  }
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) v[s] = u32x4{0u, 0u, 0u, 0u};
@@ -55,7 +50,6 @@ template <int D> struct Frag<float, D> {
       v[4 * i + 0] = x.x; v[4 * i + 1] = x.y; v[4 * i + 2] = x.z; v[4 * i + 3] = x.w;
     }
   }
-  __device__ __forceinline__ void load_cached(const float *row, int half) { load(row, half); }
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) v[s] = 0.f;

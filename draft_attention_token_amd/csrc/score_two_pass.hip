@@ -40,7 +40,7 @@ __device__ __forceinline__ f32x16 tile_logits(const AttnShape &s, const TileCtx 
                                               int g, int lane) {
   const int half = lane >> 5, r = lane & 31;
   Frag<T, D> a, bk;
-  if (r < s.L * s.G) a.load_cached(q_row_ptr(q, s, c.b, l, g, r), half); else a.zero();
+  if (r < s.L * s.G) a.load(q_row_ptr(q, s, c.b, l, g, r), half); else a.zero();
   if (c.kl < c.nkeys) bk.load(k_row_ptr(k, s, total_keys, l, c.key0 + c.kl, g), half); else bk.zero();
   return mfma_tile<D>(a, bk);
 }
@@ -85,8 +85,8 @@ __global__ __launch_bounds__(64 * kStatsWaves) void k_stats(AttnShape s, SegTabl
   const TileCtx c = tile_ctx(tiles, t, col);       // c.kl: the key this lane loads
   Frag<T, D> a, bk;
   if (col >= rows) a.zero();
-  else if (c.b == b0) a.load_cached(&qs[col][0], half);
-  else a.load_cached(q_row_ptr(q, s, c.b, l, g, col), half);
+  else if (c.b == b0) a.load(&qs[col][0], half);
+  else a.load(q_row_ptr(q, s, c.b, l, g, col), half);
   if (c.kl < c.nkeys) bk.load(k_row_ptr(k, s, total_keys, l, c.key0 + c.kl, g), half); else bk.zero();
   const f32x16 acc = mfma_tile<D>(bk, a);          // acc[i]: key acc_row(i, half), row col
   const int j = col / s.G;
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(64 * kW) void k_score_pooled(
     const bool active = prob < n_prob;
     const int l = active ? prob / s.Hkv : 0, g = active ? prob - l * s.Hkv : 0;
     Frag<T, D> a;
-    if (col < rows) a.load_cached(q_row_ptr(q, s, b, l, g, col), half); else a.zero();
+    if (col < rows) a.load(q_row_ptr(q, s, b, l, g, col), half); else a.zero();
     const float *lrow = lse + ((int64_t)b * n_prob + (active ? prob : 0)) * kRows;
     float lr[16];
 #pragma unroll

@@ -195,17 +195,10 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectTable t, double param
 
 }  // namespace
 
-size_t select_ws(int B, int total_chunks) {
-  (void)B;
-  (void)total_chunks;
-  return 0;
-}
-
 int select_rank_blocks(int nc) { return (nc + kRankTile - 1) / kRankTile; }
 
 hipError_t launch_select(int mode, double param, const SelectTable &t, const float *chunk_scores,
-                         uint8_t *keep, int32_t *n_kept, void *ws, hipStream_t st) {
-  (void)ws;
+                         uint8_t *keep, int32_t *n_kept, hipStream_t st) {
   if (mode == SP_SELECT_MASS)
     hipLaunchKernelGGL(k_select<true>, dim3(t.blk_off[t.B]), dim3(kThreads), 0, st, t, param,
                        chunk_scores, keep, n_kept);

@@ -296,9 +296,9 @@ struct SelectTable {
   int32_t kc[SP_MAX_PROMPTS];              // top-p budget per prompt
 };
 int select_rank_blocks(int nc);
-size_t select_ws(int B, int total_chunks);
+// (The selection needs no workspace.)
 hipError_t launch_select(int mode, double param, const SelectTable &t, const float *chunk_scores,
-                         uint8_t *keep, int32_t *n_kept, void *ws, hipStream_t st);
+                         uint8_t *keep, int32_t *n_kept, hipStream_t st);
 
 // Pooling, selection and compaction in one launch (post.hip): blocks of TB
 // tokens (whole pool groups of one prompt, at most kPostMaxTB tokens and

@@ -136,7 +136,10 @@ int sp_abi_version(void);
 const char *sp_status_string(int status);
 
 /* Workspace sizes (bytes, device memory) each call needs for this batch;
- * the result is written to *bytes. Alignment: 256 bytes (at least 16). */
+ * the result is written to *bytes. Alignment: 256 bytes (at least 16).
+ * The selection needs none: sp_select_workspace_bytes writes 0 for every
+ * valid batch (it checks the batch and chunk size like the call) and is
+ * kept so that callers size every stage the same way. */
 sp_status sp_score_workspace_bytes(const sp_attn_desc *desc, const sp_batch *batch,
                                    size_t *bytes);
 sp_status sp_pool_workspace_bytes(const sp_pool_desc *desc, const sp_batch *batch,
@@ -260,8 +263,7 @@ sp_status sp_pool_chunk(const sp_pool_desc *desc, const sp_batch *batch, const f
  *   chunk_scores:  [sum nc_b] fp32 in (finite, >= 0).
  *   keep:          [sum nc_b] uint8 out (0/1).
  *   n_kept_chunks: [B] int32 out.
- *   ws: device workspace of sp_select_workspace_bytes() bytes (currently
- *       0: may be NULL).
+ *   ws, ws_bytes: not used (the selection needs no workspace; may be NULL).
  */
 sp_status sp_select_chunks(int32_t mode, double param, const sp_batch *batch, int32_t chunk_size,
                            const float *chunk_scores, uint8_t *keep, int32_t *n_kept_chunks,
