@@ -101,6 +101,49 @@ def test_one_call_equals_the_three_calls(lengths, W, C, normalize, kind):
         _assert_same(fused, sep, f"{mode} {param}")
 
 
+EDGE = [
+    # (lengths, W, C, normalize, kind)
+    ((512,), 13, 32, True, "rand"),                    # exactly one 512-token block
+    ((1, 131071), 13, 32, True, "spiky"),              # a one-token prompt ahead of a long one
+    ((131071, 1), 13, 32, True, "spiky"),              # and after it
+    ((5000, 3000), 129, 1024, True, "rand"),           # widest window, largest chunk
+    ((2048, 2047, 2049), 1, 32, True, "ties"),         # no pooling; block edges
+    ((40000,), 13, 16, False, "spiky"),                # no normalisation, small chunks
+]
+
+
+@pytest.mark.parametrize("lengths, W, C, normalize, kind", EDGE,
+                         ids=["one_block", "tiny_first", "tiny_last", "W129_C1024", "W1_edges",
+                              "raw_C16"])
+def test_one_call_edges(lengths, W, C, normalize, kind):
+    off, imp, ids = _inputs(lengths, kind, seed=sum(lengths) % 7919 + W)
+    batch = sp.Batch(off)
+    imp_d, ids_d = torch.from_numpy(imp).to(DEV), torch.from_numpy(ids).to(DEV)
+    print(f"[gpu] post edge {lengths} W={W} C={C}: block tokens "
+          f"{sp.post_plan(sp.pool_desc(W, C, normalize), batch)}", flush=True)
+    for mode, param in MODES:
+        fused = sp.sp_pool_select_gather(imp_d, ids_d, batch, mode, param, W=W, C=C,
+                                         normalize=normalize)
+        sep = _separate(imp_d, ids_d, batch, W, C, normalize, mode, param)
+        torch.cuda.synchronize()
+        _assert_same(fused, sep, f"{mode} {param}")
+
+
+def test_one_call_without_token_scores():
+    """token_scores may be NULL: everything else is unchanged."""
+    off, imp, ids = _inputs((3212, 100, 5000), "spiky", seed=3)
+    batch = sp.Batch(off)
+    imp_d, ids_d = torch.from_numpy(imp).to(DEV), torch.from_numpy(ids).to(DEV)
+    a = sp.sp_pool_select_gather(imp_d, ids_d, batch, "mass", 0.85)
+    b = sp.sp_pool_select_gather(imp_d, ids_d, batch, "mass", 0.85, token_scores=False)
+    torch.cuda.synchronize()
+    assert b[0] is None
+    for x, y in zip(a[1:4] + a[6:], b[1:4] + b[6:]):
+        assert torch.equal(x, y)
+    n = int(a[6][-1])
+    assert torch.equal(a[4][:n], b[4][:n]) and torch.equal(a[5][:n], b[5][:n])
+
+
 def test_plan_takes_the_benchmark_prompt_in_one_launch():
     """128K tokens over 256 CUs: blocks of 512 tokens, one per CU; four 60000-
     token prompts of 8-token chunks need more blocks than that (separate
