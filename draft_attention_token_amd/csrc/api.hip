@@ -193,15 +193,53 @@ int post_block_tokens(const sp_batch *batch, int C, int max_blocks) {
   return 0;
 }
 
-// Workspace of sp_pool_select_gather: the status header, then either the
-// fused launch's slots or the separate kernels' workspaces (pool, gather).
+// Tokens per range of the die-local launch: the smallest multiple of the
+// pool group (at most kDieMaxTB tokens and kDieMaxChunks chunks) whose
+// ranges number at most `ranges` (the CUs of one die), for batches of at
+// most kDieMaxPrompts prompts with at most kPostMaxGroups groups each; 0
+// when there is none.
+int post_die_block_tokens(const sp_batch *batch, int C, int ranges) {
+  const int B = batch->n_prompts;
+  if (ranges <= 0 || B > kDieMaxPrompts || B > ranges) return 0;
+  const int GT = pool_block_tokens(C);
+  for (int b = 0; b < B; ++b)
+    if ((batch->token_offsets[b + 1] - batch->token_offsets[b] + GT - 1) / GT > kPostMaxGroups)
+      return 0;
+  const int64_t total = batch->token_offsets[B];
+  int per = (int)std::max<int64_t>(1, total / ((int64_t)ranges * GT));
+  for (; (int64_t)per * GT <= kDieMaxTB && (int64_t)per * GT / C <= kDieMaxChunks; ++per) {
+    const int64_t TB = (int64_t)per * GT;
+    int64_t n = 0;
+    for (int b = 0; b < B; ++b)
+      n += (batch->token_offsets[b + 1] - batch->token_offsets[b] + TB - 1) / TB;
+    if (n <= ranges) return (int)TB;
+  }
+  return 0;
+}
+
+// The form sp_pool_select_gather takes for a batch on the current device,
+// and its tokens per block (range).
+int post_form(const sp_batch *batch, int C, int32_t *block_tokens) {
+  int tb = post_die_block_tokens(batch, C, post_die_ranges());
+  if (tb > 0) {
+    *block_tokens = tb;
+    return SP_POST_DIE;
+  }
+  tb = post_block_tokens(batch, C, post_max_blocks());
+  *block_tokens = tb;
+  return tb > 0 ? SP_POST_GRID : SP_POST_SEPARATE;
+}
+
+// Workspace of sp_pool_select_gather: the status header, then the slots of
+// either one-launch form or the separate kernels' workspaces (pool, gather).
 size_t post_split_bytes(const PoolTable &pt, const SegTable &chunks) {
   return align_up(pool_ws(pt.B, pt.blk_off[pt.B])) + gather_ws(chunks.B, chunks.unit_off[chunks.B]);
 }
 size_t post_ws_bytes(const PoolTable &pt, const SegTable &chunks) {
   // The pool table's blocks are the pool groups.
-  return kStatusBytes + std::max(post_slot_bytes(chunks.unit_off[chunks.B], pt.blk_off[pt.B]),
-                                 post_split_bytes(pt, chunks));
+  const int NC = chunks.unit_off[chunks.B], G = pt.blk_off[pt.B];
+  return kStatusBytes + std::max({post_slot_bytes(NC, G), post_die_slot_bytes(chunks.B, NC, G),
+                                  post_split_bytes(pt, chunks)});
 }
 
 // Scoring workspace: header, single-pass slots, two-pass region (one layout
@@ -534,8 +572,29 @@ sp_status sp_pool_select_gather(const sp_pool_desc *pool, int32_t mode, double p
   if (!ws || ws_bytes < post_ws_bytes(pt, chunks)) return SP_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const SelectTable sel = make_select_table(chunks, param);
-  const int TB = post_block_tokens(batch, p.C, post_max_blocks());
-  if (TB > 0) {
+  int32_t TB = 0;
+  const int form = post_form(batch, p.C, &TB);
+  if (form == SP_POST_DIE) {
+    DieTable t;
+    memset(&t, 0, sizeof(t));
+    t.B = batch->n_prompts;
+    t.TB = TB;
+    t.GT = pool_block_tokens(p.C);
+    for (int b = 0; b < t.B; ++b) {
+      const int64_t n = batch->token_offsets[b + 1] - batch->token_offsets[b];
+      t.rng_off[b + 1] = t.rng_off[b] + (int32_t)((n + TB - 1) / TB);
+      t.chunk_off[b + 1] = chunks.unit_off[b + 1];
+      t.grp_off[b + 1] = pt.blk_off[b + 1];
+      t.tok_off[b] = chunks.tok_off[b];
+      t.kc[b] = sel.kc[b];
+    }
+    t.tok_off[t.B] = chunks.tok_off[t.B];
+    t.NR = t.rng_off[t.B];
+    return launched(launch_post_die(mode, param, p, t, importance, token_ids, token_scores,
+                                    chunk_scores, keep, n_kept_chunks, kept_ids, kept_pos,
+                                    kept_offsets, ws, hs));
+  }
+  if (form == SP_POST_GRID) {
     PostTable t;
     memset(&t, 0, sizeof(t));
     t.B = batch->n_prompts;
@@ -579,7 +638,21 @@ sp_status sp_pool_select_gather_plan(const sp_pool_desc *pool, const sp_batch *b
   if (st != SP_OK) return st;
   if ((st = check_batch(batch, &total)) != SP_OK) return st;
   if ((st = check_chunks(batch, p.C, &max_nc)) != SP_OK) return st;
-  *block_tokens = post_block_tokens(batch, p.C, post_max_blocks());
+  post_form(batch, p.C, block_tokens);
+  return SP_OK;
+}
+
+sp_status sp_pool_select_gather_form(const sp_pool_desc *pool, const sp_batch *batch,
+                                     int32_t *form, int32_t *block_tokens) {
+  PoolParams p;
+  int64_t total;
+  int max_nc;
+  if (!form || !block_tokens) return SP_ERR_INVALID_ARGUMENT;
+  sp_status st = check_pool(pool, &p);
+  if (st != SP_OK) return st;
+  if ((st = check_batch(batch, &total)) != SP_OK) return st;
+  if ((st = check_chunks(batch, p.C, &max_nc)) != SP_OK) return st;
+  *form = post_form(batch, p.C, block_tokens);
   return SP_OK;
 }
 

@@ -108,35 +108,6 @@ __device__ __forceinline__ void take(Addr addr, Use use, uint32_t (&v)[M], const
   }
 }
 
-// The selection's fixed point and order (as sp_select_chunks): floor(v *
-// 2^shift) from the float's bits, the shift set by the prompt's largest
-// score; an ascending key is a descending score.
-__device__ __forceinline__ int fixed_shift(float mx) {
-  int e = 0;
-  if (mx > 0.f) frexpf(mx, &e);
-  return 48 - e;
-}
-__device__ __forceinline__ long long to_fixed(float v, int shift) {
-  const uint32_t u = __float_as_uint(v);
-  const int e = (int)((u >> 23) & 0xffu);
-  const unsigned long long m = (u & 0x7fffffu) | (e ? 0x800000u : 0u);
-  const int sh = (e ? e : 1) - 150 + shift;
-  if (sh >= 0) return (long long)(m << sh);
-  return sh <= -64 ? 0ll : (long long)(m >> (-sh));
-}
-__device__ __forceinline__ uint32_t order_key(long long fx) {
-  return 0xffffffffu - (uint32_t)((unsigned long long)fx >> 16);
-}
-
-// Ordered-integer image of a float (monotone): LDS atomics take min and max.
-__device__ __forceinline__ uint32_t ord_of(float v) {
-  const uint32_t u = __float_as_uint(v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float float_of(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-
 template <bool kMass>
 __global__ __launch_bounds__(kThreads) void k_post(
     PoolParams p, PostTable t, double param, const float *__restrict__ imp,

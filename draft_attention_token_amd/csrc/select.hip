@@ -37,26 +37,6 @@ constexpr int kGroups = kThreads / kRankTile;   // lane groups splitting the oth
 constexpr int kStage = 4096;                    // chunks staged in LDS at a time
 constexpr int kPerThread = SP_MAX_CHUNKS_PER_PROMPT / kThreads;   // scores held per thread
 
-__device__ __forceinline__ int fixed_shift(float mx) {
-  int e = 0;
-  if (mx > 0.f) frexpf(mx, &e);   // mx < 2^e
-  return 48 - e;
-}
-// floor(v * 2^shift) for finite v >= 0 with v * 2^shift < 2^63, from the
-// float's bits (exact; no floating-point rounding).
-__device__ __forceinline__ long long to_fixed(float v, int shift) {
-  const uint32_t u = __float_as_uint(v);
-  const int e = (int)((u >> 23) & 0xffu);
-  const unsigned long long m = (u & 0x7fffffu) | (e ? 0x800000u : 0u);
-  const int sh = (e ? e : 1) - 150 + shift;   // v = m * 2^((e ? e : 1) - 150)
-  if (sh >= 0) return (long long)(m << sh);
-  return sh <= -64 ? 0ll : (long long)(m >> (-sh));
-}
-// Ascending key = descending score.
-__device__ __forceinline__ uint32_t order_key(long long fx) {
-  return 0xffffffffu - (uint32_t)((unsigned long long)fx >> 16);
-}
-
 __device__ __forceinline__ int table_prompt(const int32_t *off, int B, int u) {
   int lo = 0, hi = B - 1;
   while (lo < hi) {

@@ -158,6 +158,37 @@ __device__ __forceinline__ int64_t wave_prompt_offsets(const int32_t *counts, in
 }
 static_assert(SP_MAX_PROMPTS <= 128, "two prompts per lane of one wave");
 
+// The selection's fixed point and order: floor(v * 2^shift) from the
+// float's bits (exact, no floating-point rounding), the shift set by the
+// prompt's largest score so that it lands in [2^47, 2^48); chunks are
+// ranked on the top 32 bits of that value, an ascending key being a
+// descending score.
+__device__ __forceinline__ int fixed_shift(float mx) {
+  int e = 0;
+  if (mx > 0.f) frexpf(mx, &e);   // mx < 2^e
+  return 48 - e;
+}
+// For finite v >= 0 with v * 2^shift < 2^63.
+__device__ __forceinline__ long long to_fixed(float v, int shift) {
+  const uint32_t u = __float_as_uint(v);
+  const int e = (int)((u >> 23) & 0xffu);
+  const unsigned long long m = (u & 0x7fffffu) | (e ? 0x800000u : 0u);
+  const int sh = (e ? e : 1) - 150 + shift;   // v = m * 2^((e ? e : 1) - 150)
+  if (sh >= 0) return (long long)(m << sh);
+  return sh <= -64 ? 0ll : (long long)(m >> (-sh));
+}
+__device__ __forceinline__ uint32_t order_key(long long fx) {
+  return 0xffffffffu - (uint32_t)((unsigned long long)fx >> 16);
+}
+// Ordered-integer image of a float (monotone): LDS atomics take min and max.
+__device__ __forceinline__ uint32_t ord_of(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float float_of(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 struct AttnShape {
   int n_layers, Hq, Hkv, d;
   int L;                            // query steps per (layer, head): La + pre
@@ -326,6 +357,34 @@ hipError_t launch_post(int mode, double param, const PoolParams &p, const PostTa
                        const float *imp, const int32_t *ids, float *token_scores,
                        float *chunk_scores, uint8_t *keep, int32_t *n_kept, int32_t *kept_ids,
                        int32_t *kept_pos, int64_t *kept_offsets, void *ws, hipStream_t st);
+// The same in a launch whose blocks exchange values only with blocks of their
+// own chip die (post_die.hip): every die runs the whole batch, cut into NR
+// ranges of TB tokens (whole pool groups of one prompt, at most kDieMaxTB
+// tokens and kDieMaxChunks chunks); block c takes range c / 8 and writes the
+// eighth c % 8 of it. At most kDieMaxPrompts prompts and one range per CU
+// of a die.
+constexpr int kXcds = 8;                 // chip dies (XCDs); a launch deals block c to die c % 8
+constexpr int kDieMaxTB = 8192;
+constexpr int kDieMaxChunks = 1024;
+constexpr int kDieMaxPrompts = 32;
+struct DieTable {
+  int32_t B, NR, TB;
+  int32_t GT;                                // tokens per pool group: pool_block_tokens(C)
+  int32_t rng_off[kDieMaxPrompts + 1];       // range prefix per prompt
+  int32_t chunk_off[kDieMaxPrompts + 1];     // chunk prefix per prompt
+  int32_t grp_off[kDieMaxPrompts + 1];       // pool-group prefix per prompt
+  int32_t tok_off[kDieMaxPrompts + 1];       // token offsets
+  int32_t kc[kDieMaxPrompts];                // top-p budget per prompt
+};
+// Ranges per die the die-local launch may use on the current device (0: it
+// cannot run).
+int post_die_ranges();
+// Bytes of its slots (after the status header).
+size_t post_die_slot_bytes(int B, int total_chunks, int total_groups);
+hipError_t launch_post_die(int mode, double param, const PoolParams &p, const DieTable &t,
+                           const float *imp, const int32_t *ids, float *token_scores,
+                           float *chunk_scores, uint8_t *keep, int32_t *n_kept, int32_t *kept_ids,
+                           int32_t *kept_pos, int64_t *kept_offsets, void *ws, hipStream_t st);
 // Marks the status header at ws as a call with no timed-out wait.
 hipError_t launch_stamp(void *ws, hipStream_t st);
 

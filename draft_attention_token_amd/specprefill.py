@@ -42,7 +42,7 @@ EXPORTED = [
     "sp_pool_chunk", "sp_select_chunks", "sp_gather_kept", "sp_score_status", "sp_break_even",
     "sp_window_plan", "sp_stitch_windows", "sp_select_legacy_workspace_bytes", "sp_select_legacy",
     "sp_score_plan", "sp_score_attention_noalloc", "sp_pool_select_gather_workspace_bytes",
-    "sp_pool_select_gather", "sp_pool_select_gather_plan",
+    "sp_pool_select_gather", "sp_pool_select_gather_plan", "sp_pool_select_gather_form",
 ]
 
 _ALGOS = {"auto": SP_SCORE_AUTO, "two_pass": SP_SCORE_TWO_PASS, "stream": SP_SCORE_STREAM}
@@ -447,6 +447,19 @@ def post_plan(desc: sp_pool_desc, batch: Batch) -> int:
     _check(lib().sp_pool_select_gather_plan(ctypes.byref(desc), batch.ref(), ctypes.byref(tb)),
            "sp_pool_select_gather_plan")
     return tb.value
+
+
+POST_FORMS = {0: "separate", 1: "grid", 2: "die"}
+
+
+def post_form(desc: sp_pool_desc, batch: Batch):
+    """(form, tokens per block) of sp_pool_select_gather for this batch on the
+    current device: form "die" (one launch, each die runs the batch), "grid"
+    (one launch over every CU) or "separate" (the three stages' kernels)."""
+    form, tb = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    _check(lib().sp_pool_select_gather_form(ctypes.byref(desc), batch.ref(), ctypes.byref(form),
+                                            ctypes.byref(tb)), "sp_pool_select_gather_form")
+    return POST_FORMS[form.value], tb.value
 
 
 def sp_pool_select_gather(importance: torch.Tensor, token_ids: torch.Tensor, offsets, mode: str,

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SP_ABI_VERSION 2
+#define SP_ABI_VERSION 3
 #define SP_MAX_PROMPTS 128          /* prompts per batch */
 #define SP_MAX_CHUNKS_PER_PROMPT 16384
 
@@ -289,12 +289,18 @@ sp_status sp_gather_kept(const sp_batch *batch, int32_t chunk_size, const uint8_
  * sp_pool_chunk, sp_select_chunks and sp_gather_kept in one call, with the
  * same arguments and bit-identical results ([PR] Approach steps 3-4; [G]
  * v3.1 item 5, v3 items 1-2, Chunk Selection, Sparse Prefill). On the device
- * the three stages run as one launch of at most one block per compute unit
- * (blocks of whole chunks of one prompt, up to 2048 tokens and 64 chunks
- * each), the blocks handing each other min/max, chunk scores and kept
- * counts through the workspace; a batch that needs more blocks than that
- * runs the three stages' own kernels instead (sp_pool_select_gather_plan
- * tells which).
+ * the three stages run in one of three forms (sp_pool_select_gather_form
+ * tells which):
+ *   SP_POST_DIE: one launch in which each chip die (XCD) runs the whole
+ *     batch with one block per compute unit (ranges of whole chunks of one
+ *     prompt, up to 8192 tokens and 1024 chunks each; at most 32 prompts and
+ *     one range per CU of a die); blocks hand each other values only within
+ *     their die, and every block finds its prompt's selection cutoff itself;
+ *   SP_POST_GRID: one launch of at most one block per compute unit over the
+ *     whole device (blocks of up to 2048 tokens and 64 chunks), the blocks
+ *     handing each other min/max, chunk scores and kept counts;
+ *   SP_POST_SEPARATE: the three stages' own kernels, for batches that need
+ *     more blocks than that.
  *
  *   pool:         as sp_pool_chunk (its chunk_size is C).
  *   mode, param:  as sp_select_chunks.
@@ -325,6 +331,15 @@ sp_status sp_pool_select_gather(const sp_pool_desc *pool, int32_t mode, double p
  * kernels. Host arithmetic and device attribute queries only. */
 sp_status sp_pool_select_gather_plan(const sp_pool_desc *pool, const sp_batch *batch,
                                      int32_t *block_tokens);
+/* The form of sp_pool_select_gather for this batch on the current device
+ * (*form: SP_POST_DIE, SP_POST_GRID or SP_POST_SEPARATE) and its tokens per
+ * block (0 for SP_POST_SEPARATE). Host arithmetic and device attribute
+ * queries only. */
+#define SP_POST_SEPARATE 0
+#define SP_POST_GRID 1
+#define SP_POST_DIE 2
+sp_status sp_pool_select_gather_form(const sp_pool_desc *pool, const sp_batch *batch,
+                                     int32_t *form, int32_t *block_tokens);
 
 /*
  * Standalone-tool semantics ([G] Sliding Window and its worked example,

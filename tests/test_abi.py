@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     L = sp.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert L.sp_abi_version() == 2
+    assert L.sp_abi_version() == 3
 
 
 def test_status_strings():
@@ -245,7 +245,7 @@ def test_pool_select_gather_rejects_null_pointers(name):
     assert _post(sp.Batch([0, 100]), null=(name,)) == sp.SP_ERR_INVALID_ARGUMENT
 
 
-def test_pool_select_gather_workspace_covers_both_forms():
+def test_pool_select_gather_workspace_covers_every_form():
     pd = sp.pool_desc()
     for offs in ([0, 100], [0, 5000, 5001], [0, 131072], [0] + [4096 * (i + 1) for i in range(64)]):
         b = sp.Batch(offs)
@@ -255,10 +255,30 @@ def test_pool_select_gather_workspace_covers_both_forms():
         # one per block (up to 1024) and one per chunk
         groups = sum((n + 255) // 256 for n in np.diff(offs))
         assert need >= 256 + groups * 16 + 1024 * 8 + nc * 8
+        # the die-local form: per die two copies of a slot per group min, max,
+        # chunk and prompt
+        assert need >= 256 + 2 * 8 * (2 * groups + nc + len(offs) - 1) * 8
         # or the separate kernels' own workspaces
         assert need >= 256 + sp.pool_workspace_bytes(pd, b) + sp.gather_workspace_bytes(b, 32)
-    # a plan query is host arithmetic (0 = separate kernels; no device here)
-    assert sp.post_plan(pd, sp.Batch([0, 131072])) in (0, 512)
+    # form queries are host arithmetic (no device here: the separate kernels)
+    assert sp.post_plan(pd, sp.Batch([0, 131072])) in (0, 512, 4096)
+    assert sp.post_form(pd, sp.Batch([0, 131072])) in (("separate", 0), ("die", 4096))
+
+
+def test_pool_select_gather_form_rejects_bad_arguments():
+    L = sp.lib()
+    b = sp.Batch([0, 1000])
+    f, tb = ctypes.c_int32(0), ctypes.c_int32(0)
+    pd = sp.pool_desc()
+    assert L.sp_pool_select_gather_form(ctypes.byref(pd), b.ref(), None, ctypes.byref(tb)) == \
+        sp.SP_ERR_INVALID_ARGUMENT
+    assert L.sp_pool_select_gather_form(ctypes.byref(pd), b.ref(), ctypes.byref(f), None) == \
+        sp.SP_ERR_INVALID_ARGUMENT
+    bad = sp.pool_desc(W=4)
+    assert L.sp_pool_select_gather_form(ctypes.byref(bad), b.ref(), ctypes.byref(f),
+                                        ctypes.byref(tb)) == sp.SP_ERR_INVALID_ARGUMENT
+    assert L.sp_pool_select_gather_form(ctypes.byref(pd), None, ctypes.byref(f),
+                                        ctypes.byref(tb)) == sp.SP_ERR_INVALID_ARGUMENT
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -39,7 +39,10 @@ CASES = [
     ((5000, 7, 300), 13, 32, False, "rand"),
     ((20000,), 13, 32, True, "flat"),                  # no signal: every score 1, then boosts
     ((33, 64, 97, 1, 500) * 25 + (40, 41, 2), 13, 32, True, "rand"),   # 128 prompts
-    ((60000,) * 4, 13, 8, True, "rand"),               # needs more blocks than CUs
+    ((60000,) * 4, 13, 8, True, "rand"),               # die-local, 7680-token ranges
+    ((70000,) * 4, 13, 8, True, "rand"),               # fits neither one-launch form
+    ((140000,), 13, 16, True, "spiky"),                # 8750 chunks: 16 scores per thread
+    ((3000, 5000), 5, 1, True, "rand"),                # one-token chunks
 ]
 MODES = [("top_p", 0.3), ("mass", 0.85), ("mass", 0.999)]
 
@@ -87,9 +90,10 @@ def test_one_call_equals_the_three_calls(lengths, W, C, normalize, kind):
     off, imp, ids = _inputs(lengths, kind, seed=sum(lengths) % 9973 + C)
     batch = sp.Batch(off)
     pd = sp.pool_desc(W, C, normalize)
-    tb = sp.post_plan(pd, batch)
+    form, tb = sp.post_form(pd, batch)
+    assert sp.post_plan(pd, batch) == tb
     print(f"[gpu] post {len(lengths)} prompts {sum(lengths)} tokens W={W} C={C} {kind}: "
-          f"block tokens {tb}", flush=True)
+          f"form {form}, block tokens {tb}", flush=True)
     imp_d, ids_d = torch.from_numpy(imp).to(DEV), torch.from_numpy(ids).to(DEV)
     ws = sp._ws(sp.post_workspace_bytes(pd, batch), DEV)
     for mode, param in MODES:
@@ -119,8 +123,8 @@ def test_one_call_edges(lengths, W, C, normalize, kind):
     off, imp, ids = _inputs(lengths, kind, seed=sum(lengths) % 7919 + W)
     batch = sp.Batch(off)
     imp_d, ids_d = torch.from_numpy(imp).to(DEV), torch.from_numpy(ids).to(DEV)
-    print(f"[gpu] post edge {lengths} W={W} C={C}: block tokens "
-          f"{sp.post_plan(sp.pool_desc(W, C, normalize), batch)}", flush=True)
+    print(f"[gpu] post edge {lengths} W={W} C={C}: form, block tokens "
+          f"{sp.post_form(sp.pool_desc(W, C, normalize), batch)}", flush=True)
     for mode, param in MODES:
         fused = sp.sp_pool_select_gather(imp_d, ids_d, batch, mode, param, W=W, C=C,
                                          normalize=normalize)
@@ -144,15 +148,24 @@ def test_one_call_without_token_scores():
     assert torch.equal(a[4][:n], b[4][:n]) and torch.equal(a[5][:n], b[5][:n])
 
 
-def test_plan_takes_the_benchmark_prompt_in_one_launch():
-    """128K tokens over 256 CUs: blocks of 512 tokens, one per CU; four 60000-
-    token prompts of 8-token chunks need more blocks than that (separate
-    kernels)."""
+def test_forms_of_the_benchmark_batches():
+    """One 128K prompt: the die-local form, one range per CU of a die (4096
+    tokens at 32 CUs per die). The 16-prompt ragged batch of 397256 tokens
+    needs more ranges than a die has CUs at 8192 tokens each: the grid form.
+    More than 32 prompts: the grid form. Four 70000-token prompts of 8-token
+    chunks are more than a die's ranges hold and need more grid blocks than
+    the device has CUs: the separate kernels."""
     cus = torch.cuda.get_device_properties(DEV).multi_processor_count
     pd = sp.pool_desc()
-    tb = sp.post_plan(pd, sp.Batch([0, 131072]))
-    assert tb > 0 and tb % 32 == 0 and (131072 + tb - 1) // tb <= cus, tb
-    assert sp.post_plan(sp.pool_desc(C=8), sp.Batch([0, 60000, 120000, 180000, 240000])) == 0
+    form, tb = sp.post_form(pd, sp.Batch([0, 131072]))
+    assert form == "die" and tb % 256 == 0 and (131072 + tb - 1) // tb <= cus // 8, (form, tb)
+    off = np.concatenate([[0], np.cumsum(RAGGED16)])
+    assert sp.post_form(pd, sp.Batch(off))[0] == "grid"
+    assert sp.post_form(pd, sp.Batch(np.arange(0, 33 * 100 + 1, 100)))[0] == "grid"
+    assert sp.post_form(pd, sp.Batch(np.arange(0, 32 * 100 + 1, 100)))[0] == "die"
+    assert sp.post_form(sp.pool_desc(C=8), sp.Batch([0, 70000, 140000, 210000, 280000])) == \
+        ("separate", 0)
+    assert sp.post_form(sp.pool_desc(C=8), sp.Batch([0, 60000, 120000, 180000, 240000]))[0] == "die"
 
 
 @pytest.mark.parametrize("lengths, W, C, normalize, kind", [CASES[2], CASES[7], CASES[12]],
@@ -187,15 +200,18 @@ def test_one_call_against_the_oracle(lengths, W, C, normalize, kind):
             c0 += nc
 
 
-def test_timed_out_call_reports_and_the_workspace_stays_usable(monkeypatch):
+@pytest.mark.parametrize("lengths, form", [((131072,), "die"), ((70000, 3000, 60000), "die"),
+                                           (RAGGED16, "grid")], ids=["die", "die_3p", "grid"])
+def test_timed_out_call_reports_and_the_workspace_stays_usable(monkeypatch, lengths, form):
     """A zero wait budget (SP_SCORE_WAIT_US=0, read at launch) lets a block
     give up on any value not already posted: the grid still drains, and the
     call either completed anyway or reports the time-out (and then wrote no
     kept tokens). The next call on the same workspace, with the normal
     budget, matches the separate kernels bit for bit."""
-    off, imp, ids = _inputs((131072,), "rand", seed=5)
+    off, imp, ids = _inputs(lengths, "rand", seed=5)
     batch = sp.Batch(off)
     pd = sp.pool_desc()
+    assert sp.post_form(pd, batch)[0] == form
     imp_d, ids_d = torch.from_numpy(imp).to(DEV), torch.from_numpy(ids).to(DEV)
     ws = sp._ws(sp.post_workspace_bytes(pd, batch), DEV)
     sep = _separate(imp_d, ids_d, batch, 13, 32, True, "mass", 0.85)
@@ -216,7 +232,7 @@ def test_separate_form_clears_the_status_of_an_earlier_call():
     """The status header of a call that runs the separate kernels says
     'completed' even on a workspace whose previous call timed out."""
     pd = sp.pool_desc(C=8)
-    off, imp, ids = _inputs((60000,) * 4, "rand", seed=8)
+    off, imp, ids = _inputs((70000,) * 4, "rand", seed=8)
     batch = sp.Batch(off)
     assert sp.post_plan(pd, batch) == 0
     ws = sp._ws(sp.post_workspace_bytes(pd, batch), DEV)
