@@ -326,9 +326,10 @@ def main():
         post_form = "sp_stitch_windows + sp_pool_chunk + sp_select_legacy"
     else:
         assert pipe.post_status() == 0, "post-scoring launch reported a timed-out wait"
-        tb = sp.post_plan(pipe.pdesc, pipe.batch)
-        post_form = (f"sp_pool_select_gather: one launch, {tb}-token blocks" if tb
-                     else "sp_pool_select_gather: separate pool, select and gather kernels")
+        form, tb = sp.post_form(pipe.pdesc, pipe.batch)
+        post_form = {"die": f"sp_pool_select_gather: one die-local launch, {tb}-token ranges",
+                     "grid": f"sp_pool_select_gather: one launch, {tb}-token blocks",
+                     "separate": "sp_pool_select_gather: separate pool, select and gather kernels"}[form]
     log(f"after scoring: {ms_post * 1e3:.1f} us ({post_form})")
     alg_bytes = score_algorithmic_bytes(inp)
     achieved = alg_bytes / (ms_score * 1e-3) / 1e9

@@ -30,13 +30,15 @@
 //    are stored XOR-swizzled, so the MFMA operand reads (16 bytes of 32 key
 //    rows) hit distinct LDS banks.
 //  * Per problem a compute wave computes logits with 32x32x16 bf16 MFMA, K as
-//    the A operand (row = key) and Q as the B operand (column = query row):
-//    a lane holds one query row and 16 keys of each tile. The accumulator of
-//    a tile is one of the wave's "e slots": lag x tiles slots of 16 floats
-//    per lane. After the MFMAs the wave takes each row's max over its keys,
-//    turns the logits in place into e = 2^(x - m) and sums them; the slots
-//    keep e until the row lse is known. The launch takes the deepest lag its
-//    busiest wave allows: 2 problems at 3 tiles per wave, 4 at 2, 8 at 1.
+//    the A operand (row = key) and Q as the B operand (column = query row,
+//    its operands read into registers at the start of the problem): a lane
+//    holds one query row and 16 keys of each tile, 16 fp32 accumulators per
+//    tile. After the MFMAs the wave takes each row's max over its keys,
+//    turns the logits in place into e = 2^(x - m) and sums them, then parks
+//    e in 24-bit form (the rounded float's top three bytes) until the row
+//    lse is known. A wave keeps kPk problems parked, the most its registers
+//    hold: 3 at 3 tiles per wave (2 with fp8 K or small groups), 4 at 2
+//    tiles, 7 at 1.
 //  * The last compute wave to finish a problem merges the seven waves'
 //    statistics into the block's partial base-2 lse of each row and posts it
 //    to the workspace.
@@ -48,10 +50,11 @@
 //    row lse in LDS. It also stages each problem's Q in LDS, three problems
 //    ahead. Its own load queue holds only these, so its polls never wait
 //    behind the K stream.
-//  * Before a tile's MFMAs of problem x overwrite its slot, the wave folds
-//    problem x - lag: p = e * 2^(m - lse), max into a running value per
-//    (row, key) in registers (the max over layers and KV groups).
-//  * Finally: max over the G heads of a step (lanes of a group), mean over
+//  * Before parking problem x in its slot, the wave folds the slot's
+//    previous occupant, problem x - kPk: p = e * 2^(m - lse), the max over
+//    the heads on the lane bits that hold them, and the max into a running
+//    value per (row, key) in registers (the max over layers and KV groups).
+//  * Finally: the rest of the max over the G heads of a step, the mean over
 //    the steps (a butterfly across groups of lanes), store.
 //
 // Slots carry the tag of the call that posted them, next to the value, so a
