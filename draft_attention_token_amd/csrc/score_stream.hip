@@ -916,16 +916,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
     const unsigned dies = prompt_dies(c_lo, n_c);
     const int dlane = lane >> 3;
     const bool din = ((dies >> dlane) & 1u) != 0u;
+    const uint32_t voff = dlane * kRows * (int)sizeof(uint64_t) + (lane & 7) * 32;
+    auto poll = [&](int y) {
+      const __amdgpu_buffer_rsrc_t rs =
+          rsrc(ws.dslot + die_slot(y, bb, 0), kDies * kRows * (int)sizeof(uint64_t));
+      return load_quad(rs, voff, 0);
+    };
+    // The die partials of the next kPoll problems are in flight together, so
+    // a control wave that runs behind gets several problems' lse from one
+    // round trip (a device-scope load takes ~1.5 us), not one. win[i] holds
+    // problem x + i, polled when q_issued was wq[i]. Forms of three tiles per
+    // wave only (long prompts; at 128K tokens 144 -> 140 us with four in
+    // flight, eight no better): with fewer, shorter problems the extra polls
+    // cost more than they bring (32K tokens: 68.1 -> 69.9 us).
+    constexpr int kPoll = kPk <= 3 ? 4 : 1;
+    Quad win[kPoll];
+    int wq[kPoll];
+#pragma unroll
+    for (int i = 0; i < kPoll; ++i) {
+      if (i < P) win[i] = poll(i);
+      wq[i] = q_issued;
+    }
     for (int x = 0; x < P; ++x) {
       // Die partials of x. Loads of one wave return in order: once a poll's
       // values are back, every Q load issued before it has landed too.
-      const __amdgpu_buffer_rsrc_t rs =
-          rsrc(ws.dslot + die_slot(x, bb, 0), kDies * kRows * (int)sizeof(uint64_t));
-      const uint32_t voff = dlane * kRows * (int)sizeof(uint64_t) + (lane & 7) * 32;
-      Quad v[1];
+      Quad v[1] = {win[0]};
       const bool in[1] = {din};
-      int q_round = q_issued;
-      v[0] = load_quad(rs, voff, 0);
+      int q_round = wq[0];
       const uint64_t t0 = wall_clock64();
       for (;;) {
         const bool ok = !in[0] | quad_full(v[0], ws.call_tag);
@@ -938,9 +955,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
         asm volatile("" ::: "memory");
         if (q_issued <= x + kPk) {    // the compute waves may need Q(x + kPk) now
           top_up();
-          q_round = q_issued;
         }
-        if (in[0] && !quad_full(v[0], ws.call_tag)) v[0] = load_quad(rs, voff, 0);
+        q_round = q_issued;
+        if (in[0] && !quad_full(v[0], ws.call_tag)) v[0] = poll(x);
       }
       const f32x4 lq = merge_quads(v, in);
       // The slot held the lse of x - 8: free once every compute wave folded it.
@@ -948,6 +965,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(AttnShape s, StreamTable
       if (lane < 8) *reinterpret_cast<f32x4 *>(&sm.lse[x % kLseSlots][4 * lane]) = lq;
       if (lane == 0) lds_set(&sm.lse_ready[x % kLseSlots], x + 1);
       top_up();
+#pragma unroll
+      for (int i = 0; i + 1 < kPoll; ++i) {
+        win[i] = win[i + 1];
+        wq[i] = wq[i + 1];
+      }
+      if (x + kPoll < P) win[kPoll - 1] = poll(x + kPoll);
+      wq[kPoll - 1] = q_issued;
     }
     return;
   }
