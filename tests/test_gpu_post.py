@@ -43,6 +43,7 @@ CASES = [
     ((70000,) * 4, 13, 8, True, "rand"),               # fits neither one-launch form
     ((140000,), 13, 16, True, "spiky"),                # 8750 chunks: 16 scores per thread
     ((3000, 5000), 5, 1, True, "rand"),                # one-token chunks
+    ((257, 1000, 33, 8000) * 8, 13, 32, True, "spiky"),  # 32 prompts: a die's every CU
 ]
 MODES = [("top_p", 0.3), ("mass", 0.85), ("mass", 0.999)]
 
