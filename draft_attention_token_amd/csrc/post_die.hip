@@ -51,7 +51,9 @@ static_assert(kWaves <= 16, "one wave value per lane of a row of 16");
 constexpr int kMinEPT = 4096 / kThreads;
 constexpr int kMaxEPT = SP_MAX_CHUNKS_PER_PROMPT / kThreads;
 constexpr int kHalo = (kMaxPoolWindow - 1) / 2;
-constexpr int kRangeGroups = kDieMaxTB / kMaxPoolWindow + 1;      // pool groups hold >= 129 tokens
+// Pool groups of a range: a group holds C * floor(256 / C) >= 129 tokens.
+constexpr int kMinGroupTokens = 129;
+constexpr int kRangeGroups = (kDieMaxTB + kMinGroupTokens - 1) / kMinGroupTokens;
 constexpr int kBins = 256;                                        // radix digit: 8 bits
 constexpr int kKeyBits = 46;                                      // 32-bit score key + 14-bit index
 constexpr int kWriteMax = (kDieMaxTB + kXcds - 1) / kXcds;        // tokens a block writes
@@ -486,7 +488,7 @@ __global__ __launch_bounds__(kThreads) void k_post_die(
   // Each chunk's fixed-point score and key, kept in registers up to 8 per
   // thread (beyond, recomputed where needed). sc[e] is 0 past the prompt's
   // chunks.
-  constexpr bool kKeep = kPerThread <= 16;
+  constexpr bool kKeep = kPerThread <= 8;
   long long fxa[kKeep ? kPerThread : 1];
   unsigned long long cka[kKeep ? kPerThread : 1];
   auto fx = [&](int e) -> long long {
