@@ -37,7 +37,7 @@
 //    turns the logits in place into e = 2^(x - m) and sums them, then parks
 //    e in 24-bit form (the rounded float's top three bytes) until the row
 //    lse is known. A wave keeps kPk problems parked, the most its registers
-//    hold: 3 at 3 tiles per wave (2 with fp8 K or small groups), 4 at 2
+//    hold: 3 at 3 tiles per wave (2 with small groups), 4 at 2
 //    tiles, 7 at 1.
 //  * The last compute wave to finish a problem merges the seven waves'
 //    statistics into the block's partial base-2 lse of each row and posts it
@@ -226,13 +226,13 @@ __device__ __forceinline__ Group group_of(int d, int c_lo, int n_c) {
 // Kernel forms: the lag (problems folded behind) and the tiles per compute
 // wave it allows, 6 to 8 e slots of 16 registers each.
 // Problems a compute wave keeps parked (kPk) for the tiles it owns, and
-// back: the most that fit its registers without spilling. At three tiles
-// that is three, except where the running maxima take more registers
-// (CL < 2) or fp8 conversion needs some (two).
+// back: the most that fit its registers. At three tiles that is three,
+// except where the running maxima take more registers (CL < 2: two). The fp8
+// form with three spills 8 VGPRs and still beats two (the lse of a problem
+// arrives about two problems after its statistics: at 128K tokens 112 ->
+// 106 us), so it keeps three as well.
 __host__ __device__ constexpr int tpw_for_pk(int pk) { return pk <= 3 ? 3 : pk == 4 ? 2 : 1; }
-constexpr int pk_for_tpw(int tpw, int cl, bool f8) {
-  return tpw <= 1 ? 7 : tpw == 2 ? 4 : (cl == 2 && !f8) ? 3 : 2;
-}
+constexpr int pk_for_tpw(int tpw, int cl) { return tpw <= 1 ? 7 : tpw == 2 ? 4 : cl == 2 ? 3 : 2; }
 
 // A lane's four rows of a partial: two 16-byte loads of two slots each.
 struct Quad {
@@ -1036,7 +1036,7 @@ struct DeviceInfo {
 template <int D, bool F8, int CL>
 bool occupancy_cl(int *occ) {
   int a = 0, b = 0, c = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, k_stream<D, F8, pk_for_tpw(3, CL, F8), CL>, kThreads, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, k_stream<D, F8, pk_for_tpw(3, CL), CL>, kThreads, 0) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_stream<D, F8, 4, CL>, kThreads, 0) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, k_stream<D, F8, 7, CL>, kThreads, 0) != hipSuccess)
     return false;
@@ -1228,7 +1228,7 @@ hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const 
     // Head-max levels taken at fold time: lane bits 4 and 3 are head bits
     // for G >= 4, bit 4 for G = 2.
     const int cl = s.G >= 4 ? 2 : s.G == 2 ? 1 : 0;
-    const int npk = pk_for_tpw(tpw, cl, f8);
+    const int npk = pk_for_tpw(tpw, cl);
     auto pick = [&](auto d_tag, auto f8_tag) {
       constexpr int Dv = decltype(d_tag)::value;
       constexpr bool F8v = decltype(f8_tag)::value;
@@ -1236,7 +1236,7 @@ hipError_t launch_score_stream(const AttnShape &s, const SegTable &tiles, const 
         constexpr int C = decltype(cl_tag)::value;
         return npk == 7 ? k_stream<Dv, F8v, 7, C>
                : npk == 4 ? k_stream<Dv, F8v, 4, C>
-                          : k_stream<Dv, F8v, pk_for_tpw(3, C, F8v), C>;
+                          : k_stream<Dv, F8v, pk_for_tpw(3, C), C>;
       };
       return cl == 2 ? by_pk(std::integral_constant<int, 2>{})
                      : cl == 1 ? by_pk(std::integral_constant<int, 1>{})
