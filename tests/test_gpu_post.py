@@ -3,9 +3,10 @@ scoring (pooling, normalisation, boosts, chunk means, selection, compaction).
 
 Its results must equal those of sp_pool_chunk, sp_select_chunks and
 sp_gather_kept called one after the other, bit for bit (same arithmetic in
-the same order), on batches the one-launch form takes and on batches it
-hands to the separate kernels; and, prompt by prompt, those of the oracle's
-pooling, selection and gather within the parity tolerances.
+the same order), in each of its forms: the die-local launch (every chip die
+runs the batch and finds the selection cutoff itself), the launch over the
+whole chip, and the separate kernels; and, prompt by prompt, those of the
+oracle's pooling, selection and gather within the parity tolerances.
 """
 import ctypes
 
