@@ -263,13 +263,17 @@ __device__ __forceinline__ float boosted(const PoolParams &p, int N, int t, floa
   v = __fmul_rn(v, t < p.first_n ? p.first_mult : 1.f);
   return __fmul_rn(v, t >= N - p.last_n ? p.last_mult : 1.f);
 }
-// Sum of the boosts of tokens [a, e), in token order (e - a where none
-// applies: a sum of ones is exact).
+// Sum of the boosts of tokens [a, e): the tokens with no boost, then those
+// with the first boost only, the last boost only and both, each kind its
+// count times its factor (e - a where none applies).
 __device__ __forceinline__ float boost_sum(const PoolParams &p, int N, int a, int e) {
   if (a >= p.first_n && e <= N - p.last_n) return (float)(e - a);
-  float s = 0.f;
-  for (int t = a; t < e; ++t) s = __fadd_rn(s, boosted(p, N, t, 1.f));
-  return s;
+  const int fe = min(e, p.first_n), l0 = max(a, N - p.last_n);
+  const int nf = max(0, fe - a), nl = max(0, e - l0), nb = max(0, fe - l0);
+  float s = (float)(e - a - nf - nl + nb);
+  s = __fadd_rn(s, __fmul_rn((float)(nf - nb), p.first_mult));
+  s = __fadd_rn(s, __fmul_rn((float)(nl - nb), p.last_mult));
+  return __fadd_rn(s, __fmul_rn((float)nb, __fmul_rn(p.first_mult, p.last_mult)));
 }
 // Sum of b_t (x_t - g) over tokens [a, e), x_t at xs[t - base] (LDS), in a
 // fixed order: partial sums of consecutive runs of 8 tokens, each in token
