@@ -259,9 +259,17 @@ struct PoolParams {
 
 // v times the boosts of token t of a prompt of N tokens (first, then last;
 // a factor of 1 where a boost does not apply leaves v as it is).
+// The products and sums of these helpers are rounded one by one, so that
+// every kernel that inlines them gets the same bits. The rounding helpers
+// are plain operators, which the compiler may fuse into a multiply-add; a
+// product passed through rounded() is opaque to it and is not fused.
+__device__ __forceinline__ float rounded(float x) {
+  asm("" : "+v"(x));
+  return x;
+}
 __device__ __forceinline__ float boosted(const PoolParams &p, int N, int t, float v) {
   v = __fmul_rn(v, t < p.first_n ? p.first_mult : 1.f);
-  return __fmul_rn(v, t >= N - p.last_n ? p.last_mult : 1.f);
+  return rounded(__fmul_rn(v, t >= N - p.last_n ? p.last_mult : 1.f));
 }
 // Sum of the boosts of tokens [a, e): the tokens with no boost, then those
 // with the first boost only, the last boost only and both, each kind its
@@ -271,14 +279,14 @@ __device__ __forceinline__ float boost_sum(const PoolParams &p, int N, int a, in
   const int fe = min(e, p.first_n), l0 = max(a, N - p.last_n);
   const int nf = max(0, fe - a), nl = max(0, e - l0), nb = max(0, fe - l0);
   float s = (float)(e - a - nf - nl + nb);
-  s = __fadd_rn(s, __fmul_rn((float)(nf - nb), p.first_mult));
-  s = __fadd_rn(s, __fmul_rn((float)(nl - nb), p.last_mult));
-  return __fadd_rn(s, __fmul_rn((float)nb, __fmul_rn(p.first_mult, p.last_mult)));
+  s = __fadd_rn(s, rounded(__fmul_rn((float)(nf - nb), p.first_mult)));
+  s = __fadd_rn(s, rounded(__fmul_rn((float)(nl - nb), p.last_mult)));
+  return __fadd_rn(s, rounded(__fmul_rn((float)nb, __fmul_rn(p.first_mult, p.last_mult))));
 }
 // Sum of b_t (x_t - g) over tokens [a, e), x_t at xs[t - base] (LDS), in a
 // fixed order: partial sums of consecutive runs of 8 tokens, each in token
 // order, then the partials in order (chunk_rel; chunk_part gives one run so
-// that lanes can take them in parallel). Additions stay uncontracted.
+// that lanes can take them in parallel).
 __device__ __forceinline__ float chunk_part(const PoolParams &p, int N, const float *xs, int base,
                                             int a, int e, float g) {
   float v[8];
