@@ -580,6 +580,10 @@ sp_status sp_pool_select_gather(const sp_pool_desc *pool, int32_t mode, double p
     t.B = batch->n_prompts;
     t.TB = TB;
     t.GT = pool_block_tokens(p.C);
+    t.by_gt = fast_div((uint32_t)t.GT);
+    t.by_c = fast_div((uint32_t)p.C);
+    t.by_cpg = fast_div((uint32_t)(t.GT / p.C));
+    t.by_runs = fast_div((uint32_t)((p.C + 7) / 8));
     for (int b = 0; b < t.B; ++b) {
       const int64_t n = batch->token_offsets[b + 1] - batch->token_offsets[b];
       t.rng_off[b + 1] = t.rng_off[b] + (int32_t)((n + TB - 1) / TB);

@@ -354,8 +354,9 @@ __global__ __launch_bounds__(kThreads) void k_post_die(
         }
         const float wmn = wave_min(mn4), wmx = wave_max(mx4);
         if (lane == 0) {   // the wave's 256 tokens lie in one pool group
-          atomicMin(&bmn[(qt - t0) / GT], ord_of(wmn));
-          atomicMax(&bmx[(qt - t0) / GT], ord_of(wmx));
+          const int g = div_by(t.by_gt, qt - t0);
+          atomicMin(&bmn[g], ord_of(wmn));
+          atomicMax(&bmx[g], ord_of(wmx));
         }
       }
     } else {
@@ -376,13 +377,15 @@ __global__ __launch_bounds__(kThreads) void k_post_die(
             const float wmn = wave_min(tt < t1 ? x : INFINITY);
             const float wmx = wave_max(tt < t1 ? x : -INFINITY);
             if (lane == 0) {
-              atomicMin(&bmn[(wt - t0) / GT], ord_of(wmn));
-              atomicMax(&bmx[(wt - t0) / GT], ord_of(wmx));
+              const int g = div_by(t.by_gt, wt - t0);
+              atomicMin(&bmn[g], ord_of(wmn));
+              atomicMax(&bmx[g], ord_of(wmx));
             }
           }
         } else if (tt < t1) {
-          atomicMin(&bmn[(tt - t0) / GT], ord_of(x));
-          atomicMax(&bmx[(tt - t0) / GT], ord_of(x));
+          const int g = div_by(t.by_gt, tt - t0);
+          atomicMin(&bmn[g], ord_of(x));
+          atomicMax(&bmx[g], ord_of(x));
         }
       }
     }
@@ -397,11 +400,12 @@ __global__ __launch_bounds__(kThreads) void k_post_die(
     // in order (as chunk_rel adds them).
     const int runs = (p.C + 7) / 8;   // per chunk
     for (int w0 = 0; w0 < nck * runs; w0 += kThreads) {
-      const int k = w0 + tid, c = k / runs, u = k - c * runs;
+      const int k = w0 + tid, c = div_by(t.by_runs, k), u = k - c * runs;
       if (k < nck * runs) {
         const int a = t0 + c * p.C, e = min(t1, a + p.C);
-        xpart[k] = a + 8 * u < e ? chunk_part(p, N, xs, t0, a + 8 * u, e, float_of(bmn[(a - t0) / GT]))
-                                 : 0.f;
+        xpart[k] = a + 8 * u < e
+                       ? chunk_part(p, N, xs, t0, a + 8 * u, e, float_of(bmn[div_by(t.by_cpg, c)]))
+                       : 0.f;
       }
     }
     __syncthreads();
@@ -467,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void k_post_die(
       sc[e] = 0.f;
       if (e < ept && j < nc) {
         const int a = j * p.C, en = min(N, a + p.C);
-        sc[e] = chunk_score(__uint_as_float(got[2 * kQ + e]), boost_sum(p, N, a, en), gmin[a / GT],
+        sc[e] = chunk_score(__uint_as_float(got[2 * kQ + e]), boost_sum(p, N, a, en), gmin[div_by(t.by_cpg, j)],
                             en - a, p.normalize, flat, mn, range);
       }
     }
@@ -741,7 +745,7 @@ __global__ __launch_bounds__(kThreads) void k_post_die(
   }
   const long long first = base + (bos ? 1 : 0);
   for (int tt = u0 + tid; tt < u1; tt += kThreads) {
-    const int c = tt / p.C;
+    const int c = ca + div_by(t.by_c, tt - t0);
     if (!kflag[c - cu0]) continue;
     const long long out = first + (long long)kpre[c - cu0] * p.C + (tt - c * p.C);
     if (out >= total) continue;

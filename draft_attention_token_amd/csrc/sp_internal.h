@@ -379,9 +379,27 @@ constexpr int kXcds = 8;                 // chip dies (XCDs); a launch deals blo
 constexpr int kDieMaxTB = 8192;
 constexpr int kDieMaxChunks = 1024;
 constexpr int kDieMaxPrompts = 32;
+// Division by a divisor fixed for a launch, by one high multiply: for
+// d >= 1 and n (d - 1) < 2^32, floor(n / d) = hi32(n m) with m =
+// ceil(2^32 / d), since m d - 2^32 < d keeps n m / 2^32 - n / d below
+// 1 / d; d = 1 (m = 2^32) takes n itself. m comes from the host.
+struct FastDiv {
+  uint32_t m, one;
+};
+inline FastDiv fast_div(uint32_t d) {
+  FastDiv f;
+  f.m = (uint32_t)(((1ull << 32) + d - 1) / d);
+  f.one = d == 1 ? ~0u : 0u;
+  return f;
+}
+__device__ __forceinline__ int div_by(const FastDiv &f, int n) {
+  return (int)(__umulhi((uint32_t)n, f.m) + ((uint32_t)n & f.one));
+}
+
 struct DieTable {
   int32_t B, NR, TB;
   int32_t GT;                                // tokens per pool group: pool_block_tokens(C)
+  FastDiv by_gt, by_c, by_cpg, by_runs;      // / GT, / C, / (GT / C), / ceil(C / 8)
   int32_t rng_off[kDieMaxPrompts + 1];       // range prefix per prompt
   int32_t chunk_off[kDieMaxPrompts + 1];     // chunk prefix per prompt
   int32_t grp_off[kDieMaxPrompts + 1];       // pool-group prefix per prompt
