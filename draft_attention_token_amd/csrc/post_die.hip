@@ -135,29 +135,6 @@ __device__ __forceinline__ void take(At at, Use use, uint32_t (&v)[M], const Die
   }
 }
 
-// Min or max over the wave of 64-bit keys, in every lane.
-template <bool kMin>
-__device__ __forceinline__ unsigned long long wave_ext_u64(unsigned long long x) {
-#define SP_DPP_EXT64(ctrl)                                                                      \
-  {                                                                                             \
-    const uint32_t l2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, ctrl, 0xf, 0xf, false); \
-    const uint32_t h2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), ctrl, 0xf, 0xf, false); \
-    const unsigned long long y = ((unsigned long long)h2 << 32) | l2;                           \
-    x = kMin ? (y < x ? y : x) : (y > x ? y : x);                                               \
-  }
-  SP_DPP_EXT64(0xB1) SP_DPP_EXT64(0x4E) SP_DPP_EXT64(0x124) SP_DPP_EXT64(0x128)
-#undef SP_DPP_EXT64
-  unsigned long long t = 0;
-#pragma unroll
-  for (int r = 0; r < 64; r += 16) {
-    const unsigned long long y =
-        ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), r) << 32) |
-        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, r);
-    t = r == 0 ? y : (kMin ? (y < t ? y : t) : (y > t ? y : t));
-  }
-  return t;
-}
-
 // Inclusive scans over the wave in lane order, by DPP: shifts by 1, 2, 4
 // and 8 within each row of 16 lanes, then row 0's total added to row 1 and
 // row 2's to row 3 (row_bcast:15), then lane 31's to rows 2 and 3
@@ -256,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void k_post_die(
   __shared__ SelState sst;
   __shared__ float red_lo[kWaves], red_hi[kWaves], red_mx[kWaves];
   __shared__ long long red_tot[kWaves], red_base[kWaves];
-  __shared__ unsigned long long red_kmn[kWaves], red_kmx[kWaves];
+  __shared__ uint32_t red_omn[kWaves], red_omx[kWaves];
   __shared__ int red_before[kWaves], red_scan[kWaves];
   __shared__ uint8_t kraw[kScanPer * kThreads];    // the write part's chunks: kept, not final
   __shared__ uint8_t kflag[kScanPer * kThreads];   // kept (the final chunk included)
@@ -502,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void k_post_die(
     if constexpr (kKeep) return cka[e]; else return chunk_key(fx(e), tid + kThreads * e);
   };
   long long tot = 0;                              // fixed-point sum of the thread's chunks
-  unsigned long long kmn = ~0ull, kmx = 0ull;     // and its non-final chunks' keys
+  uint32_t omn = ~0u, omx = 0u;                   // its non-final chunks' score keys
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     if (e < ept) {
@@ -516,33 +493,42 @@ __global__ __launch_bounds__(kThreads) void k_post_die(
       tot += f;
       if (j == last) fx_last = f;
       if (j < last) {
-        kmn = ck < kmn ? ck : kmn;
-        kmx = ck > kmx ? ck : kmx;
+        const uint32_t ok = (uint32_t)(ck >> (kKeyBits - 32));
+        omn = min(omn, ok);
+        omx = max(omx, ok);
       }
     }
   }
   tot = wave_sum_i64(tot);
-  kmn = wave_ext_u64<true>(kmn);
-  kmx = wave_ext_u64<false>(kmx);
+  const auto umin = [](uint32_t a, uint32_t c) { return a < c ? a : c; };
+  const auto umax = [](uint32_t a, uint32_t c) { return a > c ? a : c; };
+  omn = wave_reduce_u32(omn, umin);
+  omx = wave_reduce_u32(omx, umax);
   if (lane == 0) {
     red_tot[wave] = tot;
-    red_kmn[wave] = kmn;
-    red_kmx[wave] = kmx;
+    red_omn[wave] = omn;
+    red_omx[wave] = omx;
   }
   __syncthreads();   // (also publishes fx_last)
   tot = fold_waves(red_tot, 0ll, [](long long a, long long c) { return a + c; });
-  kmn = fold_waves(red_kmn, ~0ull,
-                   [](unsigned long long a, unsigned long long c) { return a < c ? a : c; });
-  kmx = fold_waves(red_kmx, 0ull,
-                   [](unsigned long long a, unsigned long long c) { return a > c ? a : c; });
+  omn = fold_waves(red_omn, ~0u, umin);
+  omx = fold_waves(red_omx, 0u, umax);
+  // Every non-final chunk's key lies in [kmn, kmx], and the smallest and
+  // largest of them agree with these bounds on their score part, so the
+  // highest bit in which the bounds differ is that of the keys whenever
+  // two scores differ (else it lies in the index part, and the select
+  // takes one digit more at most).
+  const unsigned long long kmn = (unsigned long long)omn << (kKeyBits - 32);
+  const unsigned long long kmx = ((unsigned long long)omx << (kKeyBits - 32)) |
+                                 ((1ull << (kKeyBits - 32)) - 1ull);
   const long long need = kMass ? (long long)ceil(param * (double)tot) - fx_last
                                : (long long)(t.kc[b] - 1);   // chunks ahead of a kept one
   int R = 0, thr_sh = 0;
   unsigned long long thr_P = 0;
   if (last > 0 && need > 0) {
-    if (kmn == kmx) {
+    if (last == 1) {
       R = 1;   // one non-final chunk: nothing is ahead of it
-      thr_P = kmn;
+      thr_sh = kKeyBits;   // every key >> kKeyBits is 0 = thr_P
     } else {
       // The first digit: the highest 8 bits in which the keys differ.
       const int hb = 63 - __builtin_clzll(kmn ^ kmx);
