@@ -499,6 +499,43 @@ __global__ __launch_bounds__(kThreads) void k_post_die(
       }
     }
   }
+  // Adds the candidates of a radix pass (keys k with k >> s.top == s.P) to
+  // the bins of their digit, bits [s.sh, s.top): counts and fixed-point sums.
+  auto add_bins = [&](const SelState &s) {
+    const uint32_t dmask = (1u << (s.top - s.sh)) - 1u;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      if (e < ept) {   // (uniform)
+        const int j = tid + kThreads * e;
+        const long long f = fx(e);
+        const unsigned long long ck = key(e);
+        const bool act = j < last && (ck >> s.top) == s.P;
+        const uint32_t bin = (uint32_t)(ck >> s.sh) & dmask;
+        const unsigned long long am = __ballot(act);
+        if (am) {
+          // A wave whose candidates share one bin adds them as one.
+          const int fl = __builtin_ctzll(am);
+          const uint32_t fb = (uint32_t)__builtin_amdgcn_readlane((int)bin, fl);
+          if (__ballot(act && bin != fb) == 0) {
+            const long long ms = kMass ? wave_sum_i64(act ? f : 0ll) : 0ll;
+            if (lane == 0) {
+              atomicAdd(&hcnt[fb], (uint32_t)__popcll(am));
+              if (kMass) atomicAdd(&hmass[fb], (unsigned long long)ms);
+            }
+          } else if (act) {
+            atomicAdd(&hcnt[bin], 1u);
+            if (kMass) atomicAdd(&hmass[bin], (unsigned long long)f);
+          }
+        }
+      }
+    }
+  };
+  // The first pass's bins at once, on the top digit of the keys: the first
+  // digit whenever two non-final chunks' scores differ in their top bit,
+  // which is the usual case (checked below). The adds overlap the
+  // reductions and need no barrier of their own.
+  SelState s0 = {0ull, 0ll, 0, kKeyBits - 8, kKeyBits, 0};
+  if (last > 1) add_bins(s0);
   tot = wave_sum_i64(tot);
   const auto umin = [](uint32_t a, uint32_t c) { return a < c ? a : c; };
   const auto umax = [](uint32_t a, uint32_t c) { return a > c ? a : c; };
@@ -530,38 +567,25 @@ __global__ __launch_bounds__(kThreads) void k_post_die(
       R = 1;   // one non-final chunk: nothing is ahead of it
       thr_sh = kKeyBits;   // every key >> kKeyBits is 0 = thr_P
     } else {
-      // The first digit: the highest 8 bits in which the keys differ.
+      // The first digit: the highest 8 bits in which the keys differ. When
+      // that is the top digit its bins are filled already; else they start
+      // again from zero.
       const int hb = 63 - __builtin_clzll(kmn ^ kmx);
       SelState s = {kmn >> (hb + 1), 0ll, 0, max(0, hb - 7), hb + 1, 0};
-      for (;;) {
-        const uint32_t dmask = (1u << (s.top - s.sh)) - 1u;
-#pragma unroll
-        for (int e = 0; e < kPerThread; ++e) {
-          if (e < ept) {   // (uniform)
-            const int j = tid + kThreads * e;
-            const long long f = fx(e);
-            const unsigned long long ck = key(e);
-            const bool act = j < last && (ck >> s.top) == s.P;
-            const uint32_t bin = (uint32_t)(ck >> s.sh) & dmask;
-            const unsigned long long am = __ballot(act);
-            if (am) {
-              // A wave whose candidates share one bin adds them as one.
-              const int fl = __builtin_ctzll(am);
-              const uint32_t fb = (uint32_t)__builtin_amdgcn_readlane((int)bin, fl);
-              if (__ballot(act && bin != fb) == 0) {
-                const long long ms = kMass ? wave_sum_i64(act ? f : 0ll) : 0ll;
-                if (lane == 0) {
-                  atomicAdd(&hcnt[fb], (uint32_t)__popcll(am));
-                  if (kMass) atomicAdd(&hmass[fb], (unsigned long long)ms);
-                }
-              } else if (act) {
-                atomicAdd(&hcnt[bin], 1u);
-                if (kMass) atomicAdd(&hmass[bin], (unsigned long long)f);
-              }
-            }
-          }
+      bool pre = hb == kKeyBits - 1;
+      if (!pre) {
+        if (tid < kBins) {
+          hcnt[tid] = 0u;
+          if (kMass) hmass[tid] = 0ull;
         }
         __syncthreads();
+      }
+      for (;;) {
+        if (!pre) {
+          add_bins(s);
+          __syncthreads();
+        }
+        pre = false;
         if (wave == 0) {
           // Lane l holds bins 4 l .. 4 l + 3 (ascending keys); exclusive
           // prefixes of their counts and sums over the bins.
