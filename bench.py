@@ -114,6 +114,48 @@ def achievable_read_gbs(dev):
     return best
 
 
+def achievable_korder_gbs(dev, k):
+    """The K cache itself read in the scoring kernel's order, with no compute
+    and no exchange (read_peak.hip's k_read_heads: problem by problem, the
+    KV head's segment of every key row, 32- or 64-key groups dealt to the
+    blocks round-robin), best of a few grid sizes, median of 9 timed passes
+    each: what this access pattern reaches on this part. Returns (GB/s,
+    blocks)."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "draft_attention_token_amd", "libspbench.so")
+    lib = ctypes.CDLL(path)
+    lib.spbench_read_heads.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.spbench_read_heads.restype = ctypes.c_int
+    n_layers, n_keys, hkv, d = k.shape
+    nbytes = k.numel() * k.element_size()
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream(dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    best = (0.0, 0)
+    for blocks in (cus - 8, cus, 2 * cus):
+        def once():
+            rc = lib.spbench_read_heads(ctypes.c_void_p(k.data_ptr()), n_layers, n_keys, hkv,
+                                        d * k.element_size(), ctypes.c_void_p(flag.data_ptr()),
+                                        blocks, ctypes.c_void_p(st.cuda_stream))
+            assert rc == 0, rc
+        for _ in range(3):
+            once()
+        times = []
+        for _ in range(9):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            once()
+            b.record(st)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3)
+        times.sort()
+        best = max(best, (nbytes / times[len(times) // 2] / 1e9, blocks))
+    return best
+
+
 def score_algorithmic_bytes(inp) -> int:
     """Bytes the scoring stage must move at least once: K and Q read, the
     fp32 importance written."""
@@ -337,6 +379,8 @@ def main():
     traffic = measured_traffic(w.name)
     read_gbs, read_shape = achievable_read_gbs(dev)
     log(f"plain 1 GiB streaming read: {read_gbs:.0f} GB/s ({read_shape} blocks per CU)")
+    korder_gbs, korder_blocks = achievable_korder_gbs(dev, k)
+    log(f"K read in the scoring order: {korder_gbs:.0f} GB/s ({korder_blocks} blocks)")
 
     kept = int(pipe.kept_offsets[-1])
     kernel_name = scoring_kernels(pipe, fp8k, w)
@@ -375,7 +419,13 @@ def main():
                      "algorithmic_bytes": alg_bytes,
                      "achievable": {"read": read_gbs, "frac": achieved / read_gbs,
                                     "kernel": f"k_read, plain streaming read of 1 GiB, "
-                                              f"{read_shape} x 512 threads per CU"}},
+                                              f"{read_shape} x 512 threads per CU",
+                                    "k_order_read": korder_gbs,
+                                    "k_order_frac": achieved / korder_gbs,
+                                    "k_order_kernel": f"k_read_heads, the K cache read problem by "
+                                                      f"problem as the scoring kernel reads it, "
+                                                      f"no compute, {korder_blocks} x 512 "
+                                                      f"threads"}},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
