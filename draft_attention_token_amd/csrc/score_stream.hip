@@ -532,14 +532,23 @@ __device__ __forceinline__ void compute_wave(const WaveCtx &c, Ring &ring, QSlot
   // unit 0 MFMAs start from init: 0, or -inf where a key is past the
   // prompt's keys or hidden from the row (causality), so the logit is -inf
   // there.
-  auto mfma_unit = [&](f32x16 &acc, const uint8_t *unit, const bf16x8 (&qreg)[kSteps], int u,
-                       const f32x16 &init) {
-    bf16x8 ko[kStepsPerUnit];
+  // Q's operands: with bf16 K they are read from LDS with each unit's K
+  // operands and live only during its MFMAs, which leaves more registers to
+  // the parked problems (measured faster: 16 prompts 611 -> 604 us, 128K
+  // 141.6 -> 141.1 us); fp8 K, which widens its operands in registers, keeps
+  // them in registers for the problem (that way 108.1 us against 110.1).
+  constexpr bool kQRegs = kF8;
+  auto mfma_unit = [&](f32x16 &acc, const uint8_t *unit, const bf16x8 *qreg, const uint8_t *qs,
+                       int u, const f32x16 &init) {
+    bf16x8 ko[kStepsPerUnit], qo[kQRegs ? 1 : kStepsPerUnit];
 #pragma unroll
-    for (int j = 0; j < kStepsPerUnit; ++j) ko[j] = k_operand(unit, u * kStepsPerUnit + j);
+    for (int j = 0; j < kStepsPerUnit; ++j) {
+      ko[j] = k_operand(unit, u * kStepsPerUnit + j);
+      if constexpr (!kQRegs) qo[j] = q_operand(qs, u * kStepsPerUnit + j);
+    }
 #pragma unroll
     for (int j = 0; j < kStepsPerUnit; ++j)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ko[j], qreg[u * kStepsPerUnit + j],
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ko[j], kQRegs ? qreg[u * kStepsPerUnit + j] : qo[j],
                                                     (u == 0 && j == 0) ? init : acc, 0, 0, 0);
   };
   // Accumulator start of tile t: all 0 unless the tile reaches past the
@@ -660,11 +669,11 @@ __device__ __forceinline__ void compute_wave(const WaveCtx &c, Ring &ring, QSlot
       if (x < P) {
         __builtin_amdgcn_sched_barrier(0);
         lds_wait_ge(&sm.q_ready, x + 1, ws, dead);
-        // Q(x)'s operands stay in registers for the problem; its slot is
-        // free again once they are read.
-        bf16x8 qreg[kSteps];
-        {
-          const uint8_t *qs = &qsl.q[x % kQSlots][0];
+        // Q(x)'s slot is free again once every MFMA of the problem has read
+        // it, or once its operands are in registers.
+        const uint8_t *qs = &qsl.q[x % kQSlots][0];
+        bf16x8 qreg[kQRegs ? kSteps : 1];
+        if constexpr (kQRegs) {
 #pragma unroll
           for (int st = 0; st < kSteps; ++st) qreg[st] = q_operand(qs, st);
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -676,7 +685,7 @@ __device__ __forceinline__ void compute_wave(const WaveCtx &c, Ring &ring, QSlot
 #pragma unroll
           for (int u = 0; u < UPT; ++u) {
             wait_unit();
-            mfma_unit(ec[t], &ring.unit[wave][kc & (kRing - 1)][0], qreg, u, init);
+            mfma_unit(ec[t], &ring.unit[wave][kc & (kRing - 1)][0], qreg, qs, u, init);
             // The MFMAs above have read the unit (their operands were
             // waited for): refill its slot.
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -684,6 +693,9 @@ __device__ __forceinline__ void compute_wave(const WaveCtx &c, Ring &ring, QSlot
             issue_next();
             __builtin_amdgcn_sched_barrier(0);   // keep the next unit's reads after the refill
           }
+        }
+        if constexpr (!kQRegs) {
+          if (lane == 0) lds_inc(&sm.q_used[x % kQSlots]);   // (after the reads: lds_inc waits)
         }
         // Row max over the wave's keys (both halves), then e = 2^(x - m) in
         // place and the row sum (masked logits are -inf and give 0). The
