@@ -355,3 +355,20 @@ def test_stitch_and_legacy_reject_bad_arguments():
     assert call(C=0) == sp.SP_ERR_INVALID_ARGUMENT
     assert call(ws_bytes=4) == sp.SP_ERR_WORKSPACE_TOO_SMALL
     assert sp.select_legacy_workspace_bytes(b, 32) >= 16 + 4
+
+
+def test_bench_read_aids_load_and_refuse_bad_shapes():
+    """bench.py's measurement aids (libspbench.so, outside the product
+    library) load and export the plain read and the K-order read; the K-order
+    read refuses a segment that is not whole 16-byte chunks, or whose chunk
+    count does not divide the block, before launching anything."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "draft_attention_token_amd", "libspbench.so"))
+    assert hasattr(lib, "spbench_read") and hasattr(lib, "spbench_read_heads")
+    fn = lib.spbench_read_heads
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    for seg in (24, 16 * 3, 0):        # not whole chunks; 3 chunks do not divide 512; none
+        assert fn(None, 6, 1000, 4, seg, None, 248, None) != 0, seg
+    assert fn(None, 0, 1000, 4, 256, None, 248, None) != 0   # no layer
+    assert fn(None, 6, 1000, 4, 256, None, 0, None) != 0     # no block
