@@ -664,7 +664,9 @@ __global__ __launch_bounds__(kThreads) void k_post_die(
   const int cu0 = u0 / p.C, cu1 = u1 > u0 ? (u1 - 1) / p.C + 1 : cu0;
   const int ncu = cu1 - cu0;
   // Kept non-final chunks ahead of cu0; the flags of [cu0, cu1) to LDS,
-  // then their exclusive prefix (one chunk per thread).
+  // then their exclusive prefix: from one ballot in every wave when the
+  // part has at most 64 chunks (16 at 4096-token ranges and C = 32), else
+  // by a block scan into kpre.
   int before = 0;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
@@ -684,7 +686,14 @@ __global__ __launch_bounds__(kThreads) void k_post_die(
   before = (int)wave_reduce_u32((uint32_t)before, [](uint32_t a, uint32_t c) { return a + c; });
   if (lane == 0) red_before[wave] = before;
   __syncthreads();
-  {
+  const bool small = ncu <= 64;   // (uniform)
+  int before_all = 0;
+  unsigned long long kmask = 0;   // the part's kept non-final chunks, one bit each
+  if (small) {
+    const int w16 = lane & 15;
+    before_all = row_fold(w16 < kWaves ? red_before[w16] : 0, [](int a, int c) { return a + c; });
+    kmask = __ballot(lane < ncu && kraw[lane] != 0);
+  } else {
     // Thread tid takes chunks kScanPer tid .. + kScanPer - 1 of the part.
     int v[kScanPer], sum = 0;
 #pragma unroll
@@ -719,9 +728,13 @@ __global__ __launch_bounds__(kThreads) void k_post_die(
          [&](int) { return tid < b; }, got, ws, d, dead);
     base = block_fold(wave_sum_i64(tid < b ? (long long)got[0] : 0ll), red_base, 0ll,
                       [](long long a, long long c) { return a + c; });
-  } else {
+  } else if (!small) {
     __syncthreads();   // kpre
   }
+  // Kept non-final chunks ahead of chunk cu0 + i.
+  auto ahead = [&](int i) -> long long {
+    return small ? (long long)(before_all + __popcll(kmask & ((1ull << i) - 1ull))) : (long long)kpre[i];
+  };
   // Chunk scores, keep flags and token scores of the write part.
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
@@ -757,7 +770,7 @@ __global__ __launch_bounds__(kThreads) void k_post_die(
   for (int tt = u0 + tid; tt < u1; tt += kThreads) {
     const int c = ca + div_by(t.by_c, tt - t0);
     if (!kflag[c - cu0]) continue;
-    const long long out = first + (long long)kpre[c - cu0] * p.C + (tt - c * p.C);
+    const long long out = first + ahead(c - cu0) * p.C + (tt - c * p.C);
     if (out >= total) continue;
     kept_ids[out] = ids[tok0 + tt];
     kept_pos[out] = tt;
