@@ -30,8 +30,9 @@
 //    are stored XOR-swizzled, so the MFMA operand reads (16 bytes of 32 key
 //    rows) hit distinct LDS banks.
 //  * Per problem a compute wave computes logits with 32x32x16 bf16 MFMA, K as
-//    the A operand (row = key) and Q as the B operand (column = query row,
-//    its operands read into registers at the start of the problem): a lane
+//    the A operand (row = key) and Q as the B operand (column = query row;
+//    with bf16 K its operands are read from LDS with each unit's K operands,
+//    with fp8 K into registers at the start of the problem): a lane
 //    holds one query row and 16 keys of each tile, 16 fp32 accumulators per
 //    tile. After the MFMAs the wave takes each row's max over its keys,
 //    turns the logits in place into e = 2^(x - m) and sums them, then parks
@@ -139,7 +140,8 @@ struct Smem {
   // Hand-offs between the compute waves and the control wave, without a
   // block barrier inside the main loop. Compute waves may drift apart by up
   // to three problems (a wave needs Q(x + 3), whose slot frees only when
-  // every wave has read Q(x)), so each counter belongs to a slot and counts
+  // every wave has read Q(x): its last MFMA of x with bf16 K), so each
+  // counter belongs to a slot and counts
   // the slot's uses cumulatively: 7 per problem that used it.
   int q_ready;                 // Q of problems < q_ready is staged
   int q_used[kQSlots];         // reads of Q slot x % 3 completed
